@@ -1,0 +1,346 @@
+"""Plain CPU oracle for the INT4 dual-mode linear, the LM-head and the
+speculative verify/accept step of QSpec-style quantized speculative decoding.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, calls or links it, and this
+module imports nothing from the product path.
+
+Everything here works on *logical* tensors and is written to be checked by
+eye, not to be fast:
+  * weight codes   q  int8  [N, K], values in [-8, 7]
+  * weight scales  s  fp16  [N, K/128], one per group of 128 consecutive k
+  * activations    x  fp16  [M, K]
+  * logits            fp32  [rows, V]  (exactly the buffer the GPU reads)
+Real arithmetic is float64, integer sums are int64.  No blocking, fusion or
+reordering beyond what each definition states.
+
+Sources (pages; each function names the section it follows):
+  [P1] qiita.com, "QSpec実行時の2つの量子化による推論の一致率を調べる"
+       (measuring Top-1 agreement of QSpec's two quantized modes)
+  [P3] kasblo.com, "Speculative Decodingとは？LLM生成を速くする方法"
+       (tutorial on speculative decoding)
+Where the pages leave a detail open (grouping, rounding, tie rules), the
+reading taken is stated at the function.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128  # k-elements per weight scale group (reading: symmetric INT4, group 128 along K)
+
+
+# --------------------------------------------------------------------------
+# Quantized linear layer, one shared INT4 weight set, two execution modes.
+# [P1] sections "W4A16: 重みのみを 4-bit に量子化", "W4A4 : 重みと活性値の両方を
+# 4-bit に量子化" and the mode tree in "QSpec の W4A4 モードと W4A16 モード":
+# one 4-bit weight set is run either with 16-bit activations or with
+# activations quantized to 4 bits at compute time.
+# --------------------------------------------------------------------------
+
+def _check_weights(q: np.ndarray, s: np.ndarray) -> tuple[int, int, int]:
+    assert q.dtype == np.int8 and q.ndim == 2
+    n, k = q.shape
+    assert k % GROUP == 0, "K must be a multiple of the group size"
+    assert s.dtype == np.float16 and s.shape == (n, k // GROUP)
+    assert q.min(initial=0) >= -8 and q.max(initial=0) <= 7
+    return n, k, k // GROUP
+
+
+def dequantize_weights(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W[n, k] = q[n, k] * s[n, floor(k / 128)] in float64.
+
+    Symmetric (no zero point); the scale of element (n, k) is the one of the
+    128-wide group that k falls in, within the same output row n.
+    """
+    n, k, g = _check_weights(q, s)
+    scale_per_k = np.repeat(s.astype(np.float64), GROUP, axis=1)  # [N, K]
+    return q.astype(np.float64) * scale_per_k
+
+
+def linear_w4a16(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W4A16 mode: y[m, n] = sum_k x[m, k] * W[n, k], float64.
+
+    [P1] "W4A16" section: weights stay 4-bit in memory and are turned into
+    16-bit values during the matrix product with 16-bit activations.  The
+    oracle is the plain matrix product with the exact fp16 activation values.
+    """
+    assert x.dtype == np.float16 and x.ndim == 2
+    w = dequantize_weights(q, s)
+    assert x.shape[1] == w.shape[1]
+    return x.astype(np.float64) @ w.T
+
+
+def quantize_activations(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token symmetric INT4 activation quantization.
+
+    [P1] "W4A4" section says only that activations are quantized to 4 bits at
+    compute time.  Reading taken (per token m):
+      amax_m = max_k |x[m, k]|
+      s_m    = fp16( fp32(amax_m) / 7 )   -- correctly rounded fp32 quotient,
+                                             then round-to-nearest-even to fp16
+      xq     = clamp(rint(x / s_m), -8, 7)   with rint = round half to even of
+                                             the exact quotient
+      s_m == 0 (all-zero row)  ->  xq = 0
+    Exactness of the quotient: x and s_m are fp16, so an exact tie x/s = j+1/2
+    is exactly representable in float64 and the float64 quotient equals it;
+    away from ties the exact quotient lies at least 2**-15 from any j+1/2,
+    far more than float64 rounding can move it.  So rint of the float64
+    quotient is rint of the exact quotient.
+    Returns xq int8 [M, K] and s fp16 [M].
+    """
+    assert x.dtype == np.float16 and x.ndim == 2
+    amax = np.abs(x.astype(np.float32)).max(axis=1)              # exact (fp16 -> fp32)
+    s32 = amax.astype(np.float32) / np.float32(7.0)              # one fp32 rounding
+    s16 = s32.astype(np.float16)                                 # one fp16 rounding (RNE)
+    s64 = s16.astype(np.float64)
+    xq = np.zeros(x.shape, dtype=np.int8)
+    nz = s64 > 0
+    if nz.any():
+        quot = x[nz].astype(np.float64) / s64[nz, None]
+        xq[nz] = np.clip(np.rint(quot), -8, 7).astype(np.int8)
+    return xq, s16
+
+
+def group_accumulators(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """acc[m, n, g] = sum_{k in group g} xq[m, k] * q[n, k], exact int64.
+
+    The integer dot products that an int8 matrix engine accumulates in i32.
+    Reading: the sums are per 128-wide group, because each group carries its
+    own weight scale; a whole-K integer sum would mix scales.
+    """
+    m, k = xq.shape
+    n, k2 = q.shape
+    assert k == k2 and k % GROUP == 0
+    g = k // GROUP
+    xg = xq.astype(np.int64).reshape(m, g, GROUP)
+    qg = q.astype(np.int64).reshape(n, g, GROUP)
+    acc = np.empty((m, n, g), dtype=np.int64)
+    for gi in range(g):
+        acc[:, :, gi] = xg[:, gi, :] @ qg[:, gi, :].T
+    return acc
+
+
+def linear_w4a4(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
+    """W4A4 mode: quantize activations per token, integer group sums, rescale.
+
+      y[m, n] = s_m * sum_g s[n, g] * acc[m, n, g]     (float64)
+
+    Returns dict(xq, sx, acc, y).  [P1] "W4A4" section: both weights and the
+    activations are 4-bit, so a dedicated integer kernel can be used.
+    """
+    _check_weights(q, s)
+    xq, sx = quantize_activations(x)
+    acc = group_accumulators(xq, q)
+    per_group = acc.astype(np.float64) * s.astype(np.float64)[None, :, :]
+    y = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
+    return {"xq": xq, "sx": sx, "acc": acc, "y": y}
+
+
+def lm_head(mode: str, x: np.ndarray, q: np.ndarray, s: np.ndarray,
+            chunk: int = 8192) -> np.ndarray:
+    """LM-head logits: the same linear (mode 'w4a16' or 'w4a4') with N = vocab.
+
+    Processed in chunks of output rows only to bound memory; each chunk is the
+    same definition as the full linear.  Returns float64 [M, V].
+    """
+    n = q.shape[0]
+    out = np.empty((x.shape[0], n), dtype=np.float64)
+    if mode == "w4a4":
+        # one activation quantization for the whole row, shared by all chunks
+        xq, sx = quantize_activations(x)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        if mode == "w4a16":
+            out[:, lo:hi] = linear_w4a16(x, q[lo:hi], s[lo:hi])
+        elif mode == "w4a4":
+            acc = group_accumulators(xq, q[lo:hi])
+            per_group = acc.astype(np.float64) * s[lo:hi].astype(np.float64)[None]
+            out[:, lo:hi] = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
+        else:
+            raise ValueError(mode)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Next-token distributions and Top-1.
+# [P3] "通常のLLM生成はなぜ逐次処理になるのか": the model gives a distribution
+# over the next token; [P1] "結果": each mode's Top-1 token and the probability
+# it assigns to it.
+# --------------------------------------------------------------------------
+
+def softmax_rows(logits: np.ndarray) -> np.ndarray:
+    """p[r, j] = exp(l[r, j] - max_r) / sum_j exp(l[r, j] - max_r), float64.
+
+    Temperature 1, no top-k/top-p (the pages give no sampling knobs)."""
+    l64 = np.asarray(logits, dtype=np.float64)
+    mx = l64.max(axis=-1, keepdims=True)
+    e = np.exp(l64 - mx)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def top1(logits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Top-1 token per row (lowest index among equal maxima, as np.argmax)
+    and its probability 1 / sum_j exp(l_j - l_max)."""
+    l64 = np.asarray(logits, dtype=np.float64)
+    t = np.argmax(l64, axis=-1).astype(np.int64)
+    mx = l64.max(axis=-1, keepdims=True)
+    prob = 1.0 / np.exp(l64 - mx).sum(axis=-1)
+    return t, prob
+
+
+# --------------------------------------------------------------------------
+# Verification.  [P3] "draft modelとtarget modelの処理フロー": the target scores
+# the gamma draft positions plus the next one; candidates are checked left to
+# right, the first mismatch/rejection stops the scan, later candidates are
+# dropped, and the new prefix starts the next iteration.
+# --------------------------------------------------------------------------
+
+def verify_greedy(tgt_logits: np.ndarray, draft_ids: np.ndarray) -> dict:
+    """Greedy prefix-match acceptance.
+
+    [P3] "greedy decodingでは一致するprefixを採用する": accept draft tokens while
+    they equal the target's argmax; at the first mismatch take the target's
+    token; if all gamma match, the extra position adds a bonus token, so
+    1..gamma+1 tokens are committed per verify.  [P1] "Speculative Decoding":
+    a rejected draft token is replaced by the target's own prediction.
+
+    tgt_logits fp32 [B, gamma+1, V]; draft_ids int [B, gamma].  Draft ids
+    outside [0, V) never equal an argmax, so they count as mismatches.
+    Returns dict(t [B, gamma+1], top1_prob [B, gamma+1], n_accept [B],
+    out_tokens [B, gamma+1] padded with -1).
+    """
+    b, gp1, v = tgt_logits.shape
+    gamma = gp1 - 1
+    d = np.asarray(draft_ids, dtype=np.int64).reshape(b, gamma)
+    t, prob = top1(tgt_logits.reshape(b * gp1, v))
+    t = t.reshape(b, gp1)
+    prob = prob.reshape(b, gp1)
+    n_accept = np.zeros(b, dtype=np.int64)
+    out = np.full((b, gp1), -1, dtype=np.int64)
+    for bi in range(b):
+        n = 0
+        while n < gamma and d[bi, n] == t[bi, n]:
+            n += 1
+        out[bi, :n] = d[bi, :n]
+        out[bi, n] = t[bi, n]
+        n_accept[bi] = n
+    return {"t": t, "top1_prob": prob, "n_accept": n_accept, "out_tokens": out}
+
+
+def acceptance_probability(p_x: float, q_x: float) -> float:
+    """a(x) = min(1, p(x) / q(x))  ([P3] "samplingでもtargetの確率分布を保つ",
+    acceptance equation).  Edge readings: p(x) = 0 -> 0; q(x) = 0 < p(x) -> 1."""
+    if p_x <= 0.0:
+        return 0.0
+    if q_x <= 0.0:
+        return 1.0
+    return min(1.0, p_x / q_x)
+
+
+def residual_distribution(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """p'(x) = max(0, p(x) - q(x)) / sum_y max(0, p(y) - q(y))
+    ([P3] same section, residual-distribution equation).  If the sum is 0
+    (impossible after a rejection in exact arithmetic) fall back to p."""
+    r = np.maximum(0.0, p - q)
+    z = r.sum()
+    if z > 0.0:
+        return r / z
+    return p.copy()
+
+
+def sample_inverse_cdf(f: np.ndarray, u: float) -> int:
+    """Smallest j with sum_{k<=j} f_k > u (u in [0, 1)).  If rounding leaves
+    no such j, the last j with f_j > 0.  (Reading: inverse-CDF sampling with a
+    uniform passed in.)"""
+    cdf = np.cumsum(f)
+    hit = np.nonzero(cdf > u)[0]
+    if hit.size:
+        return int(hit[0])
+    return int(np.nonzero(f > 0)[0][-1])
+
+
+def verify_sample(tgt_logits: np.ndarray, drf_logits: np.ndarray,
+                  draft_ids: np.ndarray, u_acc: np.ndarray,
+                  u_fin: np.ndarray) -> dict:
+    """Sampling acceptance with residual resampling.
+
+    [P3] "samplingでもtargetの確率分布を保つ" and its 3-token worked example:
+      p_i = softmax(target logits row i), i = 0..gamma
+      q_i = softmax(draft logits row i),  i = 0..gamma-1
+      a_i = min(1, p_i(d_i) / q_i(d_i)) for every i < gamma
+      n   = first i with u_acc[i] >= a_i (accept iff u < a), else gamma
+      f   = normalised max(0, p_n - q_n) if n < gamma, else p_gamma
+      final token = inverse CDF of f at u_fin
+      out = d_0 .. d_{n-1}, final token, then -1 padding
+    Draft ids outside [0, V) get a = 0.  Returns dict(accept_prob [B, gamma],
+    n_accept [B], out_tokens [B, gamma+1], final_dist [B, V], cdf [B, V]).
+    """
+    b, gp1, v = tgt_logits.shape
+    gamma = gp1 - 1
+    d = np.asarray(draft_ids, dtype=np.int64).reshape(b, gamma)
+    u_acc = np.asarray(u_acc, dtype=np.float64).reshape(b, gamma)
+    u_fin = np.asarray(u_fin, dtype=np.float64).reshape(b)
+    p = softmax_rows(tgt_logits)                       # [B, gamma+1, V]
+    q = softmax_rows(drf_logits) if gamma > 0 else np.zeros((b, 0, v))
+    accept_prob = np.zeros((b, gamma), dtype=np.float64)
+    n_accept = np.zeros(b, dtype=np.int64)
+    out = np.full((b, gp1), -1, dtype=np.int64)
+    final = np.zeros((b, v), dtype=np.float64)
+    for bi in range(b):
+        for i in range(gamma):
+            di = d[bi, i]
+            if 0 <= di < v:
+                accept_prob[bi, i] = acceptance_probability(p[bi, i, di], q[bi, i, di])
+        n = 0
+        while n < gamma and u_acc[bi, n] < accept_prob[bi, n]:
+            n += 1
+        if n < gamma:
+            f = residual_distribution(p[bi, n], q[bi, n])
+        else:
+            f = p[bi, gamma]
+        out[bi, :n] = d[bi, :n]
+        out[bi, n] = sample_inverse_cdf(f, u_fin[bi])
+        n_accept[bi] = n
+        final[bi] = f
+    return {"accept_prob": accept_prob, "n_accept": n_accept,
+            "out_tokens": out, "final_dist": final,
+            "cdf": np.cumsum(final, axis=1)}
+
+
+# --------------------------------------------------------------------------
+# Closed forms used as pins ([P3] "1回のtarget検証で何token進むか").
+# --------------------------------------------------------------------------
+
+def expected_tokens(alpha: float, gamma: int) -> float:
+    """E[T] = 1 + alpha + ... + alpha**gamma, tokens committed per verify when
+    each candidate is accepted independently with probability alpha."""
+    return float(sum(alpha ** i for i in range(gamma + 1)))
+
+
+def overlap_mass(p: np.ndarray, q: np.ndarray) -> float:
+    """beta = sum_x min(p(x), q(x)): probability that a draft x ~ q is accepted
+    under a(x) = min(1, p/q)."""
+    return float(np.minimum(p, q).sum())
+
+
+def accept_length_distribution(betas: list[float]) -> np.ndarray:
+    """P(n = k), k = 0..gamma, for independent per-position acceptance
+    probabilities beta_0..beta_{gamma-1}: prod_{i<k} beta_i * (1 - beta_k) for
+    k < gamma, and prod_{i<gamma} beta_i for k = gamma."""
+    gamma = len(betas)
+    out = np.zeros(gamma + 1)
+    run = 1.0
+    for k in range(gamma):
+        out[k] = run * (1.0 - betas[k])
+        run *= betas[k]
+    out[gamma] = run
+    return out
+
+
+def speedup_model(e_t: float, t_target: float, t_draft: float, gamma: int,
+                  t_verify: float, t_overhead: float = 0.0) -> float:
+    """Rough speedup of one iteration over plain decoding ([P3] "3.36 token進んでも
+    3.36倍速いとは限らない"): E[T] * t_target / (gamma*t_draft + t_verify + t_overhead)."""
+    return e_t * t_target / (gamma * t_draft + t_verify + t_overhead)
