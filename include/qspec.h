@@ -1,0 +1,184 @@
+/*
+ * qspec.h -- C-ABI of libqspec.so, the MI355X (gfx950) hot path of QSpec-style
+ * quantized speculative decoding with one shared INT4 weight set.
+ *
+ * Sources of the operations (pages):
+ *   [P1] qiita.com, "QSpec実行時の2つの量子化による推論の一致率を調べる":
+ *        sections "W4A16", "W4A4" and "QSpec の W4A4 モードと W4A16 モード" --
+ *        one 4-bit weight set, run with 16-bit activations (verify) or with
+ *        activations quantized to 4 bits at compute time (draft).
+ *   [P3] kasblo.com, "Speculative Decodingとは？LLM生成を速くする方法":
+ *        "draft modelとtarget modelの処理フロー" (draft gamma tokens, score gamma+1
+ *        positions, accept left to right, stop at the first mismatch),
+ *        "greedy decodingでは一致するprefixを採用する" (Top-1 prefix match),
+ *        "samplingでもtargetの確率分布を保つ" (a(x) = min(1, p/q) and the residual
+ *        max(0, p - q) normalised), "3 tokenの数値例" (worked example).
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or keeps a pointer after returning.
+ *   - Tensors are dense row-major.  fp16 values travel as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on `stream` and returns; nothing synchronises.
+ *     Buffers must stay alive until that work has completed.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     returned as a negative status; a launch failure returns QS_ERR_HIP.  A
+ *     device-side fault surfaces at the caller's next synchronisation.  Nothing
+ *     is printed and no exception crosses the ABI.
+ *   - No global state besides cached device properties; calls on different
+ *     streams may run concurrently if their output buffers do not overlap.
+ *   - Shapes: K is a multiple of 128 (the weight group) and at most 65536;
+ *     1 <= M <= 256 rows; N >= 1.  Weight buffers are padded to whole 16-row
+ *     blocks (qs_packed_weight_bytes / qs_packed_scale_bytes).
+ *   - Pointers to 16-byte vector data (x, w_packed, logits when V % 4 == 0)
+ *     must be 16-byte aligned, else QS_ERR_MISALIGNED.
+ */
+#ifndef QSPEC_H
+#define QSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QS_OK 0
+#define QS_ERR_INVALID_ARG (-1) /* null pointer, bad shape, bad mode              */
+#define QS_ERR_UNSUPPORTED (-2) /* shape outside the supported range (M > 256)    */
+#define QS_ERR_MISALIGNED (-3)  /* vector-accessed pointer not 16-byte aligned    */
+#define QS_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required     */
+#define QS_ERR_HIP (-5)         /* the HIP runtime reported an error at launch    */
+#define QS_ERR_DEVICE (-6)      /* current device is not a gfx950 (CDNA4) GPU     */
+
+#define QS_GROUP 128   /* k-elements per weight scale group */
+#define QS_MAX_M 256   /* most activation rows per linear call */
+
+typedef enum { QS_W4A16 = 0, QS_W4A4 = 1 } qs_mode;
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* qs_status_string(int status);
+
+/* Bytes of the packed nibble buffer / packed scale buffer for an [N, K] weight. */
+size_t qs_packed_weight_bytes(int N, int K);
+size_t qs_packed_scale_bytes(int N, int K);
+
+/*
+ * qs_pack_weights -- re-lay one logical INT4 weight set into the layout both
+ * linear modes stream ([P1] mode tree: a single 4-bit weight set serves the
+ * W4A4 draft and the W4A16 verify).  Offline step, not on the timed path.
+ *   q        int8 [N][K], codes in [-8, 7] (values outside are clamped)
+ *   s        fp16 [N][K/128], scale of group g = k/128 of row n (symmetric,
+ *            W[n][k] = q[n][k] * s[n][k/128])
+ *   w_packed out, qs_packed_weight_bytes(N, K) bytes, 16-byte aligned
+ *   s_packed out, qs_packed_scale_bytes(N, K) bytes
+ * The packed layout is internal to the library; only the linear calls read it.
+ */
+int qs_pack_weights(const int8_t* q, const uint16_t* s, int N, int K,
+                    uint8_t* w_packed, uint16_t* s_packed, void* stream);
+
+/*
+ * qs_linear_w4a16 -- verify-mode linear ([P1] "W4A16"): 4-bit weights are
+ * expanded inside the kernel and multiplied with fp16 activations on fp16
+ * MFMA with fp32 accumulation; each 128-wide group's partial sum is scaled in
+ * fp32.
+ *   x  fp16 [M][K];  y  fp32 [M][N] (out):  y[m][n] = sum_k x[m][k] * W[n][k]
+ */
+int qs_linear_w4a16(const uint16_t* x, const uint8_t* w_packed,
+                    const uint16_t* s_packed, float* y, int M, int N, int K,
+                    void* stream);
+
+/*
+ * Workspace bytes needed by qs_linear_w4a4 / qs_lmhead for these shapes (0 when
+ * the activation quantization is fused into the GEMM, i.e. for small M).
+ */
+size_t qs_linear_workspace_bytes(int mode, int M, int N, int K);
+
+/*
+ * qs_linear_w4a4 -- draft-mode linear ([P1] "W4A4"): activations are
+ * quantized per token to INT4,
+ *     s_m = fp16(fp32(max_k |x[m][k]|) / 7),  xq = clamp(rint(x / s_m), -8, 7)
+ * (round half to even of the exact quotient; an all-zero row gives s_m = 0 and
+ * xq = 0), then multiplied with the weight codes on int8 MFMA with i32
+ * accumulation per 128-wide group:
+ *     acc[m][n][g] = sum_{k in g} xq[m][k] * q[n][k]
+ *     y[m][n]      = s_m * sum_g s[n][g] * acc[m][n][g]        (fp32)
+ *   x        fp16 [M][K];  y fp32 [M][N] (out)
+ *   xq_out   optional int8 [M][K]   (NULL: not written)
+ *   sx_out   optional fp16 [M]      (NULL: not written)
+ *   acc_out  optional int32 [M][N][K/128] (NULL: not written)
+ *   ws       workspace of at least qs_linear_workspace_bytes(QS_W4A4, M, N, K)
+ *            bytes (may be NULL when that is 0); contents are scratch.
+ */
+int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed,
+                   const uint16_t* s_packed, float* y, int M, int N, int K,
+                   int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_lmhead -- the LM-head projection hidden -> vocabulary logits in either
+ * mode (the pages' per-position next-token distributions, [P1] "結果", come from
+ * it).  Same arithmetic as the linear of that mode with N = V.
+ *   mode     QS_W4A16 or QS_W4A4
+ *   x        fp16 [M][K];  logits fp32 [M][V] (out)
+ *   ws       qs_linear_workspace_bytes(mode, M, V, K) bytes (NULL if 0)
+ */
+int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed,
+              const uint16_t* s_packed, float* logits, int M, int V, int K,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V). */
+size_t qs_verify_workspace_bytes(int B, int gamma, int V);
+
+/*
+ * qs_verify_greedy -- Top-1 and greedy prefix-match acceptance ([P3] greedy
+ * section; [P1] "Speculative Decoding": a mismatching draft token is replaced by
+ * the target's own Top-1).  Per sequence b:
+ *   t[i]      = argmax_j tgt_logits[b][i][j] (lowest index among equal maxima)
+ *   top1_prob = 1 / sum_j exp(l_j - l_max)   (softmax at temperature 1)
+ *   n         = number of leading i < gamma with draft_ids[b][i] == t[i]
+ *   out_tokens[b] = draft_ids[b][0..n-1], t[n], then -1 up to gamma+1 entries
+ * gamma = 0 is a plain Top-1 (the draft step): out_tokens[b][0] = t[0].
+ *   tgt_logits fp32 [B][gamma+1][V];  draft_ids int32 [B][gamma] (ids outside
+ *   [0, V) are mismatches and are never used as addresses; may be NULL if gamma = 0)
+ *   tgt_top1   int32 [B][gamma+1] (out);  top1_prob fp32 [B][gamma+1] (out, nullable)
+ *   n_accept   int32 [B] (out);  out_tokens int32 [B][gamma+1] (out)
+ *   ws         >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch
+ */
+int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
+                     int B, int gamma, int V,
+                     int32_t* tgt_top1, float* top1_prob,
+                     int32_t* n_accept, int32_t* out_tokens,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_verify_sample -- sampling acceptance with residual resampling ([P3]
+ * sampling section and its A/B/C example).  Per sequence b, with
+ * p_i = softmax(tgt_logits[b][i]) (i <= gamma) and q_i = softmax(drf_logits[b][i]):
+ *   a_i = min(1, p_i(d_i) / q_i(d_i)) for every i < gamma
+ *         (p_i(d_i) = 0 -> 0; q_i(d_i) = 0 < p_i(d_i) -> 1; d_i outside [0,V) -> 0)
+ *   n   = first i with u_accept[b][i] >= a_i (accept iff u < a), else gamma
+ *   f   = max(0, p_n - q_n) / sum(max(0, p_n - q_n)) if n < gamma
+ *         (falls back to p_n if that sum is 0), else p_gamma
+ *   y   = smallest j with sum_{k<=j} f_k > u_final[b]  (inverse CDF; if rounding
+ *         leaves none, the last j with f_j > 0)
+ *   out_tokens[b] = d_0..d_{n-1}, y, then -1 padding;  n_accept[b] = n
+ *   tgt_logits fp32 [B][gamma+1][V];  drf_logits fp32 [B][gamma][V]
+ *   draft_ids int32 [B][gamma];  u_accept fp32 [B][gamma] in [0,1);  u_final fp32 [B]
+ *   accept_prob fp32 [B][gamma] (out);  n_accept int32 [B] (out)
+ *   out_tokens int32 [B][gamma+1] (out);  final_dist fp32 [B][V] (out, nullable) = f
+ *   ws >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch
+ * gamma = 0 draws one token from p_0 with u_final (drf_logits, draft_ids,
+ * u_accept and accept_prob may then be NULL).
+ */
+int qs_verify_sample(const float* tgt_logits, const float* drf_logits,
+                     const int32_t* draft_ids, const float* u_accept,
+                     const float* u_final, int B, int gamma, int V,
+                     float* accept_prob, int32_t* n_accept, int32_t* out_tokens,
+                     float* final_dist, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSPEC_H */

@@ -1,0 +1,103 @@
+// Device-side helpers shared by the gfx950 kernels of libqspec: MFMA operand
+// types, the INT4 nibble expansion for both modes, and wave reductions.
+//
+// Packed weight layout (one buffer serves both modes):
+//   The [N, K] code matrix is cut into tiles of 16 rows x 128 k (one scale
+//   group).  Tile (rb, g), rb = n / 16, g = k / 128, is 1024 contiguous bytes at
+//   byte offset (rb * G + g) * 1024, G = K / 128, so a 16-row block streams its
+//   whole K range contiguously.  Inside a tile, wave lane l (0..63) owns the 16
+//   bytes at l * 16: row n = 16 rb + (l & 15), k in [128 g + 32 (l >> 4), +32),
+//   i.e. exactly the B-operand fragment that lane feeds a 16x16 MFMA.  The four
+//   dwords of a lane hold k offsets 0-7, 8-15, 16-23, 24-31; inside a dword the
+//   code of k offset e sits in nibble pos(e) = (e & 1) * 4 + (e >> 1), stored
+//   offset-binary (u = q + 8).  This order lets two AND-OR operations per half
+//   dword produce fp16 pairs already in k order (see unpack_f16x8).
+//   Scales: s_packed[(rb * G + g) * 16 + (n & 15)].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qs {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;
+constexpr int kTileBytes = 1024;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// 8 offset-binary nibbles (one packed dword, layout above) -> 8 fp16 codes q in
+// k order.  (0x6400 | v) is the fp16 value 1024 + v for v < 1024, so
+//   low nibble  : (1024 + u)        - 1032       = q
+//   high nibble : (1024 + 16 u) / 16 - 72        = q
+// Both are exact in fp16.
+__device__ __forceinline__ half8_t unpack_f16x8(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const uint32_t a = (w & 0x000F000Fu) | 0x64006400u;   // k0, k1
+  const uint32_t b = (w & 0x00F000F0u) | 0x64006400u;   // k2, k3
+  const uint32_t c = (w8 & 0x000F000Fu) | 0x64006400u;  // k4, k5
+  const uint32_t d = (w8 & 0x00F000F0u) | 0x64006400u;  // k6, k7
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sc = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off2 = {(_Float16)72.0f, (_Float16)72.0f};
+  const half2_t ha = __builtin_bit_cast(half2_t, a) - off;
+  const half2_t hb = __builtin_bit_cast(half2_t, b) * sc - off2;
+  const half2_t hc = __builtin_bit_cast(half2_t, c) - off;
+  const half2_t hd = __builtin_bit_cast(half2_t, d) * sc - off2;
+  half8_t r;
+  r[0] = ha[0]; r[1] = ha[1]; r[2] = hb[0]; r[3] = hb[1];
+  r[4] = hc[0]; r[5] = hc[1]; r[6] = hd[0]; r[7] = hd[1];
+  return r;
+}
+
+// Two packed dwords (k offsets 0-15 of a lane's slice) -> 16 int8 operands
+// holding 16 * q (two's-complement nibble in the high half of each byte).
+// Byte order of the result, as k offsets: 0,4,1,5, 2,6,3,7, 8,12,9,13, 10,14,11,15.
+// The activation operand is stored in the same order (qs_xq_pos).
+__device__ __forceinline__ int4_t unpack_i8x16(uint32_t w0, uint32_t w1) {
+  const uint32_t t0 = w0 ^ 0x88888888u;  // offset-binary -> two's complement nibbles
+  const uint32_t t1 = w1 ^ 0x88888888u;
+  int4_t r;
+  r[0] = (int)((t0 << 4) & 0xF0F0F0F0u);
+  r[1] = (int)(t0 & 0xF0F0F0F0u);
+  r[2] = (int)((t1 << 4) & 0xF0F0F0F0u);
+  r[3] = (int)(t1 & 0xF0F0F0F0u);
+  return r;
+}
+
+// Byte position, inside a 16-byte activation operand chunk, of k offset j (0..15).
+__host__ __device__ __forceinline__ int xq_pos(int j) {
+  return (j & 8) | ((j & 3) << 1) | ((j >> 2) & 1);
+}
+
+// ---- wave (64-lane) reductions -------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// (value, index) max with the lowest index winning ties.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(i, o, 64);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+}  // namespace qs

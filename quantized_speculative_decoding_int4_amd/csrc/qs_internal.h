@@ -1,0 +1,44 @@
+// Host-side declarations shared by the translation units of libqspec.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qspec.h"
+
+namespace qs {
+
+// Cached facts about the current device (checked once per device).
+struct DeviceInfo {
+  int ok;       // 1 if the device is a gfx950
+  int num_cus;  // compute units
+};
+const DeviceInfo* device_info();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Launch helpers implemented in linear.hip / verify.hip.
+int launch_pack(const int8_t* q, const uint16_t* s, int N, int K, uint8_t* wp,
+                uint16_t* sp, hipStream_t st);
+size_t linear_workspace(int mode, int M, int N, int K);
+int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp,
+                  float* y, int M, int N, int K, int8_t* xq_out, uint16_t* sx_out,
+                  int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t st);
+
+size_t verify_workspace(int B, int gamma, int V);
+int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,
+                         int32_t* t, float* p1, int32_t* n_acc, int32_t* out, void* ws,
+                         hipStream_t st);
+int launch_verify_sample(const float* tgt, const float* drf, const int32_t* d,
+                         const float* u_acc, const float* u_fin, int B, int gamma, int V,
+                         float* a, int32_t* n_acc, int32_t* out, float* fdist, void* ws,
+                         hipStream_t st);
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
+}  // namespace qs

@@ -1,0 +1,106 @@
+"""The C-ABI library loads and exports every function include/qspec.h declares;
+host-side helpers and argument checks work without a GPU (no compute calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qspec.h")
+LIB = os.path.join(ROOT, "quantized_speculative_decoding_int4_amd", "lib", "libqspec.so")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qs_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libqspec.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_six_calls():
+    names = _declared_functions()
+    for n in ("qs_pack_weights", "qs_linear_w4a16", "qs_linear_w4a4", "qs_lmhead",
+              "qs_verify_greedy", "qs_verify_sample"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert missing == []
+
+
+def test_status_strings(lib):
+    f = lib.qs_status_string
+    f.restype = ctypes.c_char_p
+    f.argtypes = [ctypes.c_int]
+    assert f(0) == b"ok"
+    for code in (-1, -2, -3, -4, -5, -6):
+        assert f(code) and f(code) != b"unknown status"
+    assert f(12345) == b"unknown status"
+
+
+def test_size_helpers(lib):
+    wb = lib.qs_packed_weight_bytes
+    sb = lib.qs_packed_scale_bytes
+    for f in (wb, sb):
+        f.restype = ctypes.c_size_t
+        f.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert wb(4096, 4096) == 4096 * 4096 // 2
+    assert sb(4096, 4096) == 4096 * 32 * 2
+    assert wb(128256, 4096) == 262668288          # LM-head nibbles
+    assert sb(128256, 4096) == 8208384            # LM-head scales
+    assert wb(17, 128) == 32 * 128 // 2          # padded to whole 16-row blocks
+    assert wb(16, 100) == 0 and wb(0, 128) == 0
+
+
+def test_verify_workspace_helper(lib):
+    f = lib.qs_verify_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int] * 3
+    assert f(1, 3, 128256) > 0
+    assert f(0, 3, 10) == 0 and f(1, -1, 10) == 0 and f(1, 64, 10) == 0
+
+
+def test_argument_errors_before_any_device_work(lib):
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lin = lib.qs_linear_w4a16
+    lin.argtypes = [p, p, p, p, i, i, i, p]
+    lin.restype = i
+    fake = 1 << 20  # never dereferenced: the checks fail first
+    assert lin(None, fake, fake, fake, 4, 4096, 4096, None) == -1
+    assert lin(fake, fake, fake, fake, 4, 4096, 4000, None) == -1     # K % 128 != 0
+    assert lin(fake, fake, fake, fake, 0, 4096, 4096, None) == -1     # M < 1
+    assert lin(fake, fake, fake, fake, 257, 4096, 4096, None) == -2   # M > 256
+    assert lin(fake + 8, fake, fake, fake, 4, 4096, 4096, None) == -3  # misaligned x
+    w4 = lib.qs_linear_w4a4
+    w4.argtypes = [p, p, p, p, i, i, i, p, p, p, p, sz, p]
+    w4.restype = i
+    assert w4(fake, fake, fake, fake, 64, 4096, 4096, None, None, None, None, 0, None) == -4
+    vg = lib.qs_verify_greedy
+    vg.argtypes = [p, p, i, i, i, p, p, p, p, p, sz, p]
+    vg.restype = i
+    assert vg(fake, fake, 1, 64, 10, fake, None, fake, fake, fake, 1 << 20, None) == -2  # gamma > 63
+    assert vg(fake, fake, 1, 3, 10, fake, None, fake, fake, None, 0, None) == -4
+    assert vg(fake, None, 1, 3, 10, fake, None, fake, fake, fake, 1 << 20, None) == -1   # draft ids
+
+
+def test_no_gpu_means_device_error(lib):
+    """Valid arguments on a machine without a gfx950 device report QS_ERR_DEVICE
+    (the library never falls back to another device or to the host)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    p, i = ctypes.c_void_p, ctypes.c_int
+    lin = lib.qs_linear_w4a16
+    lin.argtypes = [p, p, p, p, i, i, i, p]
+    lin.restype = i
+    fake = 1 << 20
+    assert lin(fake, fake, fake, fake, 4, 4096, 4096, None) == -6

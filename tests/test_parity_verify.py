@@ -1,0 +1,227 @@
+"""GPU parity of qs_verify_greedy / qs_verify_sample against the CPU oracle on
+the same fp32 logits, plus the pages' worked example and distribution checks
+run through the kernels."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qspec_oracle as O
+from quantized_speculative_decoding_int4_amd import workloads as W
+from tests.gpu_util import PROB_ABS, TIE_TAU, dev, host
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def qs():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from quantized_speculative_decoding_int4_amd import qspec
+    return qspec
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _log32(p):
+    return np.log(np.asarray(p, dtype=np.float64)).astype(np.float32)
+
+
+# ---------------------------------------------------------------- greedy
+
+def _check_greedy(qs, tg, d):
+    r = qs.qs_verify_greedy(dev(tg), dev(d.astype(np.int32)))
+    ref = O.verify_greedy(tg, d)
+    assert np.array_equal(host(r["tgt_top1"]), ref["t"]), "Top-1"
+    assert np.abs(host(r["top1_prob"]) - ref["top1_prob"]).max() <= PROB_ABS
+    assert np.array_equal(host(r["n_accept"]), ref["n_accept"])
+    assert np.array_equal(host(r["out_tokens"]), ref["out_tokens"])
+    return r, ref
+
+
+@pytest.mark.parametrize("b,gamma,v,sigma", [
+    (1, 3, 3, 1.0), (8, 3, 32, 1.0), (5, 0, 1000, 2.0), (3, 5, 5000, 3.0),
+    (1, 3, 128256, 5.24), (16, 7, 128256, 5.24),
+])
+def test_greedy_random(qs, b, gamma, v, sigma):
+    print(f"greedy b={b} gamma={gamma} v={v}", flush=True)
+    rng = W.rng_for(400 + v + gamma)
+    tg = W.logits(rng, (b, gamma + 1, v), sigma=sigma)
+    t_ref, _ = O.top1(tg.reshape(-1, v))
+    d = W.agreeing_ids(rng, t_ref.reshape(b, gamma + 1)[:, :gamma], v, agree_p=0.96)
+    _check_greedy(qs, tg, d)
+
+
+def test_greedy_worked_examples(qs):
+    for case in _golden("greedy_examples.json")["cases"]:
+        vocab = case["vocab"]
+        ids = {w: i for i, w in enumerate(vocab)}
+        d = np.array([[ids[w] for w in case["draft"]]])
+        t_ids = [ids[w] for w in case["target_argmax"]]
+        tg = np.zeros((1, len(t_ids), len(vocab)), np.float32)
+        for i, t in enumerate(t_ids):
+            tg[0, i, t] = 1.0
+        r, _ = _check_greedy(qs, tg, d)
+        committed = [vocab[i] for i in host(r["out_tokens"])[0] if i >= 0]
+        assert committed == case["committed"]
+
+
+def test_greedy_ties_across_chunks_and_bad_ids(qs):
+    v = 20000
+    tg = np.zeros((2, 3, v), np.float32)
+    tg[:, :, [9000, 100, 5000, 19999]] = 3.0          # four equal maxima in different chunks
+    tg[1, 1, 12345] = 4.0
+    d = np.array([[100, -7], [100, v + 3]])
+    r, _ = _check_greedy(qs, tg, d)
+    assert host(r["tgt_top1"]).tolist() == [[100, 100, 100], [100, 12345, 100]]
+    assert host(r["n_accept"]).tolist() == [1, 1]
+
+
+def test_greedy_unaligned_vocab(qs):
+    rng = W.rng_for(401)
+    tg = W.logits(rng, (4, 4, 4099), sigma=2.0)
+    d = rng.integers(0, 4099, size=(4, 3)).astype(np.int32)
+    d[:, 0] = O.top1(tg[:, 0])[0]
+    _check_greedy(qs, tg, d)
+
+
+# ---------------------------------------------------------------- sampling
+
+def _check_sample(qs, tg, dr, d, ua, uf, want_final=True):
+    """Exact agreement except for decisions the oracle itself marks as
+    tie-ambiguous (uniform within TIE_TAU of a threshold)."""
+    b, gp1, v = tg.shape
+    gamma = gp1 - 1
+    r = qs.qs_verify_sample(dev(tg), dev(dr) if gamma else None, dev(d.astype(np.int32)) if gamma else None,
+                            dev(ua) if gamma else None, dev(uf), want_final_dist=want_final)
+    ref = O.verify_sample(tg, dr, d, ua, uf)
+    a = host(r["accept_prob"]) if gamma else np.zeros((b, 0))
+    assert np.abs(a - ref["accept_prob"]).max(initial=0) <= PROB_ABS, "accept probabilities"
+    n = host(r["n_accept"])
+    out = host(r["out_tokens"])
+    ambiguous = 0
+    for bi in range(b):
+        if n[bi] != ref["n_accept"][bi]:
+            k = min(n[bi], ref["n_accept"][bi])
+            assert abs(float(ua[bi, k]) - ref["accept_prob"][bi, k]) <= TIE_TAU, f"seq {bi}: n"
+            ambiguous += 1
+            continue
+        nn = n[bi]
+        assert np.array_equal(out[bi, :nn], ref["out_tokens"][bi, :nn])
+        assert np.all(out[bi, nn + 1:] == -1)
+        y, y_ref = out[bi, nn], ref["out_tokens"][bi, nn]
+        if y != y_ref:
+            cdf = ref["cdf"][bi]
+            lo = cdf[y - 1] if y > 0 else 0.0
+            ok = 0 <= y < v and lo <= uf[bi] + TIE_TAU and cdf[y] >= uf[bi] - TIE_TAU
+            assert ok, f"seq {bi}: token {y} vs {y_ref}"
+            ambiguous += 1
+        if want_final:
+            fd = host(r["final_dist"])[bi]
+            assert np.abs(fd - ref["final_dist"][bi]).max() <= PROB_ABS, f"seq {bi}: final dist"
+    return r, ref, ambiguous
+
+
+def test_sample_abc_worked_example(qs):
+    g = _golden("abc_example.json")
+    lp, lq = _log32(g["p_target"]), _log32(g["q_draft"])
+    a_idx = g["tokens"].index(g["proposed"])
+    tg = np.stack([np.stack([lp, lp])] * 4)
+    dr = np.stack([lq[None]] * 4)
+    d = np.full((4, 1), a_idx)
+    ua = np.array([[0.5], [0.9], [0.74], [0.76]], np.float32)
+    uf = np.array([0.1, 0.3, 0.9, 0.999], np.float32)
+    r, ref, amb = _check_sample(qs, tg, dr, d, ua, uf)
+    assert amb == 0
+    assert np.allclose(host(r["accept_prob"]), g["accept_probability"], atol=1e-6)
+    assert host(r["n_accept"]).tolist() == [1, 0, 1, 0]
+    res_tok = g["tokens"].index(g["residual_token"])
+    assert host(r["out_tokens"])[1, 0] == res_tok and host(r["out_tokens"])[3, 0] == res_tok
+    expect_res = np.array(g["residual_unnormalised"]) / sum(g["residual_unnormalised"])
+    assert np.allclose(host(r["final_dist"])[1], expect_res, atol=1e-6)
+
+
+@pytest.mark.parametrize("b,gamma,v", [(64, 3, 32), (6, 0, 1000), (8, 2, 5003), (1, 3, 128256),
+                                       (16, 7, 128256)])
+def test_sample_random(qs, b, gamma, v):
+    print(f"sample b={b} gamma={gamma} v={v}", flush=True)
+    total_amb = 0
+    for seed in range(3):
+        rng = W.rng_for(500 + 10 * v + seed)
+        tg = W.logits(rng, (b, gamma + 1, v), sigma=5.24 if v > 10000 else 1.5)
+        dr = W.perturb(rng, tg[:, :gamma], sigma=0.3)
+        q = O.softmax_rows(dr) if gamma else np.zeros((b, 0, v))
+        ud = rng.random((b, gamma))
+        d = np.zeros((b, gamma), np.int64)
+        for bi in range(b):
+            for i in range(gamma):
+                d[bi, i] = O.sample_inverse_cdf(q[bi, i], ud[bi, i])
+        ua = W.uniforms(rng, (b, gamma))
+        uf = W.uniforms(rng, (b,))
+        _, _, amb = _check_sample(qs, tg, dr, d, ua, uf, want_final=v <= 5003 or seed == 0)
+        total_amb += amb
+    print(f"  tie-ambiguous sequences: {total_amb}")
+    assert total_amb <= max(1, b * 3 // 50)
+
+
+def test_sample_bad_draft_ids(qs):
+    rng = W.rng_for(600)
+    tg = W.logits(rng, (3, 3, 50))
+    dr = W.perturb(rng, tg[:, :2])
+    d = np.array([[-1, 3], [50, 2], [7, 1000]])
+    ua = np.zeros((3, 2), np.float32)
+    uf = W.uniforms(rng, (3,))
+    r, ref, _ = _check_sample(qs, tg, dr, d, ua, uf)
+    assert host(r["accept_prob"])[0, 0] == 0 and host(r["accept_prob"])[1, 0] == 0
+    assert host(r["accept_prob"])[2, 1] == 0
+
+
+def test_sample_distribution_by_enumeration(qs):
+    """gamma = 1, 3-token vocab: enumerate draft d (weight q(d)) and (u_acc, u_fin)
+    on a G x G midpoint grid in one launch; the first committed token must follow p."""
+    g = _golden("abc_example.json")
+    G = 160
+    for p, qv in ((g["p_target"], g["q_draft"]), ([0.1, 0.2, 0.7], [0.6, 0.3, 0.1])):
+        lp, lq = _log32(p), _log32(qv)
+        us = ((np.arange(G) + 0.5) / G).astype(np.float32)
+        dd, aa, ff = np.meshgrid(np.arange(3), us, us, indexing="ij")
+        b = dd.size
+        tg = np.broadcast_to(np.stack([lp, lp]), (b, 2, 3)).copy()
+        dr = np.broadcast_to(lq[None], (b, 1, 3)).copy()
+        r = qs.qs_verify_sample(dev(tg), dev(dr), dev(dd.reshape(b, 1).astype(np.int32)),
+                                dev(aa.reshape(b, 1).copy()), dev(ff.reshape(b).copy()))
+        first = host(r["out_tokens"])[:, 0]
+        w = np.asarray(qv)[dd.reshape(b)] / G ** 2
+        dist = np.bincount(first, weights=w, minlength=3)
+        assert np.allclose(dist, p, atol=2.0 / G), dist
+
+
+def test_sample_monte_carlo_expected_tokens(qs):
+    """gamma = 4, p = (0.2, 0.6, 0.2), q = (0.4, 0.4, 0.2): beta = 0.8 at every
+    position; drafts drawn from q; 10^6 sequences in one launch.  Mean committed
+    tokens must be E[T] = 3.3616 within 4 standard errors."""
+    e_t = _golden("expected_tokens.json")["cases"][0]
+    gamma = e_t["gamma"]
+    p = np.array([0.2, 0.6, 0.2])
+    q = np.array([0.4, 0.4, 0.2])
+    b = 1_000_000
+    rng = W.rng_for(700)
+    tg = np.broadcast_to(_log32(p), (b, gamma + 1, 3)).copy()
+    dr = np.broadcast_to(_log32(q), (b, gamma, 3)).copy()
+    d = np.searchsorted(np.cumsum(q), rng.random((b, gamma)), side="right").astype(np.int32)
+    r = qs.qs_verify_sample(dev(tg), dev(dr), dev(d), dev(W.uniforms(rng, (b, gamma))),
+                            dev(W.uniforms(rng, (b,))))
+    t = host(r["n_accept"]).astype(np.float64) + 1
+    se = t.std() / np.sqrt(b)
+    print(f"mean committed {t.mean():.5f} (E[T] {e_t['expected_tokens']}, SE {se:.2e})")
+    assert abs(t.mean() - e_t["expected_tokens"]) <= 4 * se
+    # committed tokens always a valid prefix + one token
+    out = host(r["out_tokens"])
+    n = host(r["n_accept"])
+    assert np.all(out[np.arange(b), n] >= 0)
