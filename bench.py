@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""One speculative-decoding iteration of the QSpec hot path on one MI355X.
+
+Workload: the Llama-3-8B-shaped INT4 linear stack (32 layers of fused q|k|v,
+o, fused gate|up, down; group-128 INT4 weights, random init, shared by both
+modes) plus the 4096 -> 128256 LM-head.  One step = one iteration at batch 1
+with draft length 3:
+  3 x [W4A4 draft pass at M = 1 -> draft Top-1]        (sequential draft phase)
+  1 x  W4A16 verify pass at M = 4                      (target scores 4 positions)
+  greedy accept + sampling accept over the 4 positions (V = 128256)
+Each phase is captured once as a HIP graph and replayed; HIP events between
+the phases time them.
+
+Printed JSON line: `value` = verify-pass weight GB/s (3,869,589,504 weight
+bytes per pass / verify-pass time), plus draft-pass rates, accept positions/s,
+the roofline of the dominant kernel (the W4A16 gate|up linear of the verify
+pass, timed with HIP events around each launch) and the CPU oracle baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verify-pass weight GB/s (% HBM peak) at M=4; accept positions/sec"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(budget_s: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the verify
+    pass: W4A16 linears of one layer's shapes, then LM-head row blocks, at
+    M = 4, until about budget_s seconds of work.  Rate in weight GB/s."""
+    import numpy as np
+
+    from oracle import qspec_oracle as O
+    from quantized_speculative_decoding_int4_amd import workloads as W
+
+    rng = W.rng_for(11)
+    layer = [s for s in W.stack_shapes(1) if not s[0].startswith("lm")]
+    head_block = ("lm_head_rows", 8192, W.HIDDEN)
+    # the pass's own mix: per layer q|k|v, o, gate|up, down; LM-head row blocks in between
+    shapes = (layer + [head_block]) * 1000
+    done_bytes, t_used, items = 0, 0.0, []
+    for name, n, k in shapes:
+        q, s = W.int4_weights(rng, n, k)
+        x, _ = W.activations(rng, 4, k)
+        t0 = time.perf_counter()
+        O.linear_w4a16(x, q, s)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        done_bytes += n * k // 2 + n * (k // 128) * 2
+        items.append(name)
+        if t_used >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": done_bytes / t_used / 1e9,
+        "unit": "GB/s",
+        "cores": min(threads, cores),
+        "kind": "oracle",
+        "sample": (f"oracle W4A16 linears at M=4 on {len(items)} weight blocks "
+                   f"({done_bytes / 1e9:.3f} GB of packed-equivalent weights: repeated q|k|v, o, gate|up, "
+                   f"down and an 8192-row LM-head block) in {t_used:.1f} s; float64 NumPy, "
+                   f"BLAS threads {threads}, affinity cores {cores}"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_speculative_decoding_int4_amd import qspec as qs
+    from quantized_speculative_decoding_int4_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    V, H, GAMMA = W.VOCAB, W.HIDDEN, 3
+    M_VERIFY = GAMMA + 1
+
+    # ---------------- weights (random init, generated and packed on the GPU)
+    t0 = time.perf_counter()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    shapes = W.stack_shapes()
+    layers, pass_bytes = [], 0
+    for name, n, k in shapes:
+        q, s = W.int4_weights_device(gen, n, k, device=dev)
+        wp, sp = qs.qs_pack_weights(q, s)
+        del q, s
+        layers.append((wp, sp, n, k, 1.0))
+        pass_bytes += n * k // 2 + n * (k // 128) * 2
+    torch.cuda.synchronize()
+    chain = qs.Chain(layers)
+    log(f"packed {len(shapes)} linears, {pass_bytes} weight bytes per pass, {time.perf_counter() - t0:.1f} s")
+
+    # ---------------- inputs and buffers
+    rng = W.rng_for(3)
+    x_np, _ = W.activations(rng, M_VERIFY, H)
+    x_verify = torch.from_numpy(x_np).to(dev)
+    x_draft = [x_verify[i:i + 1] for i in range(GAMMA)]
+    logits_q = torch.empty((1, GAMMA, V), dtype=torch.float32, device=dev)
+    logits_p = torch.empty((1, M_VERIFY, V), dtype=torch.float32, device=dev)
+    d = torch.zeros((1, GAMMA), dtype=torch.int32, device=dev)
+    u_acc = torch.from_numpy(W.uniforms(rng, (1, GAMMA))).to(dev)
+    u_fin = torch.from_numpy(W.uniforms(rng, (1,))).to(dev)
+    ws_draft = torch.empty(chain.workspace_bytes(qs.QS_W4A4, 1), dtype=torch.uint8, device=dev)
+    ws_verify = torch.empty(chain.workspace_bytes(qs.QS_W4A16, M_VERIFY), dtype=torch.uint8, device=dev)
+    ws_acc = torch.empty(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
+    ws_acc2 = torch.empty(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
+    draft_out = [{
+        "tgt_top1": torch.empty((1, 1), dtype=torch.int32, device=dev), "top1_prob": None,
+        "n_accept": torch.empty((1,), dtype=torch.int32, device=dev), "out_tokens": d[:, i:i + 1],
+    } for i in range(GAMMA)]
+    greedy_out = {
+        "tgt_top1": torch.empty((1, M_VERIFY), dtype=torch.int32, device=dev),
+        "top1_prob": torch.empty((1, M_VERIFY), dtype=torch.float32, device=dev),
+        "n_accept": torch.empty((1,), dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty((1, M_VERIFY), dtype=torch.int32, device=dev),
+    }
+    sample_out = {
+        "accept_prob": torch.empty((1, GAMMA), dtype=torch.float32, device=dev),
+        "n_accept": torch.empty((1,), dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty((1, M_VERIFY), dtype=torch.int32, device=dev),
+        "final_dist": None,
+    }
+
+    def draft_phase():
+        for i in range(GAMMA):
+            qs.qs_chain_forward(qs.QS_W4A4, x_draft[i], chain, out=logits_q[0, i:i + 1], ws=ws_draft)
+            qs.qs_verify_greedy(logits_q[:, i:i + 1], None, out=draft_out[i], ws=ws_acc)
+
+    def verify_phase():
+        qs.qs_chain_forward(qs.QS_W4A16, x_verify, chain, out=logits_p[0], ws=ws_verify)
+
+    def accept_phase():
+        qs.qs_verify_greedy(logits_p, d, out=greedy_out, ws=ws_acc)
+        qs.qs_verify_sample(logits_p, logits_q, d, u_acc, u_fin, out=sample_out, ws=ws_acc2)
+
+    phases = [draft_phase, verify_phase, accept_phase]
+    for f in phases:  # eager warm-up (caches device info / kernel attributes)
+        f()
+    torch.cuda.synchronize()
+    if not args.eager:
+        graphs = []
+        for f in phases:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        runners = [g.replay for g in graphs]
+    else:
+        runners = phases
+    log("graphs captured" if not args.eager else "eager mode")
+
+    def step():
+        for r in runners:
+            r()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region: exactly `steps` iterations
+    K = args.steps
+    E = torch.cuda.Event
+    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        runners[0]()
+        ev[i][1].record()
+        runners[1]()
+        ev[i][2].record()
+        runners[2]()
+        ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    draft_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    verify_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    accept_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    verify_gbs = pass_bytes / (verify_ms * 1e-3) / 1e9
+    draft_gbs = GAMMA * pass_bytes / (draft_ms * 1e-3) / 1e9
+    log(f"step {ms_step:.3f} ms (wall {wall / K * 1e3:.3f}); draft {draft_ms:.3f} verify {verify_ms:.3f} "
+        f"accept {accept_ms:.3f} ms; verify {verify_gbs:.0f} GB/s, draft {draft_gbs:.0f} GB/s")
+    n_acc = int(greedy_out["n_accept"].item())
+    assert bool(torch.isfinite(logits_p).all()) and bool(torch.isfinite(logits_q).all()), "non-finite logits"
+    agree = float((greedy_out["tgt_top1"][:, :GAMMA] == d).float().mean().item())
+
+    # ---------------- accept throughput at the batched-verify scale (B=16, gamma=7)
+    def time_calls(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    accept = {}
+    for (B, G) in ((1, GAMMA), (16, 7)):
+        tg = torch.from_numpy(W.logits(rng, (B, G + 1, V), sigma=5.24)).to(dev)
+        dr = torch.from_numpy(W.perturb(rng, tg[:, :G].cpu().numpy())).to(dev)
+        dd = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
+        ua = torch.from_numpy(W.uniforms(rng, (B, G))).to(dev)
+        uf = torch.from_numpy(W.uniforms(rng, (B,))).to(dev)
+        wsg = torch.empty(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+        go = qs.qs_verify_greedy(tg, dd, ws=wsg)
+        so = qs.qs_verify_sample(tg, dr, dd, ua, uf, ws=wsg)
+        tgms = time_calls(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg))
+        tsms = time_calls(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg))
+        pos = B * (G + 1)
+        accept[f"B{B}_gamma{G}"] = {
+            "positions": pos,
+            "greedy_us": tgms * 1e3, "greedy_positions_per_s": pos / (tgms * 1e-3),
+            "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
+            "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
+        }
+        del tg, dr, wsg
+
+    # ---------------- roofline of the dominant kernel: W4A16 gate|up at M = 4
+    gu = [(wp, sp, n, k) for (wp, sp, n, k, _), (nm, _, _) in zip(layers, shapes) if nm.endswith("gateup")]
+    y_gu = torch.empty((M_VERIFY, gu[0][2]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    durs = []
+    for rep in range(3):
+        evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in gu]
+        for (wp, sp, n, k), (a, b) in zip(gu, evs):
+            a.record(stream)
+            qs.qs_linear_w4a16(x_verify, wp, sp, n, y=y_gu)
+            b.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            durs += [a.elapsed_time(b) for a, b in evs]
+    n_gu, k_gu = gu[0][2], gu[0][3]
+    gu_bytes = n_gu * k_gu // 2 + n_gu * (k_gu // 128) * 2
+    gu_ms = float(np.mean(durs))
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "linear_stream_kernel<W4A16, MT=1, S=4, LDS> (gate|up 4096->28672, M=4)",
+                "bytes_per_launch": gu_bytes, "avg_launch_us": gu_ms * 1e3, "launches": len(durs)}
+    log(f"gate|up W4A16 M=4: {gu_ms * 1e3:.2f} us/launch, {achieved:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline(args.cpu_budget_s)
+
+    result = {
+        "metric": METRIC,
+        "value": verify_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("Llama-3-8B-shaped INT4 (group-128, fp16 scales) 32-layer linear stack + 4096->128256 "
+                         "LM-head; one speculative iteration at batch 1, gamma 3: 3 W4A4 draft passes (M=1, "
+                         "int8 MFMA), 1 W4A16 verify pass (M=4, fp16 MFMA), greedy + sampling accept"),
+            "verify_rows": M_VERIFY, "gamma": GAMMA, "batch": 1, "vocab": V,
+            "weight_bytes_per_pass": pass_bytes, "graphs": not args.eager,
+        },
+        "hbm_frac": verify_gbs / HBM_PEAK_GBS,
+        "verify_pass_ms": verify_ms,
+        "draft_pass_ms": draft_ms / GAMMA,
+        "draft_pass_GBps": draft_gbs,
+        "accept_phase_ms": accept_ms,
+        "iteration_accepted_tokens": n_acc + 1,
+        "draft_verify_top1_agreement": agree,
+        "accept_positions_per_s": accept,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

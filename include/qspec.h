@@ -127,6 +127,41 @@ int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed,
               const uint16_t* s_packed, float* logits, int M, int V, int K,
               void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * One linear of a chain (see qs_chain_forward).  Weights come from
+ * qs_pack_weights; the struct itself is read on the host during the call.
+ */
+typedef struct qs_linear_desc {
+  const uint8_t* w_packed;   /* packed codes of an [N, K] weight set          */
+  const uint16_t* s_packed;  /* packed group scales                            */
+  int N;                     /* output features                                */
+  int K;                     /* input features (multiple of 128)               */
+  float out_scale;           /* gain on this output when it feeds the next one */
+} qs_linear_desc;
+
+/* Workspace bytes needed by qs_chain_forward for this chain at M rows. */
+size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, int n);
+
+/*
+ * qs_chain_forward -- one forward pass of a stack of quantized linears in one
+ * mode: the W4A4 draft pass at M = batch rows or the W4A16 verify pass at
+ * M = batch * (gamma + 1) rows, where the target scores all candidate positions
+ * in a single pass ([P3] "draft modelとtarget modelの処理フロー"; [P1] mode tree).
+ * The pages give no layer internals, so the chain is linears only:
+ *   stage 0 reads x fp16 [M][chain[0].K];
+ *   stage i > 0 reads the first chain[i].K columns (row stride chain[i-1].N) of
+ *     stage i-1's output, kept as fp16(out_scale * y) in the workspace, and
+ *     standardises each row over those columns, fp16((v - mean) / std) with the
+ *     population std (rows with zero spread become zeros), standing in for the
+ *     normalisation between real layers (requires chain[i].K <= chain[i-1].N);
+ *   the last stage writes fp32 out [M][chain[n-1].N] (its out_scale is unused).
+ * With chain = n_layers x {q|k|v, o, gate|up, down} + LM-head this is the
+ * Llama-shaped pass: o reads the q columns, down reads the gate columns.
+ *   ws  >= qs_chain_workspace_bytes(mode, M, chain, n) bytes of scratch
+ */
+int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n,
+                     float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V). */
 size_t qs_verify_workspace_bytes(int B, int gamma, int V);
 

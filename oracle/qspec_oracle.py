@@ -163,6 +163,54 @@ def lm_head(mode: str, x: np.ndarray, q: np.ndarray, s: np.ndarray,
     return out
 
 
+def standardize_rows(y: np.ndarray) -> np.ndarray:
+    """Row-wise (y - mean) / std over the columns given (population std), then
+    rounded to fp16; a row with zero spread maps to zeros.  float64 arithmetic.
+
+    Reading (the pages give no layer internals): this stands in for the
+    normalisation between the linears of the synthetic stack, like a layer norm
+    without learned affine parameters.  It keeps activations well scaled over
+    many stages for weight codes uniform on [-8, 7], whose mean of -0.5 would
+    otherwise amplify the all-ones direction stage after stage."""
+    y64 = np.asarray(y, dtype=np.float64)
+    mu = y64.mean(axis=1, keepdims=True)
+    sd = np.sqrt(((y64 - mu) ** 2).mean(axis=1, keepdims=True))
+    out = np.zeros_like(y64)
+    ok = sd[:, 0] > 0
+    out[ok] = (y64[ok] - mu[ok]) / sd[ok]
+    return out.astype(np.float16)
+
+
+def chain_forward(mode: str, x: np.ndarray, layers) -> np.ndarray:
+    """One forward pass of a stack of quantized linears in one mode.
+
+    Reading for the synthetic stack (the pages give no layer internals):
+    stage 0 reads x; stage i > 0 reads the first K_i columns of the previous
+    stage's output, kept as fp16 and standardised per row (standardize_rows);
+    the last stage's output is returned unrounded.  layers: sequence of (q, s).
+    [P3] "draft modelとtarget modelの処理フロー": a pass scores all of its rows
+    (candidate positions) at once.
+    """
+    cur = x
+    n_layers = len(layers)
+    y = None
+    for i, layer in enumerate(layers):
+        q, s = layer[0], layer[1]
+        k = q.shape[1]
+        xin = np.ascontiguousarray(cur[:, :k])
+        if i > 0:
+            xin = standardize_rows(xin)
+        if mode == "w4a16":
+            y = linear_w4a16(xin, q, s)
+        elif mode == "w4a4":
+            y = linear_w4a4(xin, q, s)["y"]
+        else:
+            raise ValueError(mode)
+        if i + 1 < n_layers:
+            cur = y.astype(np.float16)
+    return y
+
+
 # --------------------------------------------------------------------------
 # Next-token distributions and Top-1.
 # [P3] "通常のLLM生成はなぜ逐次処理になるのか": the model gives a distribution

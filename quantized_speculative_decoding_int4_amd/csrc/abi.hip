@@ -92,7 +92,7 @@ int qs_linear_w4a16(const uint16_t* x, const uint8_t* w_packed, const uint16_t* 
 
 size_t qs_linear_workspace_bytes(int mode, int M, int N, int K) {
   if ((mode != QS_W4A16 && mode != QS_W4A4) || !linear_shape_ok(M, N, K) || M > QS_MAX_M) return 0;
-  return linear_workspace(mode, M, N, K);
+  return linear_workspace(mode, M, N, K, false);
 }
 
 int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed, float* y, int M,
@@ -103,7 +103,7 @@ int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed, const uint16_t* s
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w_packed)) return QS_ERR_MISALIGNED;
   if (xq_out && ((reinterpret_cast<uintptr_t>(xq_out) & 7u) != 0)) return QS_ERR_MISALIGNED;
-  const size_t need = linear_workspace(QS_W4A4, M, N, K);
+  const size_t need = linear_workspace(QS_W4A4, M, N, K, false);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QS_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return QS_ERR_MISALIGNED;
   if (!device_info()->ok) return QS_ERR_DEVICE;

@@ -1,0 +1,88 @@
+// qs_chain_forward: one forward pass of a stack of quantized linears (the draft
+// pass in W4A4 or the verify pass in W4A16), launched linear by linear on one
+// stream.  Intermediate activations stay in the workspace as fp16; each stage
+// after the first standardises its input rows inside its own prologue; only the
+// final stage (the LM-head) writes fp32.
+
+#include "qs_internal.h"
+
+namespace qs {
+
+static bool chain_ok(const qs_linear_desc* c, int n) {
+  if (!c || n < 1) return false;
+  for (int i = 0; i < n; ++i) {
+    if (!c[i].w_packed || !c[i].s_packed || c[i].N < 1 || c[i].K < QS_GROUP || c[i].K % QS_GROUP ||
+        c[i].K > 65536)
+      return false;
+    if (!aligned16(c[i].w_packed)) return false;
+    if (i > 0 && (c[i].K > c[i - 1].N || c[i - 1].N % 8)) return false;
+  }
+  return true;
+}
+
+static size_t act_bytes(int M, const qs_linear_desc* c, int n) {
+  int maxn = 8;
+  for (int i = 0; i + 1 < n; ++i) maxn = c[i].N > maxn ? c[i].N : maxn;
+  return align_up((size_t)M * maxn * 2, 256);
+}
+
+size_t chain_workspace(int mode, int M, const qs_linear_desc* c, int n) {
+  size_t q = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t w = linear_workspace(mode, M, c[i].N, c[i].K, i > 0);
+    q = w > q ? w : q;
+  }
+  return 2 * act_bytes(M, c, n) + q;
+}
+
+}  // namespace qs
+
+using namespace qs;
+
+extern "C" {
+
+size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, int n) {
+  if ((mode != QS_W4A16 && mode != QS_W4A4) || M < 1 || M > QS_MAX_M || !chain_ok(chain, n)) return 0;
+  return chain_workspace(mode, M, chain, n);
+}
+
+int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (!x || !out || !chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
+  if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
+  if (!aligned16(x)) return QS_ERR_MISALIGNED;
+  const size_t need = chain_workspace(mode, M, chain, n);
+  if (!ws || ws_bytes < need) return QS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QS_ERR_MISALIGNED;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t ab = act_bytes(M, chain, n);
+  uint16_t* buf[2] = {reinterpret_cast<uint16_t*>(ws),
+                      reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + ab)};
+  void* qws = static_cast<unsigned char*>(ws) + 2 * ab;
+  const size_t qws_bytes = ws_bytes - 2 * ab;
+  const uint16_t* in = x;
+  int ldx = chain[0].K;
+  for (int i = 0; i < n; ++i) {
+    LinearIO io{};
+    io.x = in;
+    io.ldx = ldx;
+    io.norm_in = i > 0;
+    if (i + 1 == n) {
+      io.y = out;
+    } else {
+      io.y16 = buf[i & 1];
+      io.out_scale = chain[i].out_scale;
+      io.ldy = chain[i].N;
+    }
+    const int rc = launch_linear_io(mode, io, chain[i].w_packed, chain[i].s_packed, M, chain[i].N, chain[i].K,
+                                    nullptr, nullptr, nullptr, qws, qws_bytes, st);
+    if (rc != QS_OK) return rc;
+    in = buf[i & 1];
+    ldx = chain[i].N;
+  }
+  return QS_OK;
+}
+
+}  // extern "C"

@@ -96,32 +96,105 @@ __device__ __forceinline__ void quant_block8(const uint4 v, float s, uint2& op, 
   logical = make_uint2(lo_lg, hi_lg);
 }
 
+// ---- input standardisation between the linears of a chain
+// x -> fp16((x - mean) / std) per row over the K columns read (population std from fp32 sums);
+// a row with zero spread maps to zeros.
+__device__ __forceinline__ void norm_params(float sum, float sq, int K, float& mu, float& inv) {
+  mu = sum / (float)K;
+  float var = sq / (float)K - mu * mu;
+  var = var > 0.0f ? var : 0.0f;
+  const float sd = sqrtf(var);
+  inv = sd > 0.0f ? 1.0f / sd : 0.0f;
+}
+__device__ __forceinline__ uint16_t norm_h(float x, float mu, float inv) {
+  return inv == 0.0f ? (uint16_t)0 : f2h((x - mu) * inv);
+}
+// Standardise 8 fp16 values.
+__device__ __forceinline__ uint4 norm_block8(uint4 v, float mu, float inv) {
+  uint16_t* h = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = norm_h(h2f(h[e]), mu, inv);
+  return v;
+}
+// Per-thread statistics of 8 fp16 values: sum, sum of squares, max, min.
+__device__ __forceinline__ void stats_block8(const uint4 v, float& sum, float& sq, float& mx, float& mn) {
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = h2f(h[e]);
+    sum += f;
+    sq += f * f;
+    mx = fmaxf(mx, f);
+    mn = fminf(mn, f);
+  }
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Stand-alone row standardisation (W4A16 chains at large M): one workgroup per row.
+__global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restrict__ x, int K, int ldx,
+                                                       uint16_t* __restrict__ out) {
+  __shared__ float r0[4], r1[4];
+  __shared__ float mu_sh, inv_sh;
+  const int m = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * ldx);
+  const int nb = K / 8;
+  float sum = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
+  for (int i = threadIdx.x; i < nb; i += 256) stats_block8(xr[i], sum, sq, mx, mn);
+  sum = wave_sum(sum);
+  sq = wave_sum(sq);
+  if ((threadIdx.x & 63) == 0) { r0[threadIdx.x >> 6] = sum; r1[threadIdx.x >> 6] = sq; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mu, inv;
+    norm_params(r0[0] + r0[1] + r0[2] + r0[3], r1[0] + r1[1] + r1[2] + r1[3], K, mu, inv);
+    mu_sh = mu;
+    inv_sh = inv;
+  }
+  __syncthreads();
+  uint4* o = reinterpret_cast<uint4*>(out + (size_t)m * K);
+  for (int i = threadIdx.x; i < nb; i += 256) o[i] = norm_block8(xr[i], mu_sh, inv_sh);
+}
+
 // Stand-alone quantizer for large M: one workgroup per row.  Writes operand-ordered codes and the
 // fp32 value of the fp16 scale to the workspace, and optionally the logical codes / fp16 scales.
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int K,
-                                                        int8_t* __restrict__ xq_op,
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int K, int ldx,
+                                                        int norm_in, int8_t* __restrict__ xq_op,
                                                         float* __restrict__ sx_f,
                                                         int8_t* __restrict__ xq_out,
                                                         uint16_t* __restrict__ sx_out) {
-  __shared__ float red[4];
-  __shared__ float s_sh;
+  __shared__ float red[4][4];
+  __shared__ float s_sh, mu_sh, inv_sh;
   const int m = blockIdx.x;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * ldx);
   const int nb = K / 8;
-  float mx = 0.0f;
-  for (int i = threadIdx.x; i < nb; i += 256) {
-    const uint4 v = xr[i];
-    const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(h2f(h[e])));
-  }
+  float sum = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
+  for (int i = threadIdx.x; i < nb; i += 256) stats_block8(xr[i], sum, sq, mx, mn);
+  sum = wave_sum(sum);
+  sq = wave_sum(sq);
   mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  mn = wave_min(mn);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = sum; red[1][w] = sq; red[2][w] = mx; red[3][w] = mn; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float xmax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    const float xmin = fminf(fminf(red[3][0], red[3][1]), fminf(red[3][2], red[3][3]));
+    float mu = 0.f, inv = 0.f, amax;
+    if (norm_in) {
+      norm_params(red[0][0] + red[0][1] + red[0][2] + red[0][3], red[1][0] + red[1][1] + red[1][2] + red[1][3],
+                  K, mu, inv);
+      amax = fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)));
+    } else {
+      amax = fmaxf(xmax, -xmin);
+    }
     const uint16_t s16 = f2h(amax / 7.0f);
     s_sh = h2f(s16);
+    mu_sh = mu;
+    inv_sh = inv;
     sx_f[m] = s_sh;
     if (sx_out) sx_out[m] = s16;
   }
@@ -129,7 +202,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   const float s = s_sh;
   for (int i = threadIdx.x; i < nb; i += 256) {
     uint2 op, lg;
-    quant_block8(xr[i], s, op, lg);
+    uint4 v = xr[i];
+    if (norm_in) v = norm_block8(v, mu_sh, inv_sh);
+    quant_block8(v, s, op, lg);
     *reinterpret_cast<uint2*>(xq_op + (size_t)m * K + 8 * i) = op;
     if (xq_out) *reinterpret_cast<uint2*>(xq_out + (size_t)m * K + 8 * i) = lg;
   }
@@ -138,9 +213,18 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 // ------------------------------------------------------------------ streaming linear
 
 enum { MODE_W4A16 = 0, MODE_W4A4 = 1 };
-constexpr int kNW = 8;        // waves per workgroup
+#ifndef QS_STREAM_WAVES
+#define QS_STREAM_WAVES 8
+#endif
+#ifndef QS_STREAM_RING
+#define QS_STREAM_RING 8
+#endif
+#ifndef QS_STREAM_WG_PER_CU
+#define QS_STREAM_WG_PER_CU 2
+#endif
+constexpr int kNW = QS_STREAM_WAVES;   // waves per workgroup
 constexpr int kThreads = kNW * 64;
-constexpr int kPF = 8;        // tiles in flight per wave
+constexpr int kPF = QS_STREAM_RING;    // tiles in flight per wave
 
 struct LinearArgs {
   const uint16_t* x;   // fp16 [M][K]
@@ -152,11 +236,22 @@ struct LinearArgs {
   int32_t* acc_out;    // optional [M][N][G]
   int8_t* xq_out;      // optional logical codes (fused quantizer, written by block 0)
   uint16_t* sx_out;    // optional fp16 scales (fused quantizer, written by block 0)
+  uint16_t* y16;       // if set: write fp16(out_scale * y) here (row stride ldy) instead of y
+  float out_scale;
   int M, N, K;
+  int ldx;             // row stride of x (elements), >= K
+  int ldy;             // row stride of y16 (elements)
+  int norm_in;         // standardise each input row over its K columns first (chain stages > 0)
 };
 
 // MODE: MODE_W4A16 / MODE_W4A4.  MT: 16-row activation tiles per wave (M <= 16 MT).
 // S: waves splitting K.  XLDS: activations staged in LDS (W4A4: quantized in the prologue).
+//
+// Work of one wave: for each row-block set handled by its workgroup, `per` consecutive 1 KiB tiles
+// of its row block (its share of K).  The wave walks this stream with a ring of kPF outstanding
+// tile loads that runs across set boundaries; the stream is padded to whole rings with dummy items
+// that re-read an already cached tile and are not computed, so every load is unconditional and the
+// compiler can wait for exactly the oldest outstanding tile.  All control flow is wave-uniform.
 template <int MODE, int MT, int S, bool XLDS>
 __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   constexpr int R = kNW / S;
@@ -164,196 +259,267 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   __shared__ float4_t red[S > 1 ? kNW : 1][64];
   __shared__ float sx_lds[16];
   __shared__ float amax_red[8][kNW];
+  __shared__ __align__(16) uint32_t zero_pad[16];  // A-operand source for lanes beyond M
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = wave / S, sidx = wave % S;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int r = wave / S, sidx = wave - (wave / S) * S;
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / kGroup;
   const int nrb = (N + 15) / 16;
   const int nsets = (nrb + R - 1) / R;
-  const int per = (G + S - 1) / S;            // uniform item count per set for every wave
+  const int per = (G + S - 1) / S;           // uniform item count per set for every wave
   const int g0 = sidx * per;
-  const int my_sets = blockIdx.x < (unsigned)nsets ? (nsets - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  const int total = my_sets * per;
+  const int gcnt = G - g0 < per ? G - g0 : per;  // valid groups of this wave (may be <= 0)
+  const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int my_sets = bid < nsets ? (nsets - 1 - bid) / grid + 1 : 0;
+  const int total = (my_sets * per + kPF - 1) / kPF * kPF;  // padded to whole rings
+  const size_t set_stride = (size_t)grid * R * G;              // tiles between consecutive sets
 
-  // ---- item -> (row block, group) and the prefetch ring
+  if (threadIdx.x < 16) zero_pad[threadIdx.x] = 0u;
+
+  // ---- load cursor (scalar): set index, item within set, tile index
+  int l_gi = 0, l_si = 0;
+  size_t l_tile = (size_t)(bid * R + r) * G + g0;
+  const uint4* __restrict__ wbase = a.w + lane;
+  const uint16_t* __restrict__ sbase = a.sc + (lane & 15);
   uint4 buf[kPF];
   uint16_t sbuf[kPF];
-  auto item_tile = [&](int it, int& rb, int& g) -> bool {
-    const int si = it / per, gi = it - si * per;
-    const int set = (int)blockIdx.x + si * (int)gridDim.x;
-    rb = set * R + r;
-    g = g0 + gi;
-    return rb < nrb && g < G;
-  };
-  auto issue = [&](int it, int slot) {
-    int rb, g;
-    if (it < total && item_tile(it, rb, g)) {
-      const size_t tile = (size_t)rb * G + g;
-      buf[slot] = a.w[tile * 64 + lane];
-      sbuf[slot] = a.sc[tile * 16 + (lane & 15)];
-    }
+  auto issue = [&](int slot) {
+    const int rb = (bid + l_si * grid) * R + r;
+    const bool ok = l_si < my_sets && rb < nrb && l_gi < gcnt;
+    const size_t t = ok ? l_tile : 0;   // dummy items re-read tile 0
+    buf[slot] = wbase[t * 64];
+    sbuf[slot] = sbase[t * 16];
+    ++l_tile;
+    if (++l_gi == per) { l_gi = 0; ++l_si; l_tile += set_stride - per; }
   };
 #pragma unroll
-  for (int i = 0; i < kPF; ++i) issue(i, i);
+  for (int i = 0; i < kPF; ++i) issue(i);
 
   // ---- prologue: stage activations
   if constexpr (XLDS) {
     if constexpr (MODE == MODE_W4A16) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.x);
       uint4* dst = reinterpret_cast<uint4*>(dyn_lds);
-      const int n16 = M * K / 8;
-      for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+      const int per_row = K / 8;
+      const int n16 = M * per_row;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f}, rq[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = threadIdx.x; i < n16; i += kThreads) {
+        const int m = i / per_row, j = i - m * per_row;
+        const uint4 v = *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.ldx + 8 * j);
+        dst[i] = v;
+        if (a.norm_in) {
+          float su = 0.f, sq = 0.f, mx = 0.f, mn = 0.f;
+          stats_block8(v, su, sq, mx, mn);
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2)
+            if (m == r2) { rs[r2] += su; rq[r2] += sq; }
+        }
+      }
+      if (a.norm_in) {
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const float su = wave_sum(rs[r2]), sq = wave_sum(rq[r2]);
+          if (lane == 0) { amax_red[r2][wave] = su; amax_red[4 + r2][wave] = sq; }
+        }
+        __syncthreads();
+        if (threadIdx.x < M) {
+          float su = 0.f, sq = 0.f;
+#pragma unroll
+          for (int w = 0; w < kNW; ++w) { su += amax_red[threadIdx.x][w]; sq += amax_red[4 + threadIdx.x][w]; }
+          float mu, inv;
+          norm_params(su, sq, K, mu, inv);
+          sx_lds[threadIdx.x] = mu;
+          sx_lds[8 + threadIdx.x] = inv;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < n16; i += kThreads) {
+          const int m = i / per_row;
+          dst[i] = norm_block8(dst[i], sx_lds[m], sx_lds[8 + m]);
+        }
+      }
     } else {
       const int nb = K / 8;
+      __shared__ float stat_red[4][8][kNW];
       for (int m = 0; m < M; ++m) {
-        const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * K);
-        float mx = 0.0f;
-        for (int i = threadIdx.x; i < nb; i += kThreads) {
-          const uint4 v = xr[i];
-          const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(h2f(h[e])));
-        }
+        const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.ldx);
+        float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
+        for (int i = threadIdx.x; i < nb; i += kThreads) stats_block8(xr[i], su, sq, mx, mn);
+        su = wave_sum(su);
+        sq = wave_sum(sq);
         mx = wave_max(mx);
-        if (lane == 0) amax_red[m][wave] = mx;
+        mn = wave_min(mn);
+        if (lane == 0) {
+          stat_red[0][m][wave] = su;
+          stat_red[1][m][wave] = sq;
+          stat_red[2][m][wave] = mx;
+          stat_red[3][m][wave] = mn;
+        }
       }
       __syncthreads();
       if (threadIdx.x < M) {
-        float amax = 0.0f;
+        const int m = threadIdx.x;
+        float su = 0.f, sq = 0.f, xmax = -INFINITY, xmin = INFINITY;
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) amax = fmaxf(amax, amax_red[threadIdx.x][w]);
+        for (int w = 0; w < kNW; ++w) {
+          su += stat_red[0][m][w];
+          sq += stat_red[1][m][w];
+          xmax = fmaxf(xmax, stat_red[2][m][w]);
+          xmin = fminf(xmin, stat_red[3][m][w]);
+        }
+        float mu = 0.f, inv = 0.f, amax;
+        if (a.norm_in) {
+          norm_params(su, sq, K, mu, inv);
+          amax = fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)));
+        } else {
+          amax = fmaxf(xmax, -xmin);
+        }
         const uint16_t s16 = f2h(amax / 7.0f);
-        sx_lds[threadIdx.x] = h2f(s16);
-        if (blockIdx.x == 0 && a.sx_out) a.sx_out[threadIdx.x] = s16;
+        sx_lds[m] = h2f(s16);
+        amax_red[0][m] = mu;
+        amax_red[1][m] = inv;
+        if (blockIdx.x == 0 && a.sx_out) a.sx_out[m] = s16;
       }
       __syncthreads();
       int8_t* xq_lds = reinterpret_cast<int8_t*>(dyn_lds);
       for (int m = 0; m < M; ++m) {
-        const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * K);
+        const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.ldx);
         const float s = sx_lds[m];
+        const float mu = amax_red[0][m], inv = amax_red[1][m];
         for (int i = threadIdx.x; i < nb; i += kThreads) {
           uint2 op, lg;
-          quant_block8(xr[i], s, op, lg);
+          uint4 v = xr[i];
+          if (a.norm_in) v = norm_block8(v, mu, inv);
+          quant_block8(v, s, op, lg);
           *reinterpret_cast<uint2*>(xq_lds + (size_t)m * K + 8 * i) = op;
           if (blockIdx.x == 0 && a.xq_out)
             *reinterpret_cast<uint2*>(a.xq_out + (size_t)m * K + 8 * i) = lg;
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   float4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int arow = lane & 15;      // A-operand row (activation row within a 16-row tile)
+  const int arow = lane & 15;       // A-operand row (activation row within a 16-row tile)
   const int kq = 32 * (lane >> 4);  // lane's k offset inside a group
+  // LDS byte address of this lane's A operand at group 0 (or the zero pad for rows beyond M).
+  const uint32_t zero_addr = (uint32_t)(uintptr_t)zero_pad;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)dyn_lds;
+  constexpr int kElt = MODE == MODE_W4A16 ? 2 : 1;  // bytes per staged activation element
+  const uint32_t a_lane = arow < M ? lds_base + (uint32_t)((arow * K + kq) * kElt) : zero_addr;
+  const uint32_t a_step = arow < M ? (uint32_t)(kGroup * kElt) : 0u;  // per group
 
+  const uint32_t magic = fp16_magic_vgpr();
+  int c_gi = 0, c_si = 0;
   for (int base = 0; base < total; base += kPF) {
 #pragma unroll
     for (int i = 0; i < kPF; ++i) {
-      const int it = base + i;
-      if (it < total) {
-        int rb, g;
-        const bool valid = item_tile(it, rb, g);
-        const uint4 wv = buf[i];
-        const float s = h2f(sbuf[i]);
-        issue(it + kPF, i);
-        if (valid) {
-          const int kb = g * kGroup + kq;
-          if constexpr (MODE == MODE_W4A16) {
-            float4_t dg[MT];
+      const uint4 wv = buf[i];
+      const float s = h2f(sbuf[i]);
+      issue(i);
+      const int rb = (bid + c_si * grid) * R + r;
+      const bool valid = c_si < my_sets && rb < nrb && c_gi < gcnt;
+      if (valid) {
+        const int g = g0 + c_gi;
+        const int kb = g * kGroup + kq;
+        if constexpr (MODE == MODE_W4A16) {
+          float4_t dg[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) dg[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < MT; ++mt) dg[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t wt = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
-              const half8_t b = unpack_f16x8(wt);
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
-                const int m = mt * 16 + arow;
-                half8_t av = {};
-                if (m < M) {
-                  if constexpr (XLDS)
-                    av = *reinterpret_cast<const half8_t*>(
-                        reinterpret_cast<const _Float16*>(dyn_lds) + (size_t)m * K + kb + 8 * t);
-                  else
-                    av = *reinterpret_cast<const half8_t*>(
-                        reinterpret_cast<const _Float16*>(a.x) + (size_t)m * K + kb + 8 * t);
-                }
-                dg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, dg[mt], 0, 0, 0);
-              }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] += s * dg[mt];
-          } else {
-            int4_t dg[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) dg[mt] = int4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const int4_t b = t2 == 0 ? unpack_i8x16(wv.x, wv.y) : unpack_i8x16(wv.z, wv.w);
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
-                const int m = mt * 16 + arow;
-                int4_t av = {0, 0, 0, 0};
-                if (m < M) {
-                  const int8_t* src = XLDS ? reinterpret_cast<const int8_t*>(dyn_lds) : a.xq;
-                  av = *reinterpret_cast<const int4_t*>(src + (size_t)m * K + kb + 16 * t2);
-                }
-                dg[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, dg[mt], 0, 0, 0);
-              }
-            }
-            const int n = rb * 16 + (lane & 15);
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t wt = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
+            const half8_t b = unpack_f16x8(wt, magic);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int gsum = dg[mt][j] >> 4;  // operands carry 16 * q: exact
-                acc[mt][j] += s * (float)gsum;
-                if (a.acc_out) {
-                  const int m = mt * 16 + 4 * (lane >> 4) + j;
-                  if (m < M && n < N) a.acc_out[((size_t)m * N + n) * G + g] = gsum;
-                }
+              half8_t av;
+              if constexpr (XLDS) {
+                const uint32_t addr = a_lane + (uint32_t)g * a_step + 16u * t;
+                av = *reinterpret_cast<const __attribute__((address_space(3))) half8_t*>(
+                    (size_t)addr);
+              } else {
+                const int m = mt * 16 + arow;
+                av = half8_t{};
+                if (m < M)
+                  av = *reinterpret_cast<const half8_t*>(
+                      reinterpret_cast<const _Float16*>(a.x) + (size_t)m * a.ldx + kb + 8 * t);
               }
+              dg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, dg[mt], 0, 0, 0);
             }
           }
-        }
-        // ---- end of this wave's share of a row-block set: reduce over S and store
-        if (it - (it / per) * per == per - 1) {
-          int rb2, g2;
-          item_tile(it - (per - 1), rb2, g2);  // row block of this set (independent of g)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] += s * dg[mt];
+        } else {
+          int4_t dg[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) dg[mt] = int4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const int4_t b = t2 == 0 ? unpack_i8x16(wv.x, wv.y) : unpack_i8x16(wv.z, wv.w);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              int4_t av;
+              if constexpr (XLDS) {
+                const uint32_t addr = a_lane + (uint32_t)g * a_step + 16u * t2;
+                av = *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
+              } else {
+                const int m = mt * 16 + arow;
+                av = int4_t{0, 0, 0, 0};
+                if (m < M) av = *reinterpret_cast<const int4_t*>(a.xq + (size_t)m * K + kb + 16 * t2);
+              }
+              dg[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, dg[mt], 0, 0, 0);
+            }
+          }
+          const int n = rb * 16 + (lane & 15);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            float4_t v = acc[mt];
-            if constexpr (S > 1) {
-              red[wave][lane] = v;
-              __syncthreads();
-              if (sidx == 0) {
 #pragma unroll
-                for (int s2 = 1; s2 < S; ++s2) v += red[wave + s2][lane];
-              }
-              __syncthreads();
-            }
-            if (sidx == 0 && rb2 < nrb) {
-              const int n = rb2 * 16 + (lane & 15);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j) {
+              const int gsum = dg[mt][j] >> 4;  // operands carry 16 * q: exact
+              acc[mt][j] += s * (float)gsum;
+              if (a.acc_out) {
                 const int m = mt * 16 + 4 * (lane >> 4) + j;
-                if (m < M && n < N) {
-                  float out = v[j];
-                  if constexpr (MODE == MODE_W4A4) out *= XLDS ? sx_lds[m] : a.sxf[m];
-                  a.y[(size_t)m * N + n] = out;
-                }
+                if (m < M && n < N) a.acc_out[((size_t)m * N + n) * G + g] = gsum;
               }
             }
           }
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
+      }
+      // ---- end of this wave's share of a row-block set: reduce over S and store
+      if (++c_gi == per) {
+        c_gi = 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          float4_t v = acc[mt];
+          if constexpr (S > 1) {
+            red[wave][lane] = v;
+            __syncthreads();
+            if (sidx == 0) {
+#pragma unroll
+              for (int s2 = 1; s2 < S; ++s2) v += red[wave + s2][lane];
+            }
+            __syncthreads();
+          }
+          if (sidx == 0 && c_si < my_sets && rb < nrb) {
+            const int n = rb * 16 + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int m = mt * 16 + 4 * (lane >> 4) + j;
+              if (m < M && n < N) {
+                float out = v[j];
+                if constexpr (MODE == MODE_W4A4) out *= XLDS ? sx_lds[m] : a.sxf[m];
+                if (a.y16) a.y16[(size_t)m * a.ldy + n] = f2h(out * a.out_scale);
+                else a.y[(size_t)m * N + n] = out;
+              }
+            }
+          }
+          acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        ++c_si;
       }
     }
   }
@@ -367,9 +533,10 @@ constexpr size_t kMaxLdsStage = 131072;  // bytes of activations staged in LDS
 static bool w4a4_fused(int M, int K) { return M <= kFusedMaxM && (size_t)M * K <= kMaxLdsStage; }
 static bool w4a16_lds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= kMaxLdsStage; }
 
-size_t linear_workspace(int mode, int M, int N, int K) {
+size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
   (void)N;
-  if (mode != QS_W4A4 || w4a4_fused(M, K)) return 0;
+  if (mode == QS_W4A16) return (norm_in && !w4a16_lds(M, K)) ? align_up((size_t)M * K * 2, 256) : 0;
+  if (w4a4_fused(M, K)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
 }
 
@@ -380,12 +547,17 @@ static int launch_one(const LinearArgs& a, size_t lds, hipStream_t st) {
   const int nrb = (a.N + 15) / 16;
   const int R = kNW / S;
   const int nsets = (nrb + R - 1) / R;
-  const int per_cu = lds > 65536 ? 1 : 2;
+  const int per_cu = lds > 65536 ? 1 : QS_STREAM_WG_PER_CU;
   const int grid = nsets < di->num_cus * per_cu ? nsets : di->num_cus * per_cu;
   if (lds > 65536) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return QS_ERR_HIP;
+    // Raise the dynamic-LDS limit once per instance (before any graph capture uses it).
+    static int lds_limit = 0;
+    if ((int)lds > lds_limit) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsStage) != hipSuccess)
+        return QS_ERR_HIP;
+      lds_limit = (int)kMaxLdsStage;
+    }
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, st, a);
   return launch_status();
@@ -396,7 +568,7 @@ static int pick_split(int N, int K) {
   const int nrb = (N + 15) / 16;
   const int G = K / kGroup;
   int s = 1;
-  while (s < 8 && nrb * s < 4096 && G / (2 * s) >= 2) s *= 2;
+  while (s < 8 && s < kNW && nrb * s < 4096 && G / (2 * s) >= 2) s *= 2;
   return s;
 }
 
@@ -405,8 +577,12 @@ static int launch_split(const LinearArgs& a, size_t lds, hipStream_t st) {
   switch (pick_split(a.N, a.K)) {
     case 1: return launch_one<MODE, MT, 1, XLDS>(a, lds, st);
     case 2: return launch_one<MODE, MT, 2, XLDS>(a, lds, st);
-    case 4: return launch_one<MODE, MT, 4, XLDS>(a, lds, st);
-    default: return launch_one<MODE, MT, 8, XLDS>(a, lds, st);
+    case 4:
+      if constexpr (kNW >= 4) return launch_one<MODE, MT, 4, XLDS>(a, lds, st);
+      return QS_ERR_UNSUPPORTED;
+    default:
+      if constexpr (kNW >= 8) return launch_one<MODE, MT, 8, XLDS>(a, lds, st);
+      return QS_ERR_UNSUPPORTED;
   }
 }
 
@@ -427,10 +603,11 @@ template <int MODE>
 static int launch_rows(LinearArgs a, int m0, int rows, hipStream_t st) {
   const int G = a.K / kGroup;
   a.M = rows;
-  a.x = a.x ? a.x + (size_t)m0 * a.K : nullptr;
+  a.x = a.x ? a.x + (size_t)m0 * a.ldx : nullptr;
   a.xq = a.xq ? a.xq + (size_t)m0 * a.K : nullptr;
   a.sxf = a.sxf ? a.sxf + m0 : nullptr;
-  a.y += (size_t)m0 * a.N;
+  if (a.y) a.y += (size_t)m0 * a.N;
+  if (a.y16) a.y16 += (size_t)m0 * a.ldy;
   a.acc_out = a.acc_out ? a.acc_out + (size_t)m0 * a.N * G : nullptr;
   return launch_mt<MODE>(a, st);
 }
@@ -448,27 +625,53 @@ static int launch_chunked(const LinearArgs& a, hipStream_t st) {
 int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* y,
                   int M, int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out,
                   void* ws, size_t ws_bytes, hipStream_t st) {
+  LinearIO io{};
+  io.x = x;
+  io.ldx = K;
+  io.y = y;
+  return launch_linear_io(mode, io, wp, sp, M, N, K, xq_out, sx_out, acc_out, ws, ws_bytes, st);
+}
+
+int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint16_t* sp, int M, int N,
+                     int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
+                     size_t ws_bytes, hipStream_t st) {
+  const uint16_t* x = io.x;
   LinearArgs a{};
   a.x = x;
   a.w = reinterpret_cast<const uint4*>(wp);
   a.sc = sp;
-  a.y = y;
+  a.y = io.y;
+  a.y16 = io.y16;
+  a.out_scale = io.out_scale;
+  a.ldx = io.ldx;
+  a.ldy = io.ldy;
   a.acc_out = acc_out;
   a.xq_out = xq_out;
   a.sx_out = sx_out;
   a.M = M;
   a.N = N;
   a.K = K;
+  a.norm_in = io.norm_in;
+  const size_t need = linear_workspace(mode, M, N, K, io.norm_in != 0);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return QS_ERR_WORKSPACE;
   if (mode == QS_W4A16) {
     if (w4a16_lds(M, K)) return launch_split<MODE_W4A16, 1, true>(a, (size_t)M * K * 2, st);
+    if (io.norm_in) {
+      uint16_t* xn = static_cast<uint16_t*>(ws);
+      hipLaunchKernelGGL(row_norm_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, xn);
+      const int rc = launch_status();
+      if (rc != QS_OK) return rc;
+      a.x = xn;
+      a.ldx = K;
+      a.norm_in = 0;
+    }
     return launch_chunked<MODE_W4A16>(a, st);
   }
   if (w4a4_fused(M, K)) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
-  const size_t need = linear_workspace(mode, M, N, K);
-  if (ws == nullptr || ws_bytes < need) return QS_ERR_WORKSPACE;
   int8_t* xq_op = static_cast<int8_t*>(ws);
   float* sxf = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + align_up((size_t)M * K, 256));
-  hipLaunchKernelGGL(act_quant_kernel, dim3(M), dim3(256), 0, st, x, K, xq_op, sxf, xq_out, sx_out);
+  hipLaunchKernelGGL(act_quant_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
+                     xq_out, sx_out);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
   a.xq = xq_op;

@@ -39,13 +39,13 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 // k order.  (0x6400 | v) is the fp16 value 1024 + v for v < 1024, so
 //   low nibble  : (1024 + u)        - 1032       = q
 //   high nibble : (1024 + 16 u) / 16 - 72        = q
-// Both are exact in fp16.
-__device__ __forceinline__ half8_t unpack_f16x8(uint32_t w) {
+// Both are exact in fp16.  `magic` must be 0x64006400 (see fp16_magic_vgpr).
+__device__ __forceinline__ half8_t unpack_f16x8(uint32_t w, uint32_t magic) {
   const uint32_t w8 = w >> 8;
-  const uint32_t a = (w & 0x000F000Fu) | 0x64006400u;   // k0, k1
-  const uint32_t b = (w & 0x00F000F0u) | 0x64006400u;   // k2, k3
-  const uint32_t c = (w8 & 0x000F000Fu) | 0x64006400u;  // k4, k5
-  const uint32_t d = (w8 & 0x00F000F0u) | 0x64006400u;  // k6, k7
+  const uint32_t a = (w & 0x000F000Fu) | magic;   // k0, k1
+  const uint32_t b = (w & 0x00F000F0u) | magic;   // k2, k3
+  const uint32_t c = (w8 & 0x000F000Fu) | magic;  // k4, k5
+  const uint32_t d = (w8 & 0x00F000F0u) | magic;  // k6, k7
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2_t sc = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t off2 = {(_Float16)72.0f, (_Float16)72.0f};
@@ -53,10 +53,20 @@ __device__ __forceinline__ half8_t unpack_f16x8(uint32_t w) {
   const half2_t hb = __builtin_bit_cast(half2_t, b) * sc - off2;
   const half2_t hc = __builtin_bit_cast(half2_t, c) - off;
   const half2_t hd = __builtin_bit_cast(half2_t, d) * sc - off2;
-  half8_t r;
-  r[0] = ha[0]; r[1] = ha[1]; r[2] = hb[0]; r[3] = hb[1];
-  r[4] = hc[0]; r[5] = hc[1]; r[6] = hd[0]; r[7] = hd[1];
-  return r;
+  uint4 u;
+  u.x = __builtin_bit_cast(uint32_t, ha);
+  u.y = __builtin_bit_cast(uint32_t, hb);
+  u.z = __builtin_bit_cast(uint32_t, hc);
+  u.w = __builtin_bit_cast(uint32_t, hd);
+  return __builtin_bit_cast(half8_t, u);
+}
+
+// 0x64006400 held in a VGPR: lets (w & mask) | magic fuse into one v_and_or_b32 (VOP3 on this
+// target cannot encode two literal operands).
+__device__ __forceinline__ uint32_t fp16_magic_vgpr() {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(v));
+  return v;
 }
 
 // Two packed dwords (k offsets 0-15 of a lane's slice) -> 16 int8 operands

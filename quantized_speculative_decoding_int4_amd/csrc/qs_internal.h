@@ -22,10 +22,26 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Launch helpers implemented in linear.hip / verify.hip.
 int launch_pack(const int8_t* q, const uint16_t* s, int N, int K, uint8_t* wp,
                 uint16_t* sp, hipStream_t st);
-size_t linear_workspace(int mode, int M, int N, int K);
+size_t linear_workspace(int mode, int M, int N, int K, bool norm_in);
 int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp,
                   float* y, int M, int N, int K, int8_t* xq_out, uint16_t* sx_out,
                   int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t st);
+
+// Input/output placement of one linear inside a chain: x with row stride ldx, optionally
+// standardised per row; output either fp32 y [M][N] or fp16(out_scale * y) into y16 with
+// row stride ldy.
+struct LinearIO {
+  const uint16_t* x;
+  int ldx;
+  float* y;
+  uint16_t* y16;
+  float out_scale;
+  int ldy;
+  int norm_in;  // standardise each input row over its K columns first
+};
+int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint16_t* sp, int M, int N,
+                     int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
+                     size_t ws_bytes, hipStream_t st);
 
 size_t verify_workspace(int B, int gamma, int V);
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,

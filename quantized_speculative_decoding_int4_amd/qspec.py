@@ -43,6 +43,8 @@ _SIGS = {
     "qs_linear_w4a4": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
     "qs_lmhead": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p], _i),
     "qs_verify_workspace_bytes": ([_i, _i, _i], _sz),
+    "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
+    "qs_chain_forward": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_sample": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
 }
@@ -234,4 +236,46 @@ def qs_verify_sample(tgt_logits, drf_logits, draft_ids, u_accept, u_final, out=N
         _ptr(out["out_tokens"], torch.int32, (b, gp1), "out_tokens"),
         _ptr(out["final_dist"], torch.float32, (b, v), "final_dist", nullable=True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
+    return out
+
+
+class LinearDesc(ctypes.Structure):
+    """Mirror of qs_linear_desc."""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("s_packed", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int), ("out_scale", ctypes.c_float)]
+
+
+class Chain:
+    """A host array of qs_linear_desc plus references that keep the packed
+    weight tensors alive.  `layers` is a sequence of (w_packed, s_packed, N, K,
+    out_scale)."""
+
+    def __init__(self, layers):
+        self.tensors = []
+        self.n = len(layers)
+        self.array = (LinearDesc * self.n)()
+        for i, (wp, sp, n, k, scale) in enumerate(layers):
+            _wcheck(wp, sp, n, k)
+            self.tensors.append((wp, sp))
+            self.array[i] = LinearDesc(wp.data_ptr(), sp.data_ptr(), n, k, float(scale))
+        self.out_features = layers[-1][2]
+        self.in_features = layers[0][3]
+
+    def workspace_bytes(self, mode: int, m: int) -> int:
+        return _lib.qs_chain_workspace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
+
+
+def qs_chain_forward(mode: int, x, chain: Chain, out=None, ws=None):
+    """x fp16 [M, chain.in_features] -> out fp32 [M, chain.out_features]."""
+    m, k = x.shape
+    if k != chain.in_features:
+        raise ValueError("x width does not match the first linear")
+    if out is None:
+        out = torch.empty((m, chain.out_features), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=x.device)
+    _check("qs_chain_forward", _lib.qs_chain_forward(
+        mode, _ptr(x, torch.float16, (m, k), "x"), m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n,
+        _ptr(out, torch.float32, (m, chain.out_features), "out"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream()))
     return out

@@ -105,3 +105,28 @@ def agreeing_ids(rng: np.random.Generator, reference_ids: np.ndarray, vocab: int
     other = rng.integers(0, vocab - 1, size=ref.shape)
     other = other + (other >= ref)          # skip the reference id
     return np.where(keep, ref, other).astype(np.int32)
+
+
+def int4_weights_device(gen, n: int, k: int, device="cuda", s_lo: float = 0.005, s_hi: float = 0.02):
+    """Same distribution as int4_weights, drawn on the GPU with a seeded
+    torch.Generator (for the multi-GB stacks where host generation is slow)."""
+    import torch
+    assert k % GROUP == 0
+    q = torch.randint(-8, 8, (n, k), dtype=torch.int8, device=device, generator=gen)
+    s = (torch.rand((n, k // GROUP), device=device, generator=gen) * (s_hi - s_lo) + s_lo).to(torch.float16)
+    return q, s
+
+
+# The verify/draft pass of the Llama-3-8B-shaped stack as a chain of linears:
+# per layer the fused q|k|v (N = 4096 + 1024 + 1024), o, fused gate|up
+# (N = 2 * 14336) and down, then the LM-head.  Fusing q|k|v and gate|up into one
+# matrix each streams exactly the same weight bytes as the separate linears.
+def stack_shapes(n_layers: int = N_LAYERS):
+    per_layer = [("qkv", 4096 + 1024 + 1024, HIDDEN), ("o", HIDDEN, HIDDEN),
+                 ("gateup", 2 * 14336, HIDDEN), ("down", HIDDEN, 14336)]
+    shapes = []
+    for layer in range(n_layers):
+        for name, n, k in per_layer:
+            shapes.append((f"L{layer}.{name}", n, k))
+    shapes.append(("lm_head", VOCAB, HIDDEN))
+    return shapes

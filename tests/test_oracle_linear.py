@@ -177,3 +177,49 @@ def test_lm_head_chunking_matches_full():
     x, _ = W.activations(rng, 3, 256)
     for mode, full in (("w4a16", O.linear_w4a16(x, q, s)), ("w4a4", O.linear_w4a4(x, q, s)["y"])):
         assert np.array_equal(O.lm_head(mode, x, q, s, chunk=64), full)
+
+
+def _balanced_chain_case(rng):
+    """Stage 1 maps a one-hot input row to outputs of exactly +-2^-6 with equal
+    counts, so standardisation gives exactly +-1 and stage 2 is exact integer
+    arithmetic."""
+    k1, n1 = 128, 256
+    q1 = np.zeros((n1, k1), np.int8)
+    half = np.array([1, -1] * 64, np.int8)        # balanced within the 128 columns read
+    signs = np.concatenate([rng.permutation(half), rng.permutation(half)])
+    q1[:, 0] = signs
+    q1[:, 1:] = rng.integers(-8, 8, size=(n1, k1 - 1), dtype=np.int8)
+    s1 = np.full((n1, 1), 2.0 ** -6, np.float16)
+    x = np.zeros((2, k1), np.float16)
+    x[:, 0] = 1.0
+    q2, s2 = W.integer_case_weights(rng, 8, 128, exponents=(-5,))
+    return x, [(q1, s1), (q2, s2)], signs
+
+
+def test_chain_exact_balanced_case():
+    rng = W.rng_for(19)
+    x, layers, signs = _balanced_chain_case(rng)
+    y = O.chain_forward("w4a16", x, layers)
+    mid = np.tile(signs[:128].astype(np.float16), (2, 1))     # standardised stage-1 output
+    ref = _brute_w4a16(mid, *layers[1])
+    for m in range(2):
+        for n in range(8):
+            assert Fraction(y[m, n]) == ref[m][n]
+
+
+def test_standardize_rows_properties():
+    rng = W.rng_for(21)
+    y = rng.standard_normal((3, 1000)) * 5 + 3
+    z = O.standardize_rows(y).astype(np.float64)
+    assert np.allclose(z.mean(axis=1), 0, atol=2e-3) and np.allclose(z.std(axis=1), 1, atol=2e-3)
+    assert np.all(O.standardize_rows(np.full((1, 8), 2.5)) == 0)          # zero spread -> zeros
+    assert np.array_equal(O.standardize_rows(np.array([[1.0, -1.0, 1.0, -1.0]])),
+                          np.array([[1, -1, 1, -1]], np.float16))
+
+
+def test_chain_single_stage_is_the_linear():
+    rng = W.rng_for(20)
+    q, s = W.int4_weights(rng, 64, 256)
+    x, _ = W.activations(rng, 3, 256)
+    assert np.array_equal(O.chain_forward("w4a16", x, [(q, s)]), O.linear_w4a16(x, q, s))
+    assert np.array_equal(O.chain_forward("w4a4", x, [(q, s)]), O.linear_w4a4(x, q, s)["y"])

@@ -171,3 +171,53 @@ def test_lmhead_full_vocab_sampled_rows(qs, mode, m):
         ref = O.linear_w4a4(x, q[cols], s[cols])["y"]
     assert_linear_close(logits[:, cols], ref, f"lmhead mode={mode}")
     assert np.isfinite(logits).all()
+
+
+# ---------------------------------------------------------------- chained pass (draft / verify pass)
+
+def _gpu_chain(qs, mode, x, layers):
+    packed = []
+    for q, s in layers:
+        wp, sp = _pack(qs, q, s)
+        packed.append((wp, sp, q.shape[0], q.shape[1], 1.0))
+    chain = qs.Chain(packed)
+    return host(qs.qs_chain_forward(mode, dev(x), chain))
+
+
+def _balanced_chain_case(rng):
+    """Stage 1 maps a one-hot input to outputs of exactly +-2^-6, balanced
+    within the 128 columns stage 2 reads, so standardisation yields exactly
+    +-1 and every step is exact: the GPU must match bit for bit."""
+    k1, n1 = 128, 256
+    q1 = np.zeros((n1, k1), np.int8)
+    half = np.array([1, -1] * 64, np.int8)
+    q1[:, 0] = np.concatenate([rng.permutation(half), rng.permutation(half)])
+    q1[:, 1:] = rng.integers(-8, 8, size=(n1, k1 - 1), dtype=np.int8)
+    s1 = np.full((n1, 1), 2.0 ** -6, np.float16)
+    x = np.zeros((2, k1), np.float16)
+    x[:, 0] = 1.0
+    q2, s2 = W.integer_case_weights(rng, 8, 128, exponents=(-5,))
+    return x, [(q1, s1), (q2, s2)]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_chain_exact_balanced_case(qs, mode):
+    x, layers = _balanced_chain_case(W.rng_for(19))
+    y = _gpu_chain(qs, mode, x, layers)
+    assert np.array_equal(y.astype(np.float64), O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers))
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20)])
+def test_chain_small_llama_like(qs, mode, m):
+    """Two layers of q|k|v, o, gate|up, down at hidden 512 plus a 3000-way head;
+    o reads the q columns, down reads the gate columns; M = 12 and 20 take the
+    large-M paths (separate standardisation / quantization kernels)."""
+    print(f"chain mode={mode} m={m}", flush=True)
+    rng = W.rng_for(800 + m)
+    h, inter = 512, 1024
+    shapes = [(h + 256, h), (h, h), (2 * inter, h), (h, inter)] * 2 + [(3000, h)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, h)
+    y = _gpu_chain(qs, mode, x, layers)
+    ref = O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers)
+    assert_linear_close(y, ref, f"chain mode={mode} m={m}")
