@@ -13,8 +13,10 @@ the phases time them.
 
 Printed JSON line: `value` = verify-pass weight GB/s (3,869,589,504 weight
 bytes per pass / verify-pass time), plus draft-pass rates, accept positions/s,
-the roofline of the dominant kernel (the W4A16 gate|up linear of the verify
-pass, timed with HIP events around each launch) and the CPU oracle baseline.
+the roofline of the dominant kernel (the persistent W4A4 pass kernel: the three
+draft passes take most of a step) and of the W4A16 verify pass kernel, each
+timed with HIP events around graph replays of one pass, and the CPU oracle
+baseline.
 """
 
 from __future__ import annotations
@@ -122,7 +124,7 @@ def main():
         q, s = W.int4_weights_device(gen, n, k, device=dev)
         wp, sp = qs.qs_pack_weights(q, s)
         del q, s
-        layers.append((wp, sp, n, k, 1.0))
+        layers.append((wp, sp, n, k))
         pass_bytes += n * k // 2 + n * (k // 128) * 2
     torch.cuda.synchronize()
     chain = qs.Chain(layers)
@@ -260,29 +262,39 @@ def main():
         }
         del tg, dr, wsg
 
-    # ---------------- roofline of the dominant kernel: W4A16 gate|up at M = 4
-    gu = [(wp, sp, n, k) for (wp, sp, n, k, _), (nm, _, _) in zip(layers, shapes) if nm.endswith("gateup")]
-    y_gu = torch.empty((M_VERIFY, gu[0][2]), dtype=torch.float32, device=dev)
+    # ---------------- rooflines of the pass kernels (HIP events on the launch stream)
+    # Algorithmic bytes of one pass: packed weights (0.515625 B per weight) plus, per linear,
+    # x = 2*M*K and y = 4*M*N bytes.  A pass runs as `launches` persistent launches, each
+    # preceded by a one-workgroup control reset; bytes and time are averaged per launch.
     stream = torch.cuda.current_stream()
-    durs = []
-    for rep in range(3):
-        evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in gu]
-        for (wp, sp, n, k), (a, b) in zip(gu, evs):
+
+    def pass_roofline(mode, m, x, out, ws, name, reps=10):
+        launches = chain.pass_launches(mode, m)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qs.qs_chain_forward(mode, x, chain, out=out, ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
             a.record(stream)
-            qs.qs_linear_w4a16(x_verify, wp, sp, n, y=y_gu)
+            g.replay()
             b.record(stream)
         torch.cuda.synchronize()
-        if rep > 0:
-            durs += [a.elapsed_time(b) for a, b in evs]
-    n_gu, k_gu = gu[0][2], gu[0][3]
-    gu_bytes = n_gu * k_gu // 2 + n_gu * (k_gu // 128) * 2
-    gu_ms = float(np.mean(durs))
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "linear_stream_kernel<W4A16, MT=1, S=4, LDS> (gate|up 4096->28672, M=4)",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": gu_ms * 1e3, "launches": len(durs)}
-    log(f"gate|up W4A16 M=4: {gu_ms * 1e3:.2f} us/launch, {achieved:.0f} GB/s")
+        pass_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        alg = pass_bytes + sum(2 * m * k + 4 * m * n for (_, n, k) in shapes)
+        per = max(launches, 1)
+        achieved = alg / (pass_ms * 1e-3) / 1e9
+        log(f"{name}: {pass_ms * 1e3:.1f} us per pass, {launches} launches, {achieved:.0f} GB/s")
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": name,
+                "bytes_per_launch": alg / per, "avg_launch_us": pass_ms * 1e3 / per,
+                "launches_per_pass": launches, "passes_timed": reps}
+
+    roof_draft = pass_roofline(qs.QS_W4A4, 1, x_draft[0], logits_q[0, 0:1], ws_draft,
+                               "pass_kernel<W4A4> (draft pass, M=1, int8 MFMA)")
+    roof_verify = pass_roofline(qs.QS_W4A16, M_VERIFY, x_verify, logits_p[0], ws_verify,
+                                "pass_kernel<W4A16> (verify pass, M=4, fp16 MFMA)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -317,7 +329,8 @@ def main():
         "iteration_accepted_tokens": n_acc + 1,
         "draft_verify_top1_agreement": agree,
         "accept_positions_per_s": accept,
-        "roofline": roofline,
+        "roofline": roof_draft,
+        "roofline_verify": roof_verify,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -136,7 +136,6 @@ typedef struct qs_linear_desc {
   const uint16_t* s_packed;  /* packed group scales                            */
   int N;                     /* output features                                */
   int K;                     /* input features (multiple of 128)               */
-  float out_scale;           /* gain on this output when it feeds the next one */
 } qs_linear_desc;
 
 /* Workspace bytes needed by qs_chain_forward for this chain at M rows. */
@@ -150,17 +149,27 @@ size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, in
  * The pages give no layer internals, so the chain is linears only:
  *   stage 0 reads x fp16 [M][chain[0].K];
  *   stage i > 0 reads the first chain[i].K columns (row stride chain[i-1].N) of
- *     stage i-1's output, kept as fp16(out_scale * y) in the workspace, and
+ *     stage i-1's output, kept as fp16(y) in the workspace, and
  *     standardises each row over those columns, fp16((v - mean) / std) with the
  *     population std (rows with zero spread become zeros), standing in for the
  *     normalisation between real layers (requires chain[i].K <= chain[i-1].N);
- *   the last stage writes fp32 out [M][chain[n-1].N] (its out_scale is unused).
+ *   the last stage writes fp32 out [M][chain[n-1].N].
  * With chain = n_layers x {q|k|v, o, gate|up, down} + LM-head this is the
  * Llama-shaped pass: o reads the q columns, down reads the gate columns.
  *   ws  >= qs_chain_workspace_bytes(mode, M, chain, n) bytes of scratch
  */
 int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n,
                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Number of persistent pass-kernel launches qs_chain_forward makes for this
+ * chain on the current device (each runs a run of consecutive linears with
+ * grid-wide hand-over between them), or 0 if the chain runs one linear per
+ * launch (row counts or shapes the persistent kernel does not take).  Each
+ * persistent launch is preceded by a one-workgroup launch that clears its
+ * control words.  Negative status codes as qs_chain_forward for bad arguments.
+ */
+int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n);
 
 /* Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V). */
 size_t qs_verify_workspace_bytes(int B, int gamma, int V);

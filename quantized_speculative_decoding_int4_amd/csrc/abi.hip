@@ -16,16 +16,20 @@ const DeviceInfo* device_info() {
   static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    static DeviceInfo bad{0, 0};
+    static DeviceInfo bad{0, 0, 0};
     return &bad;
   }
   std::lock_guard<std::mutex> lock(mu);
   if (!filled[dev]) {
     hipDeviceProp_t prop;
-    DeviceInfo d{0, 0};
+    DeviceInfo d{0, 0, 0};
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
       d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
       d.num_cus = prop.multiProcessorCount;
+      int khz = 0;
+      if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        khz = 100000;
+      d.clock_khz = khz;
     }
     cache[dev] = d;
     filled[dev] = true;

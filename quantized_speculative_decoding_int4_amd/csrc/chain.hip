@@ -32,7 +32,9 @@ size_t chain_workspace(int mode, int M, const qs_linear_desc* c, int n) {
     const size_t w = linear_workspace(mode, M, c[i].N, c[i].K, i > 0);
     q = w > q ? w : q;
   }
-  return 2 * act_bytes(M, c, n) + q;
+  // control words of the persistent pass: go + error word, then one 128-byte flag per workgroup
+  const size_t ctrl = kPassCtrlBytes;
+  return 2 * act_bytes(M, c, n) + (q > ctrl ? q : ctrl);
 }
 
 }  // namespace qs
@@ -44,6 +46,14 @@ extern "C" {
 size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, int n) {
   if ((mode != QS_W4A16 && mode != QS_W4A4) || M < 1 || M > QS_MAX_M || !chain_ok(chain, n)) return 0;
   return chain_workspace(mode, M, chain, n);
+}
+
+int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n) {
+  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (!chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
+  if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  return pass_eligible(mode, M, chain, n) ? pass_launch_count(n) : 0;
 }
 
 int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
@@ -62,6 +72,8 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
                       reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + ab)};
   void* qws = static_cast<unsigned char*>(ws) + 2 * ab;
   const size_t qws_bytes = ws_bytes - 2 * ab;
+  if (pass_eligible(mode, M, chain, n))
+    return launch_pass(mode, x, M, chain, n, out, buf[0], buf[1], static_cast<unsigned*>(qws), st);
   const uint16_t* in = x;
   int ldx = chain[0].K;
   for (int i = 0; i < n; ++i) {
@@ -73,7 +85,6 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
       io.y = out;
     } else {
       io.y16 = buf[i & 1];
-      io.out_scale = chain[i].out_scale;
       io.ldy = chain[i].N;
     }
     const int rc = launch_linear_io(mode, io, chain[i].w_packed, chain[i].s_packed, M, chain[i].N, chain[i].K,

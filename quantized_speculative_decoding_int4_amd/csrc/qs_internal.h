@@ -11,8 +11,9 @@ namespace qs {
 
 // Cached facts about the current device (checked once per device).
 struct DeviceInfo {
-  int ok;       // 1 if the device is a gfx950
-  int num_cus;  // compute units
+  int ok;              // 1 if the device is a gfx950
+  int num_cus;         // compute units
+  long long clock_khz; // rate of the device wall clock (wall_clock64), kHz
 };
 const DeviceInfo* device_info();
 
@@ -28,20 +29,30 @@ int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t
                   int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t st);
 
 // Input/output placement of one linear inside a chain: x with row stride ldx, optionally
-// standardised per row; output either fp32 y [M][N] or fp16(out_scale * y) into y16 with
-// row stride ldy.
+// standardised per row; output either fp32 y [M][N] or fp16(y) into y16 with row stride ldy.
 struct LinearIO {
   const uint16_t* x;
   int ldx;
   float* y;
   uint16_t* y16;
-  float out_scale;
   int ldy;
   int norm_in;  // standardise each input row over its K columns first
 };
 int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint16_t* sp, int M, int N,
                      int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
                      size_t ws_bytes, hipStream_t st);
+
+// Persistent pass kernel (pass.hip): one resident workgroup per CU runs up to kMaxPassStages
+// linears of a chain per launch.
+constexpr int kMaxPassStages = 64;
+constexpr int kMaxPassWorkgroups = 1024;
+// Control region of a persistent pass in the workspace: go word and error word, then one
+// 128-byte arrival flag per workgroup.
+constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
+bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
+int pass_launch_count(int n);  // launches of a persistent pass over n linears
+int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
+                uint16_t* act0, uint16_t* act1, unsigned* ctrl, hipStream_t st);
 
 size_t verify_workspace(int B, int gamma, int V);
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,

@@ -45,6 +45,7 @@ _SIGS = {
     "qs_verify_workspace_bytes": ([_i, _i, _i], _sz),
     "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
     "qs_chain_forward": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p], _i),
+    "qs_chain_pass_launches": ([_i, _i, _p, _i], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_sample": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
 }
@@ -242,27 +243,33 @@ def qs_verify_sample(tgt_logits, drf_logits, draft_ids, u_accept, u_final, out=N
 class LinearDesc(ctypes.Structure):
     """Mirror of qs_linear_desc."""
     _fields_ = [("w_packed", ctypes.c_void_p), ("s_packed", ctypes.c_void_p),
-                ("N", ctypes.c_int), ("K", ctypes.c_int), ("out_scale", ctypes.c_float)]
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
 
 
 class Chain:
     """A host array of qs_linear_desc plus references that keep the packed
-    weight tensors alive.  `layers` is a sequence of (w_packed, s_packed, N, K,
-    out_scale)."""
+    weight tensors alive.  `layers` is a sequence of (w_packed, s_packed, N, K)."""
 
     def __init__(self, layers):
         self.tensors = []
         self.n = len(layers)
         self.array = (LinearDesc * self.n)()
-        for i, (wp, sp, n, k, scale) in enumerate(layers):
+        for i, (wp, sp, n, k) in enumerate(layers):
             _wcheck(wp, sp, n, k)
             self.tensors.append((wp, sp))
-            self.array[i] = LinearDesc(wp.data_ptr(), sp.data_ptr(), n, k, float(scale))
+            self.array[i] = LinearDesc(wp.data_ptr(), sp.data_ptr(), n, k)
         self.out_features = layers[-1][2]
         self.in_features = layers[0][3]
 
     def workspace_bytes(self, mode: int, m: int) -> int:
         return _lib.qs_chain_workspace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
+
+    def pass_launches(self, mode: int, m: int) -> int:
+        """Persistent pass-kernel launches of qs_chain_forward (0: one launch per linear)."""
+        rc = _lib.qs_chain_pass_launches(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
+        if rc < 0:
+            _check("qs_chain_pass_launches", rc)
+        return rc
 
 
 def qs_chain_forward(mode: int, x, chain: Chain, out=None, ws=None):

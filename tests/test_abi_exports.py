@@ -90,6 +90,17 @@ def test_argument_errors_before_any_device_work(lib):
     assert vg(fake, fake, 1, 64, 10, fake, None, fake, fake, fake, 1 << 20, None) == -2  # gamma > 63
     assert vg(fake, fake, 1, 3, 10, fake, None, fake, fake, None, 0, None) == -4
     assert vg(fake, None, 1, 3, 10, fake, None, fake, fake, fake, 1 << 20, None) == -1   # draft ids
+    # chain descriptors are read on the host: a chain whose K does not follow the previous N
+    desc = (ctypes.c_char * 48)()
+    ctypes.memmove(desc, (ctypes.c_uint64 * 6)(fake, fake, (4096 << 32) | 4096, fake, fake,
+                                               (8192 << 32) | 4096), 48)
+    pl = lib.qs_chain_pass_launches
+    pl.argtypes = [i, i, p, i]
+    pl.restype = i
+    assert pl(0, 4, ctypes.addressof(desc), 2) == -1                  # 8192 > 4096 columns
+    assert pl(0, 4, ctypes.addressof(desc), 1) in (-6, 0, 1)          # one linear: valid
+    assert pl(2, 4, ctypes.addressof(desc), 1) == -1                  # bad mode
+    assert pl(0, 300, ctypes.addressof(desc), 1) == -2                # M > 256
 
 
 def test_no_gpu_means_device_error(lib):

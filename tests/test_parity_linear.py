@@ -7,7 +7,7 @@ import torch
 
 from oracle import qspec_oracle as O
 from quantized_speculative_decoding_int4_amd import workloads as W
-from tests.gpu_util import assert_linear_close, dev, host
+from tests.gpu_util import assert_linear_close, chain_rel_tolerance, dev, host, linear_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -179,7 +179,7 @@ def _gpu_chain(qs, mode, x, layers):
     packed = []
     for q, s in layers:
         wp, sp = _pack(qs, q, s)
-        packed.append((wp, sp, q.shape[0], q.shape[1], 1.0))
+        packed.append((wp, sp, q.shape[0], q.shape[1]))
     chain = qs.Chain(packed)
     return host(qs.qs_chain_forward(mode, dev(x), chain))
 
@@ -221,3 +221,37 @@ def test_chain_small_llama_like(qs, mode, m):
     y = _gpu_chain(qs, mode, x, layers)
     ref = O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers)
     assert_linear_close(y, ref, f"chain mode={mode} m={m}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12)])
+def test_chain_longer_than_one_persistent_launch(qs, mode, m):
+    """69 linears.  At M <= 4 (W4A16) / M <= 8 (W4A4) the persistent pass splits
+    them over two launches, so the hand-over at the seam (fp16 activations and
+    row statistics in the workspace) is covered; M = 12 runs linear by linear.
+    End to end the output must stay within the chain bound; the last stage,
+    fed the GPU's own fp16 input to it, within the single-linear bound."""
+    print(f"long chain mode={mode} m={m}", flush=True)
+    rng = W.rng_for(900 + 10 * m + mode)
+    shapes = [(384, 256), (256, 384)] * 34 + [(1000, 256)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 256)
+    packed = []
+    for q, sc in layers:
+        wp, sp = _pack(qs, q, sc)
+        packed.append((wp, sp, q.shape[0], q.shape[1]))
+    chain = qs.Chain(packed)
+    persistent = (m <= 4) if mode == 0 else (m <= 8)
+    assert chain.pass_launches(mode, m) == (2 if persistent else 0)
+    y = host(qs.qs_chain_forward(mode, dev(x), chain))
+    name = "w4a16" if mode == 0 else "w4a4"
+    ref = O.chain_forward(name, x, layers)
+    rel, mx = linear_errors(y, ref)
+    tol = chain_rel_tolerance(len(layers))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    print(f"  end to end: rel_fro={rel:.3e} max_abs={mx:.3e} (chain bound {tol:.3e}, rms {rms:.3f})", flush=True)
+    assert rel <= tol and mx <= 10.0 * tol * rms, f"long chain mode={mode} m={m}: rel_fro={rel:.3e} max_abs={mx:.3e}"
+    prev = host(qs.qs_chain_forward(mode, dev(x), qs.Chain(packed[:-1]))).astype(np.float16)
+    q, sc = layers[-1]
+    xin = O.standardize_rows(np.ascontiguousarray(prev[:, :q.shape[1]]))
+    ref_last = O.linear_w4a16(xin, q, sc) if mode == 0 else O.linear_w4a4(xin, q, sc)["y"]
+    assert_linear_close(y, ref_last, f"long chain last stage mode={mode} m={m}")
