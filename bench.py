@@ -22,6 +22,7 @@ baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +34,28 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "verify-pass weight GB/s (% HBM peak) at M=4; accept positions/sec"
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "pass_kernels_llama8b_iteration.md")
+
+
+def counted_traffic(key):
+    """HBM bytes per launch of a pass kernel, from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded
+    (copy-calibrated) in the committed profile summary; None if the summary is missing or the kernel
+    sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            line = next(ln for ln in f if ln.startswith("traffic-json: "))
+        rec = json.loads(line[len("traffic-json: "):])
+        h = hashlib.sha256()
+        for name in rec["files"]:
+            with open(os.path.join(ROOT, name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return rec[key]["fetch_bytes_per_launch"] + rec[key]["write_bytes_per_launch"]
+    except (OSError, StopIteration, KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -47,6 +70,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the bench, copy this many MiB device to device twice (a plain copy kernel of known "
+                         "size, to scale memory-traffic counters under a profiler)")
     return ap.parse_args()
 
 
@@ -268,7 +294,7 @@ def main():
     # preceded by a one-workgroup control reset; bytes and time are averaged per launch.
     stream = torch.cuda.current_stream()
 
-    def pass_roofline(mode, m, x, out, ws, name, reps=10):
+    def pass_roofline(mode, m, x, out, ws, name, traffic_key, reps=10):
         launches = chain.pass_launches(mode, m)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -287,14 +313,14 @@ def main():
         achieved = alg / (pass_ms * 1e-3) / 1e9
         log(f"{name}: {pass_ms * 1e3:.1f} us per pass, {launches} launches, {achieved:.0f} GB/s")
         return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": name,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(traffic_key), "kernel": name,
                 "bytes_per_launch": alg / per, "avg_launch_us": pass_ms * 1e3 / per,
                 "launches_per_pass": launches, "passes_timed": reps}
 
     roof_draft = pass_roofline(qs.QS_W4A4, 1, x_draft[0], logits_q[0, 0:1], ws_draft,
-                               "pass_kernel<W4A4> (draft pass, M=1, int8 MFMA)")
+                               "pass_kernel<W4A4> (draft pass, M=1, int8 MFMA)", "w4a4")
     roof_verify = pass_roofline(qs.QS_W4A16, M_VERIFY, x_verify, logits_p[0], ws_verify,
-                                "pass_kernel<W4A16> (verify pass, M=4, fp16 MFMA)")
+                                "pass_kernel<W4A16> (verify pass, M=4, fp16 MFMA)", "w4a16")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -334,6 +360,15 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB copied twice")
 
 
 if __name__ == "__main__":
