@@ -473,11 +473,23 @@ constexpr size_t kMaxLdsStage = 131072;  // bytes of activations staged in LDS
 static bool w4a4_fused(int M, int K) { return M <= kFusedMaxM && (size_t)M * K <= kMaxLdsStage; }
 static bool w4a16_lds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= kMaxLdsStage; }
 
-size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
-  (void)N;
+// From this many rows on (and without the per-group accumulator output) a linear runs as the
+// register-tiled batched kernel of gemm.hip instead of the streaming kernel.
+constexpr int kGemmMinRows = 16;
+static bool use_gemm(int M, const int32_t* acc_out) { return M >= kGemmMinRows && acc_out == nullptr; }
+
+// Scratch of one linear: the standardised (W4A16) or quantized (W4A4) activations when they are
+// staged in memory, then the K-split partials of the batched kernel.  Sized for the case without
+// the per-group accumulator output (it only ever makes the need smaller).
+static size_t staging_bytes(int mode, int M, int K, bool norm_in) {
   if (mode == QS_W4A16) return (norm_in && !w4a16_lds(M, K)) ? align_up((size_t)M * K * 2, 256) : 0;
   if (w4a4_fused(M, K)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
+}
+
+size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
+  const size_t stage = staging_bytes(mode, M, K, norm_in);
+  return stage + (use_gemm(M, nullptr) ? gemm_workspace(M, N, K) : 0);
 }
 
 template <int MODE, int MT, int S, bool XLDS>
@@ -591,8 +603,13 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   a.N = N;
   a.K = K;
   a.norm_in = io.norm_in;
-  const size_t need = linear_workspace(mode, M, N, K, io.norm_in != 0);
+  // the staging part is required; the batched kernel's split partials are optional (without them it
+  // does not split K)
+  const size_t need = staging_bytes(mode, M, K, io.norm_in != 0);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QS_ERR_WORKSPACE;
+  const bool gemm = use_gemm(M, acc_out);
+  void* gws = ws ? static_cast<unsigned char*>(ws) + need : nullptr;
+  const size_t gws_bytes = ws && ws_bytes > need ? ws_bytes - need : 0;
   if (mode == QS_W4A16) {
     if (w4a16_lds(M, K)) return launch_split<MODE_W4A16, 1, true>(a, (size_t)M * K * 2, st);
     if (io.norm_in) {
@@ -604,6 +621,9 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
       a.ldx = K;
       a.norm_in = 0;
     }
+    if (gemm)
+      return launch_gemm(QS_W4A16, a.x, a.ldx, nullptr, nullptr, wp, sp, M, N, K, a.y, a.y16,
+                         a.y16 ? a.ldy : N, gws, gws_bytes, st);
     return launch_chunked<MODE_W4A16>(a, st);
   }
   if (w4a4_fused(M, K)) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
@@ -613,6 +633,9 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
                      xq_out, sx_out);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
+  if (gemm)
+    return launch_gemm(QS_W4A4, nullptr, 0, xq_op, sxf, wp, sp, M, N, K, a.y, a.y16, a.y16 ? a.ldy : N, gws,
+                       gws_bytes, st);
   a.xq = xq_op;
   a.sxf = sxf;
   a.xq_out = nullptr;

@@ -42,6 +42,13 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
                      int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
                      size_t ws_bytes, hipStream_t st);
 
+// Batched linear (gemm.hip), M >= 16 rows: x fp16 [M][ldx] (W4A16) or operand-ordered codes
+// xq [M][K] with fp32 row scales sxf (W4A4); output fp32 y [M][N] or fp16 y16 (row stride ldy).
+size_t gemm_workspace(int M, int N, int K);
+int launch_gemm(int mode, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf, const uint8_t* wp,
+                const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy, void* ws,
+                size_t ws_bytes, hipStream_t st);
+
 // Persistent pass kernel (pass.hip): one resident workgroup per CU runs up to kMaxPassStages
 // linears of a chain per launch.
 constexpr int kMaxPassStages = 64;
