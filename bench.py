@@ -11,6 +11,9 @@ with draft length 3:
 Each phase is captured once as a HIP graph and replayed; HIP events between
 the phases time them.
 
+Also measured (batched verify): the same stack at M = B (gamma + 1) rows for
+B in {1, 4, 16} x gamma in {3, 5, 7}, both modes, with MFMA utilisation.
+
 Printed JSON line: `value` = verify-pass weight GB/s (3,869,589,504 weight
 bytes per pass / verify-pass time), plus draft-pass rates, accept positions/s,
 the roofline of the dominant kernel (the persistent W4A4 pass kernel: the three
@@ -288,6 +291,51 @@ def main():
         }
         del tg, dr, wsg
 
+    # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
+    # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in both modes; each point is one
+    # graph-replayed pass, timed with HIP events.  MFMA utilisation = 2 M (weights) flop / time
+    # against the dense peak of the mode's MFMA (fp16 2.5166 PFLOP/s, int8 5.0332 POP/s).
+    n_weights = sum(n * k for (_, n, k) in shapes)
+    peaks = {qs.QS_W4A16: 2.5166e15, qs.QS_W4A4: 5.0332e15}
+    batched = {"points": []}
+    rng_b = W.rng_for(21)
+    for (B, G) in ((1, 3), (1, 5), (1, 7), (4, 3), (4, 5), (4, 7), (16, 3), (16, 5), (16, 7)):
+        m = B * (G + 1)
+        xb = torch.from_numpy(W.activations(rng_b, m, W.HIDDEN)[0]).to(dev)
+        ob = torch.empty((m, V), dtype=torch.float32, device=dev)
+        for mode, mname in ((qs.QS_W4A16, "w4a16"), (qs.QS_W4A4, "w4a4")):
+            wsb = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
+            qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
+            g.replay()
+            torch.cuda.synchronize()
+            ea, eb = E(enable_timing=True), E(enable_timing=True)
+            ea.record()
+            for _ in range(3):
+                g.replay()
+            eb.record()
+            torch.cuda.synchronize()
+            ms = ea.elapsed_time(eb) / 3
+            ops = 2.0 * m * n_weights
+            batched["points"].append({
+                "B": B, "gamma": G, "M": m, "mode": mname, "pass_ms": ms,
+                "weight_GBps": pass_bytes / (ms * 1e-3) / 1e9,
+                "tflops": ops / (ms * 1e-3) / 1e12,
+                "mfma_util": ops / (ms * 1e-3) / peaks[mode],
+                "persistent_launches": chain.pass_launches(mode, m),
+            })
+            del g, wsb
+        assert bool(torch.isfinite(ob).all()), "non-finite batched logits"
+        del xb, ob
+    for pt in batched["points"]:
+        if pt["M"] == 128:
+            batched[f"M128_{pt['mode']}"] = {k: pt[k] for k in ("pass_ms", "weight_GBps", "tflops", "mfma_util")}
+    log("batched verify M=128: W4A16 %.3f ms (%.1f%% of fp16 MFMA), W4A4 %.3f ms (%.1f%% of int8 MFMA)" % (
+        batched["M128_w4a16"]["pass_ms"], 100 * batched["M128_w4a16"]["mfma_util"],
+        batched["M128_w4a4"]["pass_ms"], 100 * batched["M128_w4a4"]["mfma_util"]))
+
     # ---------------- rooflines of the pass kernels (HIP events on the launch stream)
     # Algorithmic bytes of one pass: packed weights (0.515625 B per weight) plus, per linear,
     # x = 2*M*K and y = 4*M*N bytes.  A pass runs as `launches` persistent launches, each
@@ -355,6 +403,7 @@ def main():
         "iteration_accepted_tokens": n_acc + 1,
         "draft_verify_top1_agreement": agree,
         "accept_positions_per_s": accept,
+        "batched_verify": batched,
         "roofline": roof_draft,
         "roofline_verify": roof_verify,
         "cpu_baseline": cpu,
