@@ -595,7 +595,9 @@ __global__ void pass_reset_kernel(unsigned* flags, int n_flags, unsigned* go, un
 static int pick_pass_split(int N, int K, int grid);
 
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
-  if (mode == QS_W4A16 ? M > 4 : M > 8) return false;
+  // W4A4 above one row: every workgroup would quantize all rows itself and the fp16 exchange grows
+  // with M; measured on MI355X, one launch per linear is as fast from M = 2 on.
+  if (mode == QS_W4A16 ? M > 4 : M > 1) return false;
   const int grid = device_info()->num_cus;
   if (grid < 1 || grid > kMaxPassWorkgroups) return false;
   for (int i = 0; i < n; ++i) {
