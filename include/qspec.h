@@ -171,6 +171,25 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
  */
 int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n);
 
+/*
+ * Wall-clock limit, in microseconds, of every grid-barrier wait inside a
+ * persistent pass (process-wide; default 200000).  A wait that passes it sets
+ * the workspace's time-out word and the workgroup exits, so a pass can never
+ * wait forever (its output is then undefined).  0 makes every wait fail at
+ * once, which exercises that path.  QS_ERR_INVALID_ARG if us < 0.
+ */
+int qs_set_barrier_timeout_us(int us);
+
+/*
+ * Whether the last qs_chain_forward call on this workspace (same chain and
+ * arguments) had a grid-barrier wait time out: *timed_out = 1 if so, else 0.
+ * Synchronises `stream`.  The word is cleared by the next persistent
+ * qs_chain_forward on the workspace.  Chains that run one launch per linear
+ * always report 0.  Errors as qs_chain_forward.
+ */
+int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, void* ws,
+                         size_t ws_bytes, int* timed_out, void* stream);
+
 /* Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V). */
 size_t qs_verify_workspace_bytes(int B, int gamma, int V);
 

@@ -56,6 +56,31 @@ int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n) 
   return pass_eligible(mode, M, chain, n) ? pass_launch_count(n) : 0;
 }
 
+int qs_set_barrier_timeout_us(int us) {
+  if (us < 0) return QS_ERR_INVALID_ARG;
+  set_pass_barrier_timeout_us(us);
+  return QS_OK;
+}
+
+int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, void* ws, size_t ws_bytes,
+                         int* timed_out, void* stream) {
+  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (!timed_out || !chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
+  if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < chain_workspace(mode, M, chain, n)) return QS_ERR_WORKSPACE;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  *timed_out = 0;
+  if (!pass_eligible(mode, M, chain, n)) return QS_OK;  // one launch per linear: no grid barrier
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // control region after the two activation buffers; its second word is the time-out word
+  unsigned* err = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + 2 * act_bytes(M, chain, n)) + 1;
+  unsigned word = 0;
+  if (hipMemcpyAsync(&word, err, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess) return QS_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QS_ERR_HIP;
+  *timed_out = word != 0 ? 1 : 0;
+  return QS_OK;
+}
+
 int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
                      void* ws, size_t ws_bytes, void* stream) {
   if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;

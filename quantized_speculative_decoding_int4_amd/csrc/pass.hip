@@ -41,6 +41,7 @@
 #include "qs_device.h"
 #include "qs_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace qs {
@@ -170,6 +171,10 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kFlagStride = 32;  // uint32 words between flags (128 bytes)
 
 __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, const PassArgs& a) {
+  if (a.deadline <= 0) {  // a zero limit fails at once (exercises the time-out path)
+    __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
   const long long t0 = wall_clock64();
   while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v) {
     __builtin_amdgcn_s_sleep(1);
@@ -625,6 +630,10 @@ static int pick_pass_split(int N, int K, int grid) {
 
 int pass_launch_count(int n) { return (n + kMaxPassStages - 1) / kMaxPassStages; }
 
+static std::atomic<int> g_barrier_timeout_us{200000};
+int pass_barrier_timeout_us() { return g_barrier_timeout_us.load(); }
+void set_pass_barrier_timeout_us(int us) { g_barrier_timeout_us.store(us); }
+
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
                 uint16_t* act0, uint16_t* act1, unsigned* ctrl, hipStream_t st) {
   const DeviceInfo* di = device_info();
@@ -669,7 +678,7 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     a.go = ctrl;
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
-    a.deadline = di->clock_khz * 200LL;  // 200 ms per barrier wait
+    a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
     a.n_stages = cnt;
     for (int i = 0; i < cnt; ++i) {

@@ -58,6 +58,8 @@ constexpr int kMaxPassWorkgroups = 1024;
 constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
 int pass_launch_count(int n);  // launches of a persistent pass over n linears
+int pass_barrier_timeout_us();  // wall-clock limit of one grid-barrier wait (process-wide)
+void set_pass_barrier_timeout_us(int us);
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
                 uint16_t* act0, uint16_t* act1, unsigned* ctrl, hipStream_t st);
 

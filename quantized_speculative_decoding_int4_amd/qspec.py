@@ -46,6 +46,8 @@ _SIGS = {
     "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
     "qs_chain_forward": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p], _i),
     "qs_chain_pass_launches": ([_i, _i, _p, _i], _i),
+    "qs_set_barrier_timeout_us": ([_i], _i),
+    "qs_chain_pass_status": ([_i, _i, _p, _i, _p, _sz, _p, _p], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_sample": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
 }
@@ -270,6 +272,20 @@ class Chain:
         if rc < 0:
             _check("qs_chain_pass_launches", rc)
         return rc
+
+
+def qs_set_barrier_timeout_us(us: int) -> None:
+    """Wall-clock limit of each grid-barrier wait of the persistent pass (0: fail at once)."""
+    _check("qs_set_barrier_timeout_us", _lib.qs_set_barrier_timeout_us(int(us)))
+
+
+def qs_chain_pass_status(mode: int, m: int, chain: "Chain", ws) -> bool:
+    """True if the last persistent chain call on `ws` had a grid-barrier wait time out."""
+    flag = ctypes.c_int(0)
+    _check("qs_chain_pass_status", _lib.qs_chain_pass_status(
+        mode, m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n, _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), ctypes.byref(flag), _stream()))
+    return bool(flag.value)
 
 
 def qs_chain_forward(mode: int, x, chain: Chain, out=None, ws=None):

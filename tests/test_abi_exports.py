@@ -101,6 +101,16 @@ def test_argument_errors_before_any_device_work(lib):
     assert pl(0, 4, ctypes.addressof(desc), 1) in (-6, 0, 1)          # one linear: valid
     assert pl(2, 4, ctypes.addressof(desc), 1) == -1                  # bad mode
     assert pl(0, 300, ctypes.addressof(desc), 1) == -2                # M > 256
+    to = lib.qs_set_barrier_timeout_us
+    to.argtypes = [i]
+    to.restype = i
+    assert to(-1) == -1
+    stf = lib.qs_chain_pass_status
+    stf.argtypes = [i, i, p, i, p, sz, p, p]
+    stf.restype = i
+    assert stf(0, 4, ctypes.addressof(desc), 1, fake, 1 << 30, None, None) == -1   # no result pointer
+    flag = ctypes.c_int(7)
+    assert stf(0, 4, ctypes.addressof(desc), 1, None, 0, ctypes.addressof(flag), None) == -4  # no workspace
 
 
 def test_no_gpu_means_device_error(lib):
