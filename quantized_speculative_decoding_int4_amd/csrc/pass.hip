@@ -60,10 +60,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 #define QS_PASS_STREAM_WAVES 8
 #endif
 #ifndef QS_PASS_CTRL_WAVES
-#define QS_PASS_CTRL_WAVES 4
+#define QS_PASS_CTRL_WAVES 8
 #endif
 #ifndef QS_PASS_RING
-#define QS_PASS_RING 24
+#define QS_PASS_RING 16
 #endif
 constexpr int kSW = QS_PASS_STREAM_WAVES;  // streaming waves: weight ring + MFMA (split S x R)
 constexpr int kCW = QS_PASS_CTRL_WAVES;    // control waves: reductions, stores, barriers, staging
