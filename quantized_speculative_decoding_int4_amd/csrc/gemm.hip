@@ -85,16 +85,18 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
                         : reinterpret_cast<const unsigned char*>(a.xq + (size_t)r * a.K) + col * 16;
     adst[j] = (uint32_t)(row * kPitch + col * 16);
   }
-  uint4 areg[kPieces];
+  // A native vector type: an array of HIP's uint4 struct is copied with memcpy and stays in
+  // scratch memory instead of registers.
+  int4_t areg[kPieces];
   auto a_load = [&](int g) __attribute__((always_inline)) {
     const int gg = g < g1 ? g : g1 - 1;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j)
-      areg[j] = *reinterpret_cast<const uint4*>(asrc[j] + (size_t)gg * kRowB);
+      areg[j] = *reinterpret_cast<const int4_t*>(asrc[j] + (size_t)gg * kRowB);
   };
   auto a_store = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kPieces; ++j) *reinterpret_cast<uint4*>(&abuf[b][adst[j]]) = areg[j];
+    for (int j = 0; j < kPieces; ++j) *reinterpret_cast<int4_t*>(&abuf[b][adst[j]]) = areg[j];
   };
 
   // Weight row blocks past N read block 0 (never stored).
