@@ -165,15 +165,17 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
  * Number of persistent pass-kernel launches qs_chain_forward makes for this
  * chain on the current device (each runs a run of consecutive linears with
  * grid-wide hand-over between them), or 0 if the chain runs one linear per
- * launch (row counts or shapes the persistent kernel does not take).  Each
- * persistent launch is preceded by a one-workgroup launch that clears its
- * control words.  Negative status codes as qs_chain_forward for bad arguments.
+ * launch (row counts or shapes the persistent kernel does not take).  The
+ * persistent launches of a pass are preceded by one launch that clears the
+ * control words and (W4A4) fills the stage outputs with the not-yet-written
+ * pattern.  Negative status codes as qs_chain_forward for bad arguments.
  */
 int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n);
 
 /*
- * Wall-clock limit, in microseconds, of every grid-barrier wait inside a
- * persistent pass (process-wide; default 200000).  A wait that passes it sets
+ * Wall-clock limit, in microseconds, of every wait inside a persistent pass
+ * (W4A16: a grid-barrier wait; W4A4: the wait for one stage's input to be
+ * written) (process-wide; default 200000).  A wait that passes it sets
  * the workspace's time-out word and the workgroup exits, so a pass can never
  * wait forever (its output is then undefined).  0 makes every wait fail at
  * once, which exercises that path.  QS_ERR_INVALID_ARG if us < 0.
@@ -182,7 +184,7 @@ int qs_set_barrier_timeout_us(int us);
 
 /*
  * Whether the last qs_chain_forward call on this workspace (same chain and
- * arguments) had a grid-barrier wait time out: *timed_out = 1 if so, else 0.
+ * arguments) had a wait time out: *timed_out = 1 if so, else 0.
  * Synchronises `stream`.  The word is cleared by the next persistent
  * qs_chain_forward on the workspace.  Chains that run one launch per linear
  * always report 0.  Errors as qs_chain_forward.

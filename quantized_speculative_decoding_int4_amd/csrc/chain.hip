@@ -26,15 +26,21 @@ static size_t act_bytes(int M, const qs_linear_desc* c, int n) {
   return align_up((size_t)M * maxn * 2, 256);
 }
 
-size_t chain_workspace(int mode, int M, const qs_linear_desc* c, int n) {
+// Workspace: two fp16 ping-pong buffers for the launch-per-linear path, then the per-linear scratch
+// or the control words of the persistent pass, then (for row counts a persistent pass takes) the
+// stage outputs of the persistent pass.
+static size_t scratch_bytes(int mode, int M, const qs_linear_desc* c, int n) {
   size_t q = 0;
   for (int i = 0; i < n; ++i) {
     const size_t w = linear_workspace(mode, M, c[i].N, c[i].K, i > 0);
     q = w > q ? w : q;
   }
-  // control words of the persistent pass: go + error word, then one 128-byte flag per workgroup
-  const size_t ctrl = kPassCtrlBytes;
-  return 2 * act_bytes(M, c, n) + (q > ctrl ? q : ctrl);
+  return align_up(q > kPassCtrlBytes ? q : kPassCtrlBytes, 256);
+}
+
+size_t chain_workspace(int mode, int M, const qs_linear_desc* c, int n) {
+  const size_t stages = M <= pass_max_rows(mode) ? pass_stage_bytes(M, c, n) : 0;
+  return 2 * act_bytes(M, c, n) + scratch_bytes(mode, M, c, n) + stages;
 }
 
 }  // namespace qs
@@ -70,9 +76,9 @@ int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, vo
   if (!ws || ws_bytes < chain_workspace(mode, M, chain, n)) return QS_ERR_WORKSPACE;
   if (!device_info()->ok) return QS_ERR_DEVICE;
   *timed_out = 0;
-  if (!pass_eligible(mode, M, chain, n)) return QS_OK;  // one launch per linear: no grid barrier
+  if (!pass_eligible(mode, M, chain, n)) return QS_OK;  // one launch per linear: no waits
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // control region after the two activation buffers; its second word is the time-out word
+  // control region after the two activation buffers; its second word is the error word
   unsigned* err = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + 2 * act_bytes(M, chain, n)) + 1;
   unsigned word = 0;
   if (hipMemcpyAsync(&word, err, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess) return QS_ERR_HIP;
@@ -97,8 +103,11 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
                       reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + ab)};
   void* qws = static_cast<unsigned char*>(ws) + 2 * ab;
   const size_t qws_bytes = ws_bytes - 2 * ab;
-  if (pass_eligible(mode, M, chain, n))
-    return launch_pass(mode, x, M, chain, n, out, buf[0], buf[1], static_cast<unsigned*>(qws), st);
+  if (pass_eligible(mode, M, chain, n)) {
+    uint16_t* stage_out =
+        reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(qws) + scratch_bytes(mode, M, chain, n));
+    return launch_pass(mode, x, M, chain, n, out, static_cast<unsigned*>(qws), stage_out, st);
+  }
   const uint16_t* in = x;
   int ldx = chain[0].K;
   for (int i = 0; i < n; ++i) {

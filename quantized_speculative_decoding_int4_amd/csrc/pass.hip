@@ -9,18 +9,29 @@
 // compute unit stays resident for all stages.  Every wave owns a flattened
 // stream of 1 KiB weight tiles across all stages of the launch and keeps a ring
 // of kPRing tile loads in flight; weights do not depend on activations, so the
-// ring runs ahead into the next stage while the workgroups wait at the grid
-// barrier between stages and stage the next activations in LDS.  HBM keeps
-// streaming through the dependency.
+// ring runs ahead into the next stage while the workgroups wait for the stage's
+// input and stage it in LDS.  HBM keeps streaming through the dependency.
 //
-// Stage hand-over without cache maintenance: stage outputs are written with
-// device-coherent stores (they bypass the per-XCD L2 on the way to memory) and
-// read back with device-coherent loads, so neither side needs the L2 write-back
-// and invalidate of an agent-scope release/acquire (measured at about 3.5 us per
-// boundary on MI355X).  The grid barrier is a flag per workgroup gathered by
-// workgroup 0, which then publishes a `go` word; every wait has a wall-clock
-// deadline that sets an error word and makes the workgroup exit, so no wave can
-// wait forever even if the workgroups were not all resident.
+// Stage hand-over.  Every stage of a pass writes its fp16 output to a buffer of
+// its own with device-coherent stores, and the next stage reads it with
+// device-coherent loads (both go past the per-XCD L2 to memory), so no L2
+// write-back or invalidate is needed (an agent-scope release/acquire costs about
+// 3.5 us per boundary on MI355X).  Two ways to know the input is complete:
+//  * W4A4 (one row, 8-28 KiB of input): the data carries the signal.  The output
+//    buffers start filled with the pattern 0xFFFF (a NaN the epilogue never
+//    emits: it rewrites that one pattern as the canonical NaN 0x7E00).  A
+//    consumer fetches its input as soon as its own stage is done and reads again
+//    every 16-byte piece that still holds the pattern.  Each piece is written by
+//    one workgroup in 2-byte stores, so a piece read while it is being written
+//    shows the pattern in the halves not yet written.  This saves the producer's
+//    wait for its store acknowledgements and the two hops of a grid barrier.
+//  * W4A16 (four rows, up to 112 KiB of input): a grid barrier, then one fetch.
+//    A premature fetch of that much data costs a second full round trip, which
+//    measured slower than the barrier.  Workgroup b stores an epoch into its own
+//    flag once its outputs are acknowledged; workgroup 0 gathers the flags and
+//    publishes the epoch in a `go` word.
+// Every wait has a wall-clock deadline that sets an error word and makes the
+// workgroup exit, so no wave can wait forever.
 //
 // Tile math per stage is the one of linear.hip: a wave's share of a 16-row block
 // (S waves split K), expansion of the nibbles in VGPRs, MFMA with the staged
@@ -31,7 +42,7 @@
 // the contraction: with mean mu and 1/std inv of input row m,
 //   sum_k w[n,k] (x[m,k] - mu) inv = (sum_k w[n,k] x[m,k] - mu sum_k w[n,k]) inv,
 // and sum_k w[n,k] comes for free from an all-ones row placed in the zero padding
-// of the 16-row A operand.  The input therefore goes to LDS by direct DMA and its
+// of the 16-row A operand.  The input therefore goes to LDS as it arrives and its
 // statistics are computed while the contraction runs.  This skips the fp16
 // rounding of the standardised input (a relative 2^-12 per term).  W4A4 stages
 // must quantise the standardised row first, so they stage through registers:
@@ -73,30 +84,31 @@ constexpr int kPThreads = 64 * (kSW + kCW);
 constexpr int kPRing = QS_PASS_RING;       // tiles in flight per streaming wave (two loads each)
 constexpr size_t kPassLdsStage = 114688;   // activations staged per stage: M * K * element bytes
 constexpr int kPassSlots = 4;              // row-block sets a workgroup may own per stage
+constexpr int kPiecesMax4 = 8;             // W4A4: 16-byte input pieces a control thread holds per stage
+constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
 constexpr int kSc1 = 16;                   // cache-policy bit SC1: device-coherent access
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw 32-bit buffer resource, no swizzle
 
 struct PassStage {
   const uint4* w;      // packed tiles
   const uint16_t* sc;  // packed scales
+  uint16_t* y16;       // fp16 output [M][N], filled with kEmpty before the launch (not the last stage)
   int N, K;
   int s_log2;          // S = 1 << s_log2 streaming waves split K of one row block
   int nsets;           // row-block sets: ceil(nrb / R), R = kSW / S
 };
 
 struct PassArgs {
-  const uint16_t* x;  // input of the launch's first stage, fp16, row stride ldx0
+  const uint16_t* x;  // input of the launch's first stage, fp16, row stride ldx0 (complete at launch)
   int ldx0;
   int norm0;          // standardise the first stage's input rows
-  uint16_t* act0;     // ping-pong fp16 stage outputs (row stride = that stage's N)
-  uint16_t* act1;
-  int act_first;      // act buffer written by the launch's first stage
   float* out;         // fp32 output of the launch's last stage when last_is_final
   int last_is_final;
-  unsigned* flags;    // per-workgroup arrival epochs (kFlagStride apart), zeroed before the launch
-  unsigned* go;       // released epoch, zeroed before the launch
-  unsigned* error;    // set to 1 if a barrier wait passed its deadline
-  long long deadline; // wall-clock ticks allowed per barrier wait
+  unsigned* flags;    // W4A16: per-workgroup arrival epochs (kFlagStride apart), zero at pass start
+  unsigned* go;       // W4A16: released epoch, zero at pass start
+  unsigned epoch0;    // W4A16: epochs of this launch's boundaries are epoch0 + 1, epoch0 + 2, ...
+  unsigned* error;    // set to 1 if a wait passed its deadline
+  long long deadline; // wall-clock ticks allowed per wait
   int M;
   int n_stages;
   PassStage st[kMaxPassStages];
@@ -113,6 +125,7 @@ __device__ __forceinline__ PassStage stage_at(int i) {
   PassStage p;
   p.w = k->st[u].w;
   p.sc = k->st[u].sc;
+  p.y16 = k->st[u].y16;
   p.N = k->st[u].N;
   p.K = k->st[u].K;
   p.s_log2 = k->st[u].s_log2;
@@ -164,10 +177,48 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Grid barrier between stages, free of contended atomics: workgroup b release-stores the epoch
-// into its own flag (one 128-byte line each); the control threads of workgroup 0 each watch flags
-// and, once all have arrived, workgroup 0 release-stores the epoch into the `go` word that every
-// workgroup acquires.  Each wait has a wall-clock deadline; passing it sets the error word.
+// True if any of the 8 halves of v holds kEmpty: ~v then has a zero halfword, which the
+// borrow test (w - 0x00010001) & ~w & 0x80008000 detects (exactly, for the "any" question).
+__device__ __forceinline__ bool has_empty(const uint4 v) {
+  auto zero_half = [](uint32_t w) { return (w - 0x00010001u) & ~w & 0x80008000u; };
+  return (zero_half(~v.x) | zero_half(~v.y) | zero_half(~v.z) | zero_half(~v.w)) != 0u;
+}
+
+// Buffer resource over extent bytes at base (base the same in all lanes); reads past the extent
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sc1_rsrc(const void* base, uint32_t extent) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent, (int)kBufWord3);
+}
+// 16 bytes from a device-coherent read at byte offset voff (per lane) + soff (uniform).
+__device__ __forceinline__ uint4 load_sc1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kSc1));
+}
+
+// 16 bytes per active lane from global memory straight into LDS (lane l writes lds_addr + 16 l),
+// with a device-coherent read.  Written as inline assembly: when the compiler sees an LDS-DMA
+// anywhere in the kernel it makes every LDS read wait for all outstanding vector loads, which would
+// drain the weight rings of the streaming waves.  The caller waits (s_waitcnt vmcnt(0)) before
+// using the data; loads the compiler does not know about only make its own waits stricter, since
+// loads complete in order.  lds_addr must be the same in all lanes.
+__device__ __forceinline__ void dma_to_lds_sc1(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory", "m0");
+}
+
+// LDS barriers every wave executes at a stage boundary:
+//   A partials parked |
+//   W4A16 grid barrier: B outputs stored | C arrivals seen (workgroup 0) | D go seen |
+//   staging: W4A16 G activations in LDS; W4A4 E statistics | F row parameters | G codes in LDS
+// and the staging barriers once before the first stage.  The last stage ends after A.
+// Streaming waves only pass through them.
+constexpr int kGridBarriers = 3;
+template <int MODE>
+constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
+
+// W4A16 grid barrier between stages, free of contended atomics: workgroup b stores the epoch into
+// its own flag (one 128-byte line each) once its outputs are acknowledged; the control threads of
+// workgroup 0 each watch flags and, once all have arrived, workgroup 0 stores the epoch into the
+// `go` word that every workgroup waits for.  All of these are device-coherent accesses.
 constexpr int kFlagStride = 32;  // uint32 words between flags (128 bytes)
 
 __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, const PassArgs& a) {
@@ -185,32 +236,6 @@ __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, con
   }
   return true;
 }
-
-// 16 bytes per lane from global memory straight into LDS (lane l writes lds_addr + 16 l), with a
-// device-coherent read.  Written as inline assembly: when the compiler sees an LDS-DMA anywhere in
-// the kernel it makes every LDS read wait for all outstanding vector loads, which would drain the
-// weight rings of the streaming waves.  The caller waits (s_waitcnt vmcnt(0)) before using the data;
-// loads the compiler does not know about only make its own waits stricter, since loads complete in
-// order.  lds_addr must be the same in all lanes.
-__device__ __forceinline__ void dma_to_lds_sc1(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory", "m0");
-}
-
-// 16 bytes from a device-coherent read of base + byte offset (base the same in all lanes).
-__device__ __forceinline__ uint4 load_sc1(const void* base, uint32_t off, uint32_t extent) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent, (int)kBufWord3);
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
-}
-
-// LDS barriers every wave executes at a stage boundary:
-//   A partials parked | B outputs stored | C arrivals seen (workgroup 0) | D go seen |
-//   staging: W4A16 G activations in LDS; W4A4 E statistics | F row parameters | G codes in LDS
-// and the staging barriers once before the first stage.  The last stage ends after B.
-// Streaming waves only pass through them.
-template <int MODE>
-constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
 
 template <int MODE>
 __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
@@ -297,12 +322,10 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     auto next_stage = [&]() __attribute__((always_inline)) {
       while (true) {
         lds_barrier();  // A
-        lds_barrier();  // B
         if (cs + 1 >= a.n_stages) { cs = a.n_stages; return; }
-        lds_barrier();  // C
-        lds_barrier();  // D
-        if (__builtin_amdgcn_readfirstlane(fail_sh)) { cs = a.n_stages; return; }
+        if constexpr (MODE == 0) static_for<0, kGridBarriers>([&](auto) { lds_barrier(); });  // B C D
         static_for<0, kStagingBarriers<MODE>>([&](auto) { lds_barrier(); });
+        if (__builtin_amdgcn_readfirstlane(fail_sh)) { cs = a.n_stages; return; }
         ++cs;
         cv = stage_view(stage_at(cs), wave, bid, grid);
         set_a();
@@ -380,115 +403,143 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     zero_pad[ct] = 0u;
     ones_pad[ct] = 0x3C003C00u;
   }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)dyn_lds;
-  // W4A4 staging layout: rows spread over groups of control threads (gsz threads per row).
-  const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  const int gsz = kCT / mp;                   // threads per row
-  const int unit = gsz < 64 ? gsz : 64;       // lanes per reduction unit (32 or 64)
+  // Input rows spread over groups of control threads: gsz threads per row (M <= 4, so gsz >= 128),
+  // thread row_tid of a group holds pieces row_tid, row_tid + gsz, ... (at most kPiecesMax4, host
+  // check) of its row.  Reduction units are whole waves.
+  const int mp = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+  const int gsz = kCT / mp;
   const int my_row = ct / gsz;
   const int row_tid = ct - my_row * gsz;
-  const int my_unit = ct / unit;              // reduction unit index (< 2 * kCW)
-  const int units_per_row = gsz / unit;
-  constexpr int kXBatch = 8;
-
-  auto unit_sum = [&](float v) {
-    for (int o = unit >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-  };
-  auto unit_max = [&](float v) {
-    for (int o = unit >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-  };
-  auto unit_min = [&](float v) {
-    for (int o = unit >> 1; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-    return v;
-  };
-  auto stage_input = [&](int s) -> const uint16_t* {
-    return s == 0 ? a.x : (((a.act_first + s - 1) & 1) ? a.act1 : a.act0);
-  };
+  const int units_per_row = gsz / 64;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)dyn_lds;
 
   // Stage s input -> LDS, ending with the staging barriers (work only if this workgroup has sets).
-  auto prologue = [&](int s, bool has) {
+  auto wait_failed = [&](long long t0) {
+    if (a.deadline > 0 && wall_clock64() - t0 <= a.deadline) return false;  // a zero limit fails at once
+    __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fail_sh = 1;
+    return true;
+  };
+
+  // W4A16 (input complete: after the grid barrier, or from the previous launch): raw fp16 rows
+  // straight into LDS, [M][K] row-major, by direct DMA, 64 pieces (1 KiB) per wave instruction.
+  // The row statistics for the epilogue are taken after barrier G, while the contraction runs,
+  // by one control wave per row (needed at barrier A).
+  auto stage_in16 = [&](int s, bool has) __attribute__((always_inline)) {
     const int K = stage_at(s).K;
-    const uint16_t* x = stage_input(s);
+    const uint16_t* x = s == 0 ? a.x : stage_at(s - 1).y16;
     const int ldx = s == 0 ? a.ldx0 : stage_at(s - 1).N;
     const int norm = s == 0 ? a.norm0 : 1;
-    if constexpr (MODE == 0) {
-      // Raw fp16 rows straight into LDS, [M][K] row-major: one 1 KiB chunk per wave instruction.
-      if (has) {
-        const int total = M * K;
-        const int nch = (total + 511) / 512;
-        for (int ch = cw; ch < nch; ch += kCW) {
-          const int e = ch * 512 + lane * 8;
-          if (e < total) {
-            const int row = e / K, col = e - row * K;
-            dma_to_lds_sc1(x + (size_t)row * ldx + col, lds_base + (uint32_t)ch * 1024u);
-          }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int nb = K / 8;  // pieces per row
+    if (has) {
+      // the wave's chunks q = cw, cw + kCW, ... of M * cpr: (row, 64-piece column block), no division
+      const int cpr = (nb + 63) >> 6;
+      int m = 0, c = cw;
+      while (c >= cpr) { c -= cpr; ++m; }
+      while (m < M) {
+        const int pi = (c << 6) + lane;
+        if (pi < nb) dma_to_lds_sc1(x + (size_t)m * ldx + 8 * pi, lds_base + (uint32_t)(m * K + 8 * (c << 6)) * 2u);
+        c += kCW;
+        while (c >= cpr) { c -= cpr; ++m; }
       }
-      lds_barrier();  // G
-      // Row statistics for the epilogue, one control wave per row, while the contraction runs.
-      if (has && cw < M) {
-        float mu = 0.f, inv = 1.f;
-        if (norm) {
-          const uint4* r = reinterpret_cast<const uint4*>(dyn_lds) + (size_t)cw * (K / 8);
-          float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-          for (int i = lane; i < K / 8; i += 64) stats_block8(r[i], su, sq, mx, mn);
-          su = wave_sum(su);
-          sq = wave_sum(sq);
-          norm_params(su, sq, K, mu, inv);
-        }
-        if (lane == 0) {
-          row_a[cw] = mu;
-          row_b[cw] = inv;
-        }
-      }
-    } else {
-      const int nb = K / 8;
-      const bool active = has && my_row < M;
-      const bool one_batch = nb <= kXBatch * gsz;
-      const uint32_t rows_bytes = (uint32_t)(((M - 1) * ldx + K) * 2);
-      const uint32_t row_off = (uint32_t)((my_row < M ? my_row : 0) * ldx * 2);
-      uint4 v[kXBatch];
-      auto load_batch = [&](int base) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();  // G
+    if (has && cw < M) {
+      float mu = 0.f, inv = 1.f;
+      if (norm) {
+        const uint4* r = reinterpret_cast<const uint4*>(dyn_lds) + (size_t)cw * nb;
+        float su = 0.f, sq = 0.f, mx = 0.f, mn = 0.f;
+        for (int i0 = 0; i0 < nb; i0 += 256) {  // four LDS reads in flight per lane
+          uint4 v[4];
 #pragma unroll
-        for (int j = 0; j < kXBatch; ++j) {
-          const int i = base + row_tid + j * gsz;
-          if (i < nb) v[j] = load_sc1(x, row_off + (uint32_t)i * 16u, rows_bytes);
-        }
-      };
-      float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-      if (active) {
-        for (int base = 0; base < nb; base += kXBatch * gsz) {
-          load_batch(base);
-#pragma unroll
-          for (int j = 0; j < kXBatch; ++j) {
-            const int i = base + row_tid + j * gsz;
-            if (i < nb) stats_block8(v[j], su, sq, mx, mn);
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 64 * u + lane;
+            v[u] = i < nb ? r[i] : make_uint4(0u, 0u, 0u, 0u);
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) stats_block8(v[u], su, sq, mx, mn);  // zero pieces add nothing
+        }
+        su = wave_sum_dpp(su);
+        sq = wave_sum_dpp(sq);
+        norm_params(su, sq, K, mu, inv);
+      }
+      if (lane == 0) {
+        row_a[cw] = mu;
+        row_b[cw] = inv;
+      }
+    }
+  };
+
+  // W4A4: rows staged through registers (statistics, scale, quantisation, then LDS).  From the
+  // launch's second stage on, the input is being written by other workgroups: pieces that still
+  // hold kEmpty are read again until all hold data or the deadline passes.  Each thread
+  // holds P pieces, P a compile-time bucket of the stage's pieces per thread chosen with a uniform
+  // branch.  The loads are unconditional: a load under a condition is merged with the old value by
+  // a select, and the compiler then keeps two copies of all pieces live.  Pieces past this thread's
+  // count are read (next row, or zeros past the buffer resource's extent) and not used.
+  auto stage_in4 = [&](auto pc, int s, bool has) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    const int K = stage_at(s).K;
+    const uint16_t* x = s == 0 ? a.x : stage_at(s - 1).y16;
+    const int ldx = s == 0 ? a.ldx0 : stage_at(s - 1).N;
+    const int norm = s == 0 ? a.norm0 : 1;
+    const int nb = K / 8;  // pieces per row
+    // A whole wave serves one row (gsz >= 128), so `active` is wave-uniform.
+    const bool active = has && my_row < M;
+    const int np = row_tid < nb ? (nb - row_tid + gsz - 1) / gsz : 0;  // this thread's pieces
+    // piece j of this thread: byte offset voff + j * pstride
+    const __amdgpu_buffer_rsrc_t rs = sc1_rsrc(x, (uint32_t)(((M - 1) * ldx + K) * 2));
+    const uint32_t voff = (uint32_t)(((my_row < M ? my_row : 0) * ldx + 8 * row_tid) * 2);
+    const uint32_t pstride = (uint32_t)gsz * 16u;
+    uint4 v[P];
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)j * pstride);
+      if (s > 0) {
+        auto pending = [&]() {
+          uint32_t m = 0;
+#pragma unroll
+          for (int j = 0; j < P; ++j)
+            if (j < np && has_empty(v[j])) m |= 1u << j;
+          return m;
+        };
+        const long long t0 = wall_clock64();
+        while (a.deadline <= 0 || __any(pending() != 0u)) {
+          if (wait_failed(t0)) break;
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)j * pstride);  // data, once there, stays
         }
       }
-      su = unit_sum(su);
-      sq = unit_sum(sq);
-      mx = unit_max(mx);
-      mn = unit_min(mn);
-      if ((ct & (unit - 1)) == 0) {
-        stat_red[0][my_unit] = su;
-        stat_red[1][my_unit] = sq;
-        stat_red[2][my_unit] = mx;
-        stat_red[3][my_unit] = mn;
-      }
-      lds_barrier();  // E
-      if (has && ct < M) {
-        const int m = ct;
-        float tsu = 0.f, tsq = 0.f, xmax = -INFINITY, xmin = INFINITY;
-        for (int u = m * units_per_row; u < (m + 1) * units_per_row; ++u) {
-          tsu += stat_red[0][u];
-          tsq += stat_red[1][u];
-          xmax = fmaxf(xmax, stat_red[2][u]);
-          xmin = fminf(xmin, stat_red[3][u]);
-        }
+    }
+    float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < P; ++j)
+        if (j < np) stats_block8(v[j], su, sq, mx, mn);
+    }
+    su = wave_sum_dpp(su);
+    sq = wave_sum_dpp(sq);
+    mx = wave_max_dpp(mx);
+    mn = wave_min_dpp(mn);
+    if (lane == 0) {
+      stat_red[0][cw] = su;
+      stat_red[1][cw] = sq;
+      stat_red[2][cw] = mx;
+      stat_red[3][cw] = mn;
+    }
+    lds_barrier();  // E
+    // Row parameters, one wave per row: lane u reads the statistics of the row's u-th wave.
+    if (has && cw < M) {
+      const int m = cw;
+      const bool mine = lane < units_per_row;
+      const int u = m * units_per_row + (mine ? lane : 0);
+      const float tsu = lanes8_reduce_dpp(mine ? stat_red[0][u] : 0.f, [](float p, float q) { return p + q; });
+      const float tsq = lanes8_reduce_dpp(mine ? stat_red[1][u] : 0.f, [](float p, float q) { return p + q; });
+      const float xmax = lanes8_reduce_dpp(mine ? stat_red[2][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
+      const float xmin = lanes8_reduce_dpp(mine ? stat_red[3][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
+      if (lane == 0) {
         float mu = 0.f, inv = 0.f;
         if (norm) norm_params(tsu, tsq, K, mu, inv);
         row_a[m] = mu;
@@ -497,31 +548,44 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
                                 : fmaxf(xmax, -xmin);
         row_c[m] = h2f(f2h(amax / 7.0f));
       }
-      lds_barrier();  // F
-      if (active) {
-        int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K;
-        const float mu = row_a[my_row], inv = row_b[my_row], sc = row_c[my_row];
-        for (int base = 0; base < nb; base += kXBatch * gsz) {
-          if (!one_batch) load_batch(base);
+    }
+    lds_barrier();  // F
+    if (active) {
+      int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K + 8 * row_tid;
+      const float mu = row_a[my_row], inv = row_b[my_row], sc = row_c[my_row];
 #pragma unroll
-          for (int j = 0; j < kXBatch; ++j) {
-            const int i = base + row_tid + j * gsz;
-            if (i < nb) {
-              uint4 w = v[j];
-              if (norm) w = norm_block8(w, mu, inv);
-              uint2 op, lg;
-              quant_block8(w, sc, op, lg);
-              *reinterpret_cast<uint2*>(xq + (size_t)i * 8) = op;
-            }
-          }
+      for (int j = 0; j < P; ++j) {
+        if (j < np) {
+          uint4 w = v[j];
+          if (norm) w = norm_block8(w, mu, inv);
+          uint2 op, lg;
+          quant_block8(w, sc, op, lg);
+          *reinterpret_cast<uint2*>(xq + j * (pstride / 2)) = op;
         }
       }
-      lds_barrier();  // G
+    }
+    lds_barrier();  // G
+  };
+
+  auto prologue = [&](int s) {
+    const bool has = stage_sets(stage_at(s), bid, grid) > 0 && !fail_sh;
+    if constexpr (MODE == 0) {
+      stage_in16(s, has);
+    } else {
+      const int npmax = (stage_at(s).K / 8 + gsz - 1) / gsz;  // <= kPiecesMax4 (host check)
+      static_assert(kPiecesMax4 == 8, "piece buckets below end at kPiecesMax4");
+      if (npmax <= 2)
+        stage_in4(std::integral_constant<int, 2>{}, s, has);
+      else if (npmax <= 4)
+        stage_in4(std::integral_constant<int, 4>{}, s, has);
+      else
+        stage_in4(std::integral_constant<int, 8>{}, s, has);
     }
   };
 
-  prologue(0, stage_sets(stage_at(0), bid, grid) > 0);
   for (int s = 0; s < a.n_stages; ++s) {
+    prologue(s);
+    if (__builtin_amdgcn_readfirstlane(fail_sh)) return;
     lds_barrier();  // A: the streaming waves have parked the partials of stage s
     const PassStage ps = stage_at(s);
     const int sets = stage_sets(ps, bid, grid);
@@ -531,7 +595,6 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       const int S = 1 << ps.s_log2, R = kSW >> ps.s_log2;
       const int nrb = (ps.N + 15) >> 4, N = ps.N;
       const int norm = s == 0 ? a.norm0 : 1;
-      uint16_t* o16 = ((a.act_first + s) & 1) ? a.act1 : a.act0;
       for (int p = cw; p < sets * R; p += kCW) {
         const int si = p / R, r2 = p - si * R;
         const int rb = (bid + si * grid) * R + r2;
@@ -555,44 +618,52 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
               } else {
                 outv *= row_c[m];
               }
-              if (final_out)
+              if (final_out) {
                 a.out[(size_t)m * N + n] = outv;
-              else  // device-coherent store: read by other workgroups after the grid barrier
-                __hip_atomic_store(o16 + (size_t)m * N + n, f2h(outv), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              } else {  // device-coherent store, read by other workgroups in the next stage
+                uint16_t h = f2h(outv);
+                if (h == kEmpty) h = 0x7E00u;
+                __hip_atomic_store(ps.y16 + (size_t)m * N + n, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
             }
           }
         }
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's output stores have completed
-    lds_barrier();  // B
-    if (s + 1 >= a.n_stages) return;
-    const unsigned epoch = (unsigned)(s + 1);
-    if (ct == 0)
-      __hip_atomic_store(a.flags + (size_t)bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (bid == 0) {
-      for (int t = ct; t < grid; t += kCT)
-        if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
+    if constexpr (MODE == 0) {
+      if (s + 1 < a.n_stages) {  // grid barrier: all outputs of stage s are in memory
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's output stores have completed
+        lds_barrier();  // B
+        const unsigned epoch = a.epoch0 + (unsigned)(s + 1);
+        if (ct == 0)
+          __hip_atomic_store(a.flags + (size_t)bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bid == 0) {
+          for (int t = ct; t < grid; t += kCT)
+            if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
+        }
+        lds_barrier();  // C
+        if (ct == 0) {
+          if (bid == 0 && !fail_sh) __hip_atomic_store(a.go, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (!fail_sh && !wait_at_least(a.go, epoch, a)) fail_sh = 1;
+        }
+        lds_barrier();  // D
+      }
     }
-    lds_barrier();  // C
-    if (ct == 0) {
-      if (bid == 0 && !fail_sh)
-        __hip_atomic_store(a.go, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!fail_sh && !wait_at_least(a.go, epoch, a)) fail_sh = 1;
-    }
-    lds_barrier();  // D
-    if (__builtin_amdgcn_readfirstlane(fail_sh)) return;
-    prologue(s + 1, stage_sets(stage_at(s + 1), bid, grid) > 0);
   }
 }
 
-__global__ void pass_reset_kernel(unsigned* flags, int n_flags, unsigned* go, unsigned* error,
-                                  int clear_error) {
-  for (int i = threadIdx.x; i < n_flags; i += blockDim.x) flags[(size_t)i * 32] = 0u;
-  if (threadIdx.x == 0) {
-    go[0] = 0u;
-    if (clear_error) error[0] = 0u;
+// Start of a pass: fills the stage outputs with kEmpty (W4A4; device-coherent stores) and zeroes the
+// control words (go and error word, then n_flags arrival flags kFlagStride apart).
+__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < 2) __hip_atomic_store(ctrl + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < n_flags; i += 256)
+      __hip_atomic_store(ctrl + (size_t)(i + 1) * kFlagStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bufs, (short)0, (int)(n16 * 16u), (int)kBufWord3);
+  const int4_t e = int4_t{-1, -1, -1, -1};
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += gridDim.x * 256u)
+    __builtin_amdgcn_raw_buffer_store_b128(e, r, (int)(i * 16u), 0, kSc1);
 }
 
 // ------------------------------------------------------------------ host side
@@ -602,14 +673,24 @@ static int pick_pass_split(int N, int K, int grid);
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   // W4A4 above one row: every workgroup would quantize all rows itself and the fp16 exchange grows
   // with M; measured on MI355X, one launch per linear is as fast from M = 2 on.
-  if (mode == QS_W4A16 ? M > 4 : M > 1) return false;
+  if (M > pass_max_rows(mode)) return false;
   const int grid = device_info()->num_cus;
   if (grid < 1 || grid > kMaxPassWorkgroups) return false;
+  const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);  // control threads per input row
   for (int i = 0; i < n; ++i) {
     if ((size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1) > kPassLdsStage) return false;
+    if (mode == QS_W4A4 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
     if (pick_pass_split(c[i].N, c[i].K, grid) < 0) return false;
   }
   return true;
+}
+
+int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : 1; }
+
+size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
+  size_t b = 0;
+  for (int i = 0; i + 1 < n; ++i) b += align_up((size_t)M * c[i].N * 2, 256);
+  return b;
 }
 
 // K-split S per stage: fewest tiles per wave, subject to at most kPassSlots sets per workgroup;
@@ -635,7 +716,7 @@ int pass_barrier_timeout_us() { return g_barrier_timeout_us.load(); }
 void set_pass_barrier_timeout_us(int us) { g_barrier_timeout_us.store(us); }
 
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                uint16_t* act0, uint16_t* act1, unsigned* ctrl, hipStream_t st) {
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st) {
   const DeviceInfo* di = device_info();
   const int grid = di->num_cus;
   auto fn0 = pass_kernel<0>;
@@ -655,10 +736,23 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     lds = b > lds ? b : lds;
   }
 
+  // Stage outputs of the whole pass -> kEmpty, error word -> 0.
+  const size_t sb = pass_stage_bytes(M, c, n);
+  if (sb > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
+  const uint32_t n16 = mode == QS_W4A4 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
+  const unsigned rblocks = n16 == 0 ? 1u : (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024u;
+  hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks), dim3(256), 0, st, reinterpret_cast<uint4*>(stage_out),
+                     n16, ctrl, mode == QS_W4A16 ? grid : 0);
+  int rc = launch_status();
+  if (rc != QS_OK) return rc;
+
+  // Output of stage i at the running offset: stages are laid out in chain order.
+  unsigned char* const base = reinterpret_cast<unsigned char*>(stage_out);
+  size_t off = 0;           // offset of the next stage's output
+  uint16_t* prev = nullptr;  // output of the stage before the launch's first
   const int launches = pass_launch_count(n);
   const int per_launch = (n + launches - 1) / launches;
-  int act_first = 0;
-  for (int s0 = 0, li = 0; s0 < n; s0 += per_launch, ++li) {
+  for (int s0 = 0; s0 < n; s0 += per_launch) {
     const int cnt = n - s0 < per_launch ? n - s0 : per_launch;
     PassArgs a{};
     if (s0 == 0) {
@@ -666,18 +760,16 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
       a.ldx0 = c[0].K;
       a.norm0 = 0;
     } else {
-      a.x = ((act_first + 1) & 1) ? act1 : act0;  // output of stage s0-1
+      a.x = prev;  // written by the previous launch
       a.ldx0 = c[s0 - 1].N;
       a.norm0 = 1;
     }
-    a.act0 = act0;
-    a.act1 = act1;
-    a.act_first = act_first;
     a.out = out;
     a.last_is_final = s0 + cnt == n;
     a.go = ctrl;
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
+    a.epoch0 = (unsigned)s0;
     a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
     a.n_stages = cnt;
@@ -686,23 +778,24 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
       PassStage& p = a.st[i];
       p.w = reinterpret_cast<const uint4*>(d.w_packed);
       p.sc = d.s_packed;
+      p.y16 = nullptr;
+      if (s0 + i + 1 < n) {
+        p.y16 = reinterpret_cast<uint16_t*>(base + off);
+        off += align_up((size_t)M * d.N * 2, 256);
+        prev = p.y16;
+      }
       p.N = d.N;
       p.K = d.K;
       p.s_log2 = pick_pass_split(d.N, d.K, grid);
       const int R = kPW >> p.s_log2;
       p.nsets = ((d.N + 15) / 16 + R - 1) / R;
     }
-    hipLaunchKernelGGL(pass_reset_kernel, dim3(1), dim3(256), 0, st, ctrl + kFlagStride, grid, ctrl, ctrl + 1,
-                       li == 0 ? 1 : 0);
-    int rc = launch_status();
-    if (rc != QS_OK) return rc;
     if (mode == QS_W4A16)
       hipLaunchKernelGGL(pass_kernel<0>, dim3(grid), dim3(kPThreads), lds, st, a);
     else
       hipLaunchKernelGGL(pass_kernel<1>, dim3(grid), dim3(kPThreads), lds, st, a);
     rc = launch_status();
     if (rc != QS_OK) return rc;
-    act_first = (act_first + cnt) & 1;
   }
   return QS_OK;
 }

@@ -100,6 +100,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Data-parallel-primitive (DPP) reductions: four in-row steps (pairs, quads, halves of 8, rows of
+// 16) leave every lane with its 16-lane row's result; the four rows are then combined from lanes
+// 0, 16, 32 and 48.  Fixed order, all 64 lanes active, result in every lane.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
+  auto dpp = [](float x, int ctrl) {
+    switch (ctrl) {  // the control word must be a constant
+      case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+      case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+      case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  v = op(v, dpp(v, 0));  // quad_perm [1,0,3,2]
+  v = op(v, dpp(v, 1));  // quad_perm [2,3,0,1]
+  v = op(v, dpp(v, 2));  // row_half_mirror
+  v = op(v, dpp(v, 3));  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return wave_reduce_dpp(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return wave_reduce_dpp(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_min_dpp(float v) {
+  return wave_reduce_dpp(v, [](float a, float b) { return fminf(a, b); });
+}
+// Result of op over lanes 0..7 (after the first three in-row steps), returned from lane 0.
+template <typename Op>
+__device__ __forceinline__ float lanes8_reduce_dpp(float v, Op op) {
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+}
+
 // (value, index) max with the lowest index winning ties.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll

@@ -53,15 +53,18 @@ int launch_gemm(int mode, const uint16_t* x, int ldx, const int8_t* xq, const fl
 // linears of a chain per launch.
 constexpr int kMaxPassStages = 64;
 constexpr int kMaxPassWorkgroups = 1024;
-// Control region of a persistent pass in the workspace: go word and error word, then one
-// 128-byte arrival flag per workgroup.
+// Control region of a persistent pass in the workspace: go word and error word, then one 128-byte
+// arrival flag per workgroup.
 constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
+int pass_max_rows(int mode);   // most rows a persistent pass takes in this mode
 int pass_launch_count(int n);  // launches of a persistent pass over n linears
-int pass_barrier_timeout_us();  // wall-clock limit of one grid-barrier wait (process-wide)
+// fp16 outputs of all stages but the last, each 256-byte aligned, in chain order
+size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n);
+int pass_barrier_timeout_us();  // wall-clock limit of one wait for a stage's input (process-wide)
 void set_pass_barrier_timeout_us(int us);
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                uint16_t* act0, uint16_t* act1, unsigned* ctrl, hipStream_t st);
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st);
 
 size_t verify_workspace(int B, int gamma, int V);
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,
