@@ -171,8 +171,8 @@ def main():
     u_fin = torch.from_numpy(W.uniforms(rng, (1,))).to(dev)
     ws_draft = torch.empty(chain.workspace_bytes(qs.QS_W4A4, 1), dtype=torch.uint8, device=dev)
     ws_verify = torch.empty(chain.workspace_bytes(qs.QS_W4A16, M_VERIFY), dtype=torch.uint8, device=dev)
-    ws_acc = torch.empty(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
-    ws_acc2 = torch.empty(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
+    ws_acc = torch.zeros(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
+    ws_acc2 = torch.zeros(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
     draft_out = [{
         "tgt_top1": torch.empty((1, 1), dtype=torch.int32, device=dev), "top1_prob": None,
         "n_accept": torch.empty((1,), dtype=torch.int32, device=dev), "out_tokens": d[:, i:i + 1],
@@ -277,7 +277,7 @@ def main():
         dd = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
         ua = torch.from_numpy(W.uniforms(rng, (B, G))).to(dev)
         uf = torch.from_numpy(W.uniforms(rng, (B,))).to(dev)
-        wsg = torch.empty(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+        wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
         go = qs.qs_verify_greedy(tg, dd, ws=wsg)
         so = qs.qs_verify_sample(tg, dr, dd, ua, uf, ws=wsg)
         tgms = time_calls(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg))

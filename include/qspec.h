@@ -53,6 +53,7 @@ extern "C" {
 
 #define QS_GROUP 128   /* k-elements per weight scale group */
 #define QS_MAX_M 256   /* most activation rows per linear call */
+#define QS_MAX_VERIFY_SEQS 16384 /* sequences per verify launch block */
 
 typedef enum { QS_W4A16 = 0, QS_W4A4 = 1 } qs_mode;
 
@@ -192,7 +193,18 @@ int qs_set_barrier_timeout_us(int us);
 int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, void* ws,
                          size_t ws_bytes, int* timed_out, void* stream);
 
-/* Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V). */
+/*
+ * Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V);
+ * 0 for arguments out of range (gamma > 63).  A batch of more than
+ * QS_MAX_VERIFY_SEQS sequences runs as consecutive blocks of at most that many
+ * on the stream, so the size stops growing there.
+ *
+ * A verify workspace must be zero-filled once before its first use: its first
+ * 4 MiB hold per-sequence arrival counters (the last workgroup of a sequence
+ * to arrive finishes it within the same launch), and every call leaves them at
+ * zero again, so one workspace can then serve any sequence of calls and shapes
+ * on one stream.  Calls that overlap in time must not share a workspace.
+ */
 size_t qs_verify_workspace_bytes(int B, int gamma, int V);
 
 /*
@@ -208,7 +220,8 @@ size_t qs_verify_workspace_bytes(int B, int gamma, int V);
  *   [0, V) are mismatches and are never used as addresses; may be NULL if gamma = 0)
  *   tgt_top1   int32 [B][gamma+1] (out);  top1_prob fp32 [B][gamma+1] (out, nullable)
  *   n_accept   int32 [B] (out);  out_tokens int32 [B][gamma+1] (out)
- *   ws         >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch
+ *   ws         >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch,
+ *              zero-filled before its first use (see qs_verify_workspace_bytes)
  */
 int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
                      int B, int gamma, int V,
@@ -232,7 +245,8 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
  *   draft_ids int32 [B][gamma];  u_accept fp32 [B][gamma] in [0,1);  u_final fp32 [B]
  *   accept_prob fp32 [B][gamma] (out);  n_accept int32 [B] (out)
  *   out_tokens int32 [B][gamma+1] (out);  final_dist fp32 [B][V] (out, nullable) = f
- *   ws >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch
+ *   ws >= qs_verify_workspace_bytes(B, gamma, V) bytes of scratch, zero-filled
+ *   before its first use (see qs_verify_workspace_bytes)
  * gamma = 0 draws one token from p_0 with u_final (drf_logits, draft_ids,
  * u_accept and accept_prob may then be NULL).
  */

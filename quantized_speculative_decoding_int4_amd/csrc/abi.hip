@@ -133,8 +133,9 @@ static int verify_common_checks(const float* tgt, int B, int gamma, int V, void*
   if (!tgt) return QS_ERR_INVALID_ARG;
   if (B < 1 || gamma < 0 || V < 1) return QS_ERR_INVALID_ARG;
   if (gamma > kMaxGamma || V > kMaxVocab) return QS_ERR_UNSUPPORTED;
-  const size_t C = (size_t)((V + 4095) / 4096);
-  if ((size_t)B * (2 * (size_t)gamma + 1) * C > (size_t)INT_MAX) return QS_ERR_UNSUPPORTED;
+  const size_t C = (size_t)((V + 2047) / 2048);  // the finest chunking of a row
+  const size_t Bb = B < QS_MAX_VERIFY_SEQS ? (size_t)B : (size_t)QS_MAX_VERIFY_SEQS;  // one block's grid
+  if (Bb * (2 * (size_t)gamma + 1) * C > (size_t)INT_MAX) return QS_ERR_UNSUPPORTED;
   const size_t need = verify_workspace(B, gamma, V);
   if (ws == nullptr || ws_bytes < need) return QS_ERR_WORKSPACE;
   if (!aligned16(ws)) return QS_ERR_MISALIGNED;

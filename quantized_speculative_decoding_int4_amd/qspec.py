@@ -180,8 +180,8 @@ def qs_lmhead(mode: int, x, w_packed, s_packed, v: int, logits=None, ws=None):
 
 def _ws_for(b, gamma, v, ws, device):
     need = verify_workspace_bytes(b, gamma, v)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws is None:  # zero-filled: the first bytes are arrival counters that start at zero
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
     return ws
 
 

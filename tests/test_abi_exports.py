@@ -67,6 +67,10 @@ def test_verify_workspace_helper(lib):
     f.argtypes = [ctypes.c_int] * 3
     assert f(1, 3, 128256) > 0
     assert f(0, 3, 10) == 0 and f(1, -1, 10) == 0 and f(1, 64, 10) == 0
+    # per-sequence arrival counters sit in a fixed area at the start, one 256-byte line per
+    # sequence; larger batches run in blocks of 16384 sequences that reuse one block's workspace
+    assert f(1, 0, 1) >= 16384 * 256
+    assert f(16384, 3, 4096) > f(8192, 3, 4096) and f(10**6, 3, 4096) == f(16384, 3, 4096)
 
 
 def test_argument_errors_before_any_device_work(lib):
@@ -89,7 +93,7 @@ def test_argument_errors_before_any_device_work(lib):
     vg.restype = i
     assert vg(fake, fake, 1, 64, 10, fake, None, fake, fake, fake, 1 << 20, None) == -2  # gamma > 63
     assert vg(fake, fake, 1, 3, 10, fake, None, fake, fake, None, 0, None) == -4
-    assert vg(fake, None, 1, 3, 10, fake, None, fake, fake, fake, 1 << 20, None) == -1   # draft ids
+    assert vg(fake, None, 1, 3, 10, fake, None, fake, fake, fake, 1 << 24, None) == -1   # draft ids
     # chain descriptors are read on the host: a chain whose K does not follow the previous N
     desc = (ctypes.c_char * 48)()
     ctypes.memmove(desc, (ctypes.c_uint64 * 6)(fake, fake, (4096 << 32) | 4096, fake, fake,
