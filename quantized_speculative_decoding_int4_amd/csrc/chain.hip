@@ -110,11 +110,15 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
   }
   const uint16_t* in = x;
   int ldx = chain[0].K;
+  // every linear's workspace starts at qws, so its K-split counters are shared: clear them once
+  const int rc0 = linear_clear_counters(M, qws, st);
+  if (rc0 != QS_OK) return rc0;
   for (int i = 0; i < n; ++i) {
     LinearIO io{};
     io.x = in;
     io.ldx = ldx;
     io.norm_in = i > 0;
+    io.counters_zero = 1;
     if (i + 1 == n) {
       io.y = out;
     } else {

@@ -1,9 +1,10 @@
 // Batched linear (M >= 16 activation rows): the verify pass over many sequences, where the
 // target scores B * (gamma + 1) positions at once ([P3] "draft modelとtarget modelの処理フロー";
 // modes from [P1] "QSpec の W4A4 モードと W4A16 モード").  Same arithmetic as the streaming
-// linear: W4A16 expands the INT4 codes to fp16 in registers and runs v_mfma_f32_16x16x32_f16,
-// W4A4 runs v_mfma_i32_16x16x64_i8 on the quantized activations; both scale each 128-wide group
-// partial sum in fp32.
+// linear: W4A16 expands the INT4 codes to fp16 in registers, multiplies them by their group scale
+// (q s rounded to fp16; exact when s is a power of two) and runs v_mfma_f32_16x16x32_f16 with one
+// fp32 accumulator over all of K; W4A4 runs v_mfma_i32_16x16x64_i8 on the quantized activations and
+// scales each 128-wide group's exact i32 sum in fp32.
 //
 // Work split.  A workgroup of 4 waves owns an output tile of 64 rows (4 MFMA row tiles) x 256
 // columns (16 packed row blocks, 4 per wave) over a range of K, one 128-wide group at a time:
@@ -16,6 +17,7 @@
 // The row tile is the fastest-varying workgroup index, so the workgroups that read the same weight
 // tiles for different rows run back to back and the second read is served by the caches.
 
+#include "qs_act.h"
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -24,11 +26,33 @@
 namespace qs {
 
 constexpr int kGemmWaves = 4;
-constexpr int kGemmMt = 4;                      // 16-row MFMA tiles per workgroup (all waves)
-constexpr int kGemmRows = kGemmMt * 16;         // 64 activation rows per workgroup
+constexpr int kGemmMaxMt = 4;                   // 16-row MFMA tiles per workgroup: 1, 2 or 4
+constexpr int kGemmMaxRows = kGemmMaxMt * 16;
 constexpr int kGemmNt = 4;                      // 16-column row blocks per wave
 constexpr int kGemmBlocks = kGemmWaves * kGemmNt;  // row blocks per workgroup (256 columns)
 constexpr int kGemmMaxSplits = 16;
+constexpr int kGemmMinGroupsPerSplit = 4;
+constexpr int kGemmMaxCounters = 1024;           // split runs have fewer than 256 output tiles
+
+// Partial slot of one (K split, output tile) workgroup, device-coherent, read back only by the
+// tile's last-arriving workgroup: the accumulators in register order ([wave][mt][nt][lane] float4),
+// then the column sums of the expanded weights ([wave][nt][16 columns]) and the row sums (sum, sum
+// of squares) of the staged activations ([rows] float2).  Sized for the largest row tile.
+constexpr int kSlotAcc = kGemmWaves * kGemmMaxMt * kGemmNt * 64 * 16;
+constexpr int kSlotCs = kSlotAcc;
+constexpr int kSlotStats = kSlotCs + kGemmWaves * kGemmNt * 16 * 4;
+constexpr int kSlotBytes = kSlotStats + kGemmMaxRows * 8;
+static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
+
+// 16-row tiles per workgroup (measured over the Llama-3-8B-shaped stack at M = 16...128): the
+// smallest tile that covers M up to 32 rows; beyond that 64 rows for W4A16 (each expanded weight
+// fragment feeds four MFMAs) and 32 rows for W4A4 (its expansion is cheaper, and smaller tiles need
+// fewer K splits), except for vocabulary-wide linears, where 64 rows halve the weight re-reads.
+static int gemm_mt(int mode, int M, int N) {
+  if (M <= 16) return 1;
+  if (M <= 32) return 2;
+  return (mode == QS_W4A16 || N >= 32768) ? 4 : 2;
+}
 
 struct GemmArgs {
   const uint16_t* x;   // W4A16: fp16 activations [M][ldx]
@@ -39,8 +63,10 @@ struct GemmArgs {
   const uint16_t* sc;  // packed scales
   int M, N, K;
   int gps;             // 128-wide groups per K split
-  float* part;         // splits > 1: fp32 partials [split][M][N]
-  float* y;            // splits == 1: fp32 output [M][N] ...
+  int splits;
+  unsigned char* slots;  // splits > 1: partial slots [split][tile]
+  unsigned* cnt;         // splits > 1: arrival counter per output tile (zero at launch, left zero)
+  float* y;            // fp32 output [M][N] ...
   uint16_t* y16;       // ... or fp16 output with row stride ldy
   int ldy;
 };
@@ -49,37 +75,97 @@ __device__ __forceinline__ void gemm_lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename F>
-__device__ __forceinline__ void gemm_static_for_2(F&& f) {
-  f(std::integral_constant<int, 0>{});
-  f(std::integral_constant<int, 1>{});
+template <typename F, int... Is>
+__device__ __forceinline__ void gemm_static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void gemm_static_for(F&& f) {
+  gemm_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a) {
+// Device-coherent (SC1) 16-byte and 8-byte accesses to the partial slots, through a buffer
+// resource over the slot array (offsets stay below 2^31: at most 256 tiles x 16 splits x 67 KB).
+constexpr int kGemmSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void slot_store4(unsigned char* base, int off, float4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4_t, v), gemm_rsrc(base), off, 0, kGemmSc1);
+}
+__device__ __forceinline__ float4_t slot_load4(const unsigned char* base, int off) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(gemm_rsrc(base), off, 0, kGemmSc1));
+}
+__device__ __forceinline__ void slot_store1(unsigned char* base, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), gemm_rsrc(base), off, 0, kGemmSc1);
+}
+__device__ __forceinline__ float slot_load1(const unsigned char* base, int off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(gemm_rsrc(base), off, 0, kGemmSc1));
+}
+
+// Sum of the 32 codes q of one lane's fragment (four packed dwords, offset-binary nibbles).
+__device__ __forceinline__ int fragment_code_sum(const uint4 w) {
+  unsigned u = __builtin_amdgcn_udot8(w.x, 0x11111111u, 0u, false);
+  u = __builtin_amdgcn_udot8(w.y, 0x11111111u, u, false);
+  u = __builtin_amdgcn_udot8(w.z, 0x11111111u, u, false);
+  u = __builtin_amdgcn_udot8(w.w, 0x11111111u, u, false);
+  return (int)u - 32 * 8;
+}
+
+// MODE 0 (W4A16) with NORM: the input rows are standardised over their K columns, applied after
+// the contraction as y = (sum_k x w - mu sum_k w) / sd.  The row sums come from the activations as
+// they are staged, the weight sums sum_k w from the packed codes, so no separate pass over the
+// activations is needed.  MT: 16-row tiles per workgroup; D: groups of weights in flight per wave
+// (a register ring: the weights do not depend on the activations, so they are fetched D groups
+// ahead of their use).
+template <int MODE, bool NORM, int MT, int D>
+__global__ __launch_bounds__(kGemmWaves * 64, 2) void gemm_kernel(const GemmArgs a) {
+  static_assert(MODE == 0 || !NORM, "standardisation is fused for W4A16 only");
+  constexpr int kRows = MT * 16;
   constexpr int kRowB = MODE == 0 ? 256 : 128;  // activation bytes per row and group
   constexpr int kPitch = kRowB + 16;
-  constexpr int kPieces = kGemmRows * kRowB / 16 / (kGemmWaves * 64);  // 16-byte copies per thread
+  constexpr int kTotalPieces = kRows * kRowB / 16;  // 16-byte copies per group
+  constexpr int kPieces = (kTotalPieces + kGemmWaves * 64 - 1) / (kGemmWaves * 64);
   constexpr int kSteps = MODE == 0 ? 4 : 2;     // MFMA k-steps per group
-  __shared__ __align__(16) unsigned char abuf[2][kGemmRows * kPitch];
+  static_assert(!NORM || kTotalPieces % (kGemmWaves * 64) == 0, "row statistics assume whole pieces");
+  __shared__ __align__(16) unsigned char abuf[2][kRows * kPitch];
+  __shared__ float row_mu[kRows], row_inv[kRows];
+  __shared__ int last_sh;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int G = a.K >> 7;
   const int nrb = (a.N + 15) >> 4;
-  const int m0 = (int)blockIdx.x * kGemmRows;
-  const int rb0 = (int)blockIdx.y * kGemmBlocks + wave * kGemmNt;
-  const int g0 = (int)blockIdx.z * a.gps;
+  // XCD-aware order: workgroup L of the launch runs on XCD L % 8, so consecutive logical indices
+  // (the row tiles of one column block, then its neighbours) are given to one XCD and share its L2.
+  int bx, by, split;
+  {
+    const int mtiles = (int)gridDim.x, ntiles = (int)gridDim.y;
+    const int total = mtiles * ntiles * (int)gridDim.z;
+    const int L = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int xcd = L & 7, idx = L >> 3, per = total >> 3, rem = total & 7;
+    const int lg = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    bx = lg % mtiles;
+    by = (lg / mtiles) % ntiles;
+    split = lg / (mtiles * ntiles);
+  }
+  const int m0 = bx * kRows;
+  const int rb0 = by * kGemmBlocks + wave * kGemmNt;
+  const int g0 = split * a.gps;
   const int g1 = g0 + a.gps < G ? g0 + a.gps : G;
 
-  // Activation staging: thread t copies pieces t + 256 j of the [64 rows][kRowB] chunk.  Rows past
+  // Activation staging: thread t copies pieces t + 256 j of the [rows][kRowB] chunk.  Rows past
   // M copy row M-1: result row i depends only on operand row i, and those rows are not stored.
+  // (W4A16: piece t + 256 j is row t / 16 + 16 j, so the 16 lanes of a DPP row share a row.)
   const unsigned char* asrc[kPieces];
   uint32_t adst[kPieces];
+  bool aon[kPieces];
 #pragma unroll
   for (int j = 0; j < kPieces; ++j) {
     const int p = (int)threadIdx.x + j * kGemmWaves * 64;
-    const int row = p / (kRowB / 16), col = p - row * (kRowB / 16);
+    aon[j] = p < kTotalPieces;
+    const int pc = aon[j] ? p : 0;
+    const int row = pc / (kRowB / 16), col = pc - row * (kRowB / 16);
     const int r = m0 + row < a.M ? m0 + row : a.M - 1;
     asrc[j] = MODE == 0 ? reinterpret_cast<const unsigned char*>(a.x + (size_t)r * a.ldx) + col * 16
                         : reinterpret_cast<const unsigned char*>(a.xq + (size_t)r * a.K) + col * 16;
@@ -88,15 +174,35 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
   // A native vector type: an array of HIP's uint4 struct is copied with memcpy and stays in
   // scratch memory instead of registers.
   int4_t areg[kPieces];
+  float rsum[kPieces], rsq[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) rsum[j] = rsq[j] = 0.0f;
   auto a_load = [&](int g) __attribute__((always_inline)) {
     const int gg = g < g1 ? g : g1 - 1;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j)
-      areg[j] = *reinterpret_cast<const int4_t*>(asrc[j] + (size_t)gg * kRowB);
+      if (aon[j]) areg[j] = *reinterpret_cast<const int4_t*>(asrc[j] + (size_t)gg * kRowB);
   };
-  auto a_store = [&](int b) __attribute__((always_inline)) {
+  // store the staged group into LDS buffer b; `real` = it is a group of this split (not a re-read
+  // past the end)
+  auto a_store = [&](int b, bool real) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kPieces; ++j) *reinterpret_cast<int4_t*>(&abuf[b][adst[j]]) = areg[j];
+    for (int j = 0; j < kPieces; ++j)
+      if (aon[j]) *reinterpret_cast<int4_t*>(&abuf[b][adst[j]]) = areg[j];
+    if constexpr (NORM) {
+      if (real) {
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+          const half8_t h = __builtin_bit_cast(half8_t, areg[j]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = (float)h[e];
+            rsum[j] += f;
+            rsq[j] += f * f;
+          }
+        }
+      }
+    }
   };
 
   // Weight row blocks past N read block 0 (never stored).
@@ -106,8 +212,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
     const int rb = rb0 + nt < nrb ? rb0 + nt : 0;
     wbase[nt] = (size_t)rb * G;
   }
-  uint4 wr[2][kGemmNt];
-  uint16_t sr[2][kGemmNt];
+  uint4 wr[D][kGemmNt];
+  uint16_t sr[D][kGemmNt];
   // Unconditional (a group past the range re-reads the last one), so the loads in flight are the
   // same at every slot and the compiler waits for exactly the oldest.
   auto w_issue = [&](int slot, int g) __attribute__((always_inline)) {
@@ -120,23 +226,25 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
     }
   };
 
-  float4_t acc[kGemmMt][kGemmNt];
+  float4_t acc[MT][kGemmNt];
 #pragma unroll
-  for (int mt = 0; mt < kGemmMt; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < kGemmNt; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float csum[kGemmNt];  // NORM: this lane's share of sum_k w for column lane & 15 of each block
+#pragma unroll
+  for (int nt = 0; nt < kGemmNt; ++nt) csum[nt] = 0.0f;
 
   a_load(g0);
-  w_issue(0, g0);
-  w_issue(1, g0 + 1);
-  a_store(0);
+  gemm_static_for<D>([&](auto ic) __attribute__((always_inline)) { w_issue(decltype(ic)::value, g0 + decltype(ic)::value); });
+  a_store(0, true);
   gemm_lds_barrier();
   const uint32_t magic = fp16_magic_vgpr();
   // fragment offset of this lane inside a staged row: k = 32 (lane >> 4) + step * (32 or 16)
   const uint32_t lane_off = (uint32_t)((lane & 15) * kPitch + (MODE == 0 ? 64 : 32) * (lane >> 4));
 
-  for (int g = g0; g < g1; g += 2) {
-    gemm_static_for_2([&](auto ic) __attribute__((always_inline)) {
+  for (int g = g0; g < g1; g += D) {
+    gemm_static_for<D>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       const int gi = g + i;
       if (gi < g1) {
@@ -144,11 +252,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
         a_load(gi + 1);  // next group's activations, stored after this group's math
         const unsigned char* ab = abuf[cur];
         if constexpr (MODE == 0) {
-          float4_t dg[kGemmMt][kGemmNt];
-#pragma unroll
-          for (int mt = 0; mt < kGemmMt; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kGemmNt; ++nt) dg[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+          // the group scale is folded into the expanded weights (q s rounded to fp16), so the MFMAs
+          // accumulate across groups directly
 #pragma unroll
           for (int t = 0; t < kSteps; ++t) {
             half8_t b[kGemmNt];
@@ -156,26 +261,25 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
             for (int nt = 0; nt < kGemmNt; ++nt) {
               const uint4 wv = wr[i][nt];
               const uint32_t wt = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
-              b[nt] = unpack_f16x8(wt, magic);
+              b[nt] = unpack_f16x8(wt, magic) * __builtin_bit_cast(_Float16, sr[i][nt]);
             }
 #pragma unroll
-            for (int mt = 0; mt < kGemmMt; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
               const half8_t av = *reinterpret_cast<const half8_t*>(ab + lane_off + mt * 16 * kPitch + 16 * t);
 #pragma unroll
               for (int nt = 0; nt < kGemmNt; ++nt)
-                dg[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], dg[mt][nt], 0, 0, 0);
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], acc[mt][nt], 0, 0, 0);
             }
           }
+          if constexpr (NORM) {
 #pragma unroll
-          for (int nt = 0; nt < kGemmNt; ++nt) {
-            const float s = h2f(sr[i][nt]);
-#pragma unroll
-            for (int mt = 0; mt < kGemmMt; ++mt) acc[mt][nt] += s * dg[mt][nt];
+            for (int nt = 0; nt < kGemmNt; ++nt)  // exact product; the weights' own sum, unrounded
+              csum[nt] += h2f(sr[i][nt]) * (float)fragment_code_sum(wr[i][nt]);
           }
         } else {
-          int4_t dg[kGemmMt][kGemmNt];
+          int4_t dg[MT][kGemmNt];
 #pragma unroll
-          for (int mt = 0; mt < kGemmMt; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < kGemmNt; ++nt) dg[mt][nt] = int4_t{0, 0, 0, 0};
 #pragma unroll
@@ -187,7 +291,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
               b[nt] = t2 == 0 ? unpack_i8x16(wv.x, wv.y) : unpack_i8x16(wv.z, wv.w);
             }
 #pragma unroll
-            for (int mt = 0; mt < kGemmMt; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
               const int4_t av = *reinterpret_cast<const int4_t*>(ab + lane_off + mt * 16 * kPitch + 16 * t2);
 #pragma unroll
               for (int nt = 0; nt < kGemmNt; ++nt)
@@ -196,38 +300,156 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
           }
 #pragma unroll
           for (int nt = 0; nt < kGemmNt; ++nt) {
-            const float s = h2f(sr[i][nt]);
+            const float s = h2f(sr[i][nt]) * 0.0625f;  // operands carry 16 q: exact rescale
 #pragma unroll
-            for (int mt = 0; mt < kGemmMt; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mt][nt][j] += s * (float)(dg[mt][nt][j] >> 4);  // operands carry 16 q
+              for (int j = 0; j < 4; ++j) acc[mt][nt][j] += s * (float)dg[mt][nt][j];
           }
         }
-        w_issue(i, gi + 2);  // refill this slot after consuming it
-        a_store(cur ^ 1);
+        w_issue(i, gi + D);  // refill this slot after consuming it
+        a_store(cur ^ 1, gi + 1 < g1);
         gemm_lds_barrier();
       }
     });
   }
 
-  // Epilogue: lane holds rows 4 (lane >> 4) + j of each row tile, column lane & 15 of each block.
-  const bool split = a.part != nullptr;
+  // ---- this split's column and row sums (NORM)
+  if constexpr (NORM) {
+    // columns: lanes l, l + 16, l + 32, l + 48 hold the four k quarters of column l & 15
 #pragma unroll
-  for (int mt = 0; mt < kGemmMt; ++mt) {
+    for (int nt = 0; nt < kGemmNt; ++nt) {
+      const float c0 = __shfl(csum[nt], lane & 15, 64), c1 = __shfl(csum[nt], (lane & 15) + 16, 64);
+      const float c2 = __shfl(csum[nt], (lane & 15) + 32, 64), c3 = __shfl(csum[nt], (lane & 15) + 48, 64);
+      csum[nt] = (c0 + c1) + (c2 + c3);
+    }
+    // rows: the 16 lanes of a DPP row share a row; lane 16 r + 0 keeps the result
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      auto row16 = [](float v) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+        return v;
+      };
+      rsum[j] = row16(rsum[j]);
+      rsq[j] = row16(rsq[j]);
+    }
+  }
+
+  // ---- K splits: publish this split's partials; the tile's last arrival sums all splits in split
+  // order (deterministic whichever workgroup arrives last) and writes the output.
+  const int tile = by * (int)gridDim.x + bx;
+  if (a.splits > 1) {
+    const int tiles = (int)(gridDim.x * gridDim.y);
+    unsigned char* my = a.slots + ((size_t)split * tiles + tile) * kSlotBytes;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kGemmNt; ++nt)
+        slot_store4(my, (((wave * MT + mt) * kGemmNt + nt) * 64 + lane) * 16, acc[mt][nt]);
+    if constexpr (NORM) {
+      if (lane < 16) {
+#pragma unroll
+        for (int nt = 0; nt < kGemmNt; ++nt) slot_store1(my, kSlotCs + ((wave * kGemmNt + nt) * 16 + lane) * 4, csum[nt]);
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+          const int row = (int)(threadIdx.x >> 4) + 16 * j;
+          slot_store1(my, kSlotStats + row * 8, rsum[j]);
+          slot_store1(my, kSlotStats + row * 8 + 4, rsq[j]);
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are in memory
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old + 1u == (unsigned)a.splits;
+      if (last) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_sh = last;
+    }
+    __syncthreads();
+    if (!last_sh) return;
+    // sum every split's partial (this workgroup's own included, as stored) in split order, so the
+    // result does not depend on which workgroup arrives last; two splits' loads are in flight at once
+    for (int s = 0; s < a.splits; s += 2) {
+      const bool two = s + 1 < a.splits;
+      const unsigned char* p0 = a.slots + ((size_t)s * tiles + tile) * kSlotBytes;
+      const unsigned char* p1 = a.slots + ((size_t)(two ? s + 1 : s) * tiles + tile) * kSlotBytes;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kGemmNt; ++nt) {
+          const int off = (((wave * MT + mt) * kGemmNt + nt) * 64 + lane) * 16;
+          const float4_t v0 = slot_load4(p0, off), v1 = slot_load4(p1, off);
+          float4_t t = s == 0 ? v0 : acc[mt][nt] + v0;
+          if (two) t += v1;
+          acc[mt][nt] = t;
+        }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int nt = 0; nt < kGemmNt; ++nt) {
+          const int off = kSlotCs + ((wave * kGemmNt + nt) * 16 + (lane & 15)) * 4;
+          const float v0 = slot_load1(p0, off), v1 = slot_load1(p1, off);
+          float t = s == 0 ? v0 : csum[nt] + v0;
+          if (two) t += v1;
+          csum[nt] = t;
+        }
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+          const int off = kSlotStats + ((int)(threadIdx.x >> 4) + 16 * j) * 8;
+          const float s0 = slot_load1(p0, off), q0 = slot_load1(p0, off + 4);
+          const float s1 = slot_load1(p1, off), q1 = slot_load1(p1, off + 4);
+          float ts = s == 0 ? s0 : rsum[j] + s0, tq = s == 0 ? q0 : rsq[j] + q0;
+          if (two) {
+            ts += s1;
+            tq += q1;
+          }
+          rsum[j] = ts;
+          rsq[j] = tq;
+        }
+      }
+    }
+  }
+  if constexpr (NORM) {
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) {
+        const int row = (int)(threadIdx.x >> 4) + 16 * j;
+        float mu, inv;
+        norm_params(rsum[j], rsq[j], a.K, mu, inv);
+        row_mu[row] = mu;
+        row_inv[row] = inv;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds rows 4 (lane >> 4) + j of each row tile, column lane & 15 of each block.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int m = m0 + mt * 16 + 4 * (lane >> 4) + j;
+      const int ml = mt * 16 + 4 * (lane >> 4) + j;
+      const int m = m0 + ml;
       if (m >= a.M) continue;
       const float sx = MODE == 1 ? a.sxf[m] : 1.0f;
+      float mu = 0.0f, inv = 1.0f;
+      if constexpr (NORM) {
+        mu = row_mu[ml];
+        inv = row_inv[ml];
+      }
 #pragma unroll
       for (int nt = 0; nt < kGemmNt; ++nt) {
         const int n = (rb0 + nt) * 16 + (lane & 15);
         if (n >= a.N) continue;
         float v = acc[mt][nt][j];
         if constexpr (MODE == 1) v *= sx;
-        if (split)
-          a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = v;
-        else if (a.y16)
+        if constexpr (NORM) v = (v - mu * csum[nt]) * inv;
+        if (a.y16)
           a.y16[(size_t)m * a.ldy + n] = f2h(v);
         else
           a.y[(size_t)m * a.N + n] = v;
@@ -236,47 +458,67 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(const GemmArgs a)
   }
 }
 
-// out[m][n] = sum over splits s (in order) of part[s][m][n], as fp32 y or fp16 y16 (row stride ldy).
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int splits, int M,
-                                                          int N, float* __restrict__ y,
-                                                          uint16_t* __restrict__ y16, int ldy) {
-  const size_t total = (size_t)M * N;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    float v = part[i];
-    for (int s = 1; s < splits; ++s) v += part[(size_t)s * total + i];
-    const size_t m = i / (size_t)N, n = i - m * (size_t)N;
-    if (y16)
-      y16[m * (size_t)ldy + n] = f2h(v);
-    else
-      y[i] = v;
-  }
+__global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ cnt, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) cnt[i] = 0u;
 }
 
 // ------------------------------------------------------------------ host side
 
-// K splits for an M x N x K linear: enough workgroups for a 256-CU part, at least 2 groups per split.
-int gemm_splits(int M, int N, int K) {
-  const int tiles = (((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks) * ((M + kGemmRows - 1) / kGemmRows);
+// K splits for an M x N x K linear: enough workgroups for a 256-CU part, at least
+// kGemmMinGroupsPerSplit groups per split.
+static int gemm_tiles(int mode, int M, int N) {
+  const int rows = gemm_mt(mode, M, N) * 16;
+  return (((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks) * ((M + rows - 1) / rows);
+}
+
+int gemm_splits(int mode, int M, int N, int K) {
+  const int tiles = gemm_tiles(mode, M, N);
   const int G = K / kGroup;
   int s = 1;
-  while (s < kGemmMaxSplits && tiles * s < 256 && G / (2 * s) >= 2) s *= 2;
+  while (s < kGemmMaxSplits && tiles * s < 256 && G / (2 * s) >= kGemmMinGroupsPerSplit) s *= 2;
   return s;
 }
 
-size_t gemm_workspace(int M, int N, int K) {
-  const int s = gemm_splits(M, N, K);
-  return s > 1 ? align_up((size_t)s * M * N * 4, 256) : 0;
+size_t gemm_counter_bytes() { return (size_t)kGemmMaxCounters * 4; }
+
+size_t gemm_workspace(int mode, int M, int N, int K) {
+  const int s = gemm_splits(mode, M, N, K);
+  if (s <= 1) return 0;
+  return (size_t)s * gemm_tiles(mode, M, N) * kSlotBytes;
 }
 
-int launch_gemm(int mode, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf, const uint8_t* wp,
-                const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy, void* ws,
-                size_t ws_bytes, hipStream_t st) {
-  // split K only when the caller's scratch holds the partials (results then differ from the
-  // unsplit order by fp32 rounding only)
-  const size_t need = gemm_workspace(M, N, K);
-  const int splits = need > 0 && ws != nullptr && ws_bytes >= need ? gemm_splits(M, N, K) : 1;
+int launch_gemm_clear(unsigned* cnt, hipStream_t st) {
+  hipLaunchKernelGGL(gemm_clear_kernel, dim3(1), dim3(256), 0, st, cnt, kGemmMaxCounters);
+  return launch_status();
+}
+
+template <int MODE, bool NORM, int MT, int D>
+static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D>), grid, dim3(kGemmWaves * 64), 0, st, a);
+}
+
+// Weight ring depth per row tile: deeper where the accumulators leave room for it (two waves per
+// SIMD must fit).
+template <int MODE, bool NORM>
+static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st) {
+  if (mt == 1)
+    gemm_launch_one<MODE, NORM, 1, 6>(a, grid, st);
+  else if (mt == 2)
+    gemm_launch_one<MODE, NORM, 2, 6>(a, grid, st);
+  else
+    gemm_launch_one<MODE, NORM, 4, MODE == 0 ? 4 : 2>(a, grid, st);
+}
+
+int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
+                const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
+                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (mode == QS_W4A4 && norm) return QS_ERR_INVALID_ARG;
+  // split K only when the caller's scratch holds the partial slots and the (zeroed) counters;
+  // results then differ from the unsplit order by fp32 rounding only
+  const size_t need = gemm_workspace(mode, M, N, K);
+  const int splits = need > 0 && cnt != nullptr && ws != nullptr && ws_bytes >= need ? gemm_splits(mode, M, N, K) : 1;
   const int G = K / kGroup;
+  const int mt = gemm_mt(mode, M, N);
   GemmArgs a{};
   a.x = x;
   a.ldx = ldx;
@@ -288,23 +530,23 @@ int launch_gemm(int mode, const uint16_t* x, int ldx, const int8_t* xq, const fl
   a.N = N;
   a.K = K;
   a.gps = (G + splits - 1) / splits;
-  a.part = splits > 1 ? static_cast<float*>(ws) : nullptr;
+  a.splits = (G + a.gps - 1) / a.gps;
+  a.slots = a.splits > 1 ? static_cast<unsigned char*>(ws) : nullptr;
+  a.cnt = a.splits > 1 ? cnt : nullptr;
   a.y = y;
   a.y16 = y16;
   a.ldy = ldy;
   const int nrb = (N + 15) / 16;
-  const dim3 grid((M + kGemmRows - 1) / kGemmRows, (nrb + kGemmBlocks - 1) / kGemmBlocks, (G + a.gps - 1) / a.gps);
-  if (mode == QS_W4A16)
-    hipLaunchKernelGGL(gemm_kernel<0>, grid, dim3(kGemmWaves * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(kGemmWaves * 64), 0, st, a);
-  int rc = launch_status();
-  if (rc != QS_OK || grid.z == 1) return rc;
-  const size_t total = (size_t)M * N;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.part, (int)grid.z, M, N, y,
-                     y16, ldy);
+  const dim3 grid((M + mt * 16 - 1) / (mt * 16), (nrb + kGemmBlocks - 1) / kGemmBlocks, a.splits);
+  if (a.splits > 1 && (int)(grid.x * grid.y) > kGemmMaxCounters) return QS_ERR_UNSUPPORTED;
+  if (mode == QS_W4A16) {
+    if (norm)
+      gemm_launch_mt<0, true>(a, mt, grid, st);
+    else
+      gemm_launch_mt<0, false>(a, mt, grid, st);
+  } else {
+    gemm_launch_mt<1, false>(a, mt, grid, st);
+  }
   return launch_status();
 }
 

@@ -482,14 +482,25 @@ static bool use_gemm(int M, const int32_t* acc_out) { return M >= kGemmMinRows &
 // staged in memory, then the K-split partials of the batched kernel.  Sized for the case without
 // the per-group accumulator output (it only ever makes the need smaller).
 static size_t staging_bytes(int mode, int M, int K, bool norm_in) {
-  if (mode == QS_W4A16) return (norm_in && !w4a16_lds(M, K)) ? align_up((size_t)M * K * 2, 256) : 0;
+  if (mode == QS_W4A16)  // the batched kernel standardises inside the GEMM
+    return (norm_in && !w4a16_lds(M, K) && !use_gemm(M, nullptr)) ? align_up((size_t)M * K * 2, 256) : 0;
   if (w4a4_fused(M, K)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
 }
 
+// Layout of a linear's workspace: [K-split arrival counters (batched kernel)] [staging] [K-split
+// partial slots].  The counters come first so that every linear of a chain finds them at the same
+// place: they are cleared once per chain call and every batched launch leaves them at zero.
+static size_t counter_bytes(int M) { return use_gemm(M, nullptr) ? gemm_counter_bytes() : 0; }
+
 size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
   const size_t stage = staging_bytes(mode, M, K, norm_in);
-  return stage + (use_gemm(M, nullptr) ? gemm_workspace(M, N, K) : 0);
+  return counter_bytes(M) + stage + (use_gemm(M, nullptr) ? gemm_workspace(mode, M, N, K) : 0);
+}
+
+int linear_clear_counters(int M, void* ws, hipStream_t st) {
+  if (counter_bytes(M) == 0) return QS_OK;
+  return launch_gemm_clear(static_cast<unsigned*>(ws), st);
 }
 
 template <int MODE, int MT, int S, bool XLDS>
@@ -605,15 +616,28 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   a.norm_in = io.norm_in;
   // the staging part is required; the batched kernel's split partials are optional (without them it
   // does not split K)
+  const size_t pre = counter_bytes(M);
   const size_t need = staging_bytes(mode, M, K, io.norm_in != 0);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return QS_ERR_WORKSPACE;
+  if (need > 0 && (ws == nullptr || ws_bytes < pre + need)) return QS_ERR_WORKSPACE;
   const bool gemm = use_gemm(M, acc_out);
-  void* gws = ws ? static_cast<unsigned char*>(ws) + need : nullptr;
-  const size_t gws_bytes = ws && ws_bytes > need ? ws_bytes - need : 0;
+  unsigned char* stg = ws ? static_cast<unsigned char*>(ws) + pre : nullptr;
+  unsigned* cnt = pre > 0 && ws != nullptr && ws_bytes >= pre ? static_cast<unsigned*>(ws) : nullptr;
+  if (cnt && !io.counters_zero) {
+    // counters of a workspace not known to be clear; only needed if the GEMM splits K
+    if (gemm && gemm_workspace(mode, M, N, K) > 0 && ws_bytes >= pre + need + gemm_workspace(mode, M, N, K)) {
+      const int rc = launch_gemm_clear(cnt, st);
+      if (rc != QS_OK) return rc;
+    }
+  }
+  void* gws = ws ? stg + need : nullptr;
+  const size_t gws_bytes = ws && ws_bytes > pre + need ? ws_bytes - pre - need : 0;
   if (mode == QS_W4A16) {
     if (w4a16_lds(M, K)) return launch_split<MODE_W4A16, 1, true>(a, (size_t)M * K * 2, st);
+    if (gemm)
+      return launch_gemm(QS_W4A16, io.norm_in != 0, a.x, a.ldx, nullptr, nullptr, wp, sp, M, N, K, a.y, a.y16,
+                         a.y16 ? a.ldy : N, cnt, gws, gws_bytes, st);
     if (io.norm_in) {
-      uint16_t* xn = static_cast<uint16_t*>(ws);
+      uint16_t* xn = reinterpret_cast<uint16_t*>(stg);
       hipLaunchKernelGGL(row_norm_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, xn);
       const int rc = launch_status();
       if (rc != QS_OK) return rc;
@@ -621,21 +645,18 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
       a.ldx = K;
       a.norm_in = 0;
     }
-    if (gemm)
-      return launch_gemm(QS_W4A16, a.x, a.ldx, nullptr, nullptr, wp, sp, M, N, K, a.y, a.y16,
-                         a.y16 ? a.ldy : N, gws, gws_bytes, st);
     return launch_chunked<MODE_W4A16>(a, st);
   }
   if (w4a4_fused(M, K)) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
-  int8_t* xq_op = static_cast<int8_t*>(ws);
-  float* sxf = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + align_up((size_t)M * K, 256));
+  int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
+  float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
   hipLaunchKernelGGL(act_quant_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
                      xq_out, sx_out);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
   if (gemm)
-    return launch_gemm(QS_W4A4, nullptr, 0, xq_op, sxf, wp, sp, M, N, K, a.y, a.y16, a.y16 ? a.ldy : N, gws,
-                       gws_bytes, st);
+    return launch_gemm(QS_W4A4, false, nullptr, 0, xq_op, sxf, wp, sp, M, N, K, a.y, a.y16, a.y16 ? a.ldy : N,
+                       cnt, gws, gws_bytes, st);
   a.xq = xq_op;
   a.sxf = sxf;
   a.xq_out = nullptr;

@@ -37,17 +37,26 @@ struct LinearIO {
   uint16_t* y16;
   int ldy;
   int norm_in;  // standardise each input row over its K columns first
+  int counters_zero;  // the workspace's K-split counters are known to be zero (chain calls)
 };
 int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint16_t* sp, int M, int N,
                      int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
                      size_t ws_bytes, hipStream_t st);
 
-// Batched linear (gemm.hip), M >= 16 rows: x fp16 [M][ldx] (W4A16) or operand-ordered codes
-// xq [M][K] with fp32 row scales sxf (W4A4); output fp32 y [M][N] or fp16 y16 (row stride ldy).
-size_t gemm_workspace(int M, int N, int K);
-int launch_gemm(int mode, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf, const uint8_t* wp,
-                const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy, void* ws,
-                size_t ws_bytes, hipStream_t st);
+// Clears the K-split counters at the start of a linear's workspace (before the first linear of a
+// chain call); a no-op for row counts that never use the batched kernel.
+int linear_clear_counters(int M, void* ws, hipStream_t st);
+
+// Batched linear (gemm.hip), M >= 16 rows: x fp16 [M][ldx] (W4A16, standardised per row inside
+// the kernel when norm) or operand-ordered codes xq [M][K] with fp32 row scales sxf (W4A4); output
+// fp32 y [M][N] or fp16 y16 (row stride ldy).  K is split over workgroups when cnt (zeroed arrival
+// counters, left zero) and ws (partial slots of gemm_workspace bytes) are given.
+size_t gemm_counter_bytes();
+size_t gemm_workspace(int mode, int M, int N, int K);
+int launch_gemm_clear(unsigned* cnt, hipStream_t st);
+int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
+                const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
+                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st);
 
 // Persistent pass kernel (pass.hip): one resident workgroup per CU runs up to kMaxPassStages
 // linears of a chain per launch.

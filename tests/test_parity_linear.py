@@ -207,11 +207,13 @@ def test_chain_exact_balanced_case(qs, mode):
     assert np.array_equal(y.astype(np.float64), O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers))
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20), (0, 20), (0, 70), (1, 70)])
 def test_chain_small_llama_like(qs, mode, m):
     """Two layers of q|k|v, o, gate|up, down at hidden 512 plus a 3000-way head;
-    o reads the q columns, down reads the gate columns; M = 12 and 20 take the
-    large-M paths (separate standardisation / quantization kernels)."""
+    o reads the q columns, down reads the gate columns; M = 12 takes the
+    streaming kernel after a standardisation kernel, M = 20 and 70 the batched
+    kernel (K split over workgroups; W4A16 standardises inside it, W4A4 after a
+    quantization kernel)."""
     print(f"chain mode={mode} m={m}", flush=True)
     rng = W.rng_for(800 + m)
     h, inter = 512, 1024
@@ -223,7 +225,7 @@ def test_chain_small_llama_like(qs, mode, m):
     assert_linear_close(y, ref, f"chain mode={mode} m={m}")
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     """69 linears.  At M <= 4 (W4A16) / M = 1 (W4A4) the persistent pass splits
     them over two launches, so the hand-over at the seam (fp16 activations in
