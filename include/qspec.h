@@ -90,8 +90,11 @@ int qs_linear_w4a16(const uint16_t* x, const uint8_t* w_packed,
                     void* stream);
 
 /*
- * Workspace bytes needed by qs_linear_w4a4 / qs_lmhead for these shapes (0 when
- * the activation quantization is fused into the GEMM, i.e. for small M).
+ * Workspace bytes needed by qs_linear_w4a4 / qs_lmhead for these shapes: the
+ * quantized activations and, for the batched kernel (W4A16 from 5 rows, W4A4
+ * from 2), its K-split counters and partials.  0 when nothing is staged (one
+ * W4A4 row, or W4A16 up to 4 rows).  A workspace given for a batched call is
+ * cleared of stale counters by the call itself.
  */
 size_t qs_linear_workspace_bytes(int mode, int M, int N, int K);
 

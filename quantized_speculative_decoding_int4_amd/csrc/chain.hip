@@ -111,7 +111,7 @@ int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* c
   const uint16_t* in = x;
   int ldx = chain[0].K;
   // every linear's workspace starts at qws, so its K-split counters are shared: clear them once
-  const int rc0 = linear_clear_counters(M, qws, st);
+  const int rc0 = linear_clear_counters(mode, M, qws, st);
   if (rc0 != QS_OK) return rc0;
   for (int i = 0; i < n; ++i) {
     LinearIO io{};

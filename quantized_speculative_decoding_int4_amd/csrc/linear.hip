@@ -474,32 +474,37 @@ static bool w4a4_fused(int M, int K) { return M <= kFusedMaxM && (size_t)M * K <
 static bool w4a16_lds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= kMaxLdsStage; }
 
 // From this many rows on (and without the per-group accumulator output) a linear runs as the
-// register-tiled batched kernel of gemm.hip instead of the streaming kernel.
-constexpr int kGemmMinRows = 16;
-static bool use_gemm(int M, const int32_t* acc_out) { return M >= kGemmMinRows && acc_out == nullptr; }
+// register-tiled batched kernel of gemm.hip instead of the streaming kernel: above the rows the
+// LDS-staged streaming kernel takes (W4A16, up to 4) or the single-row fused one (W4A4).  Measured
+// on the Llama-3-8B-shaped stack, the batched kernel's 16-row tile is faster from these row counts
+// on (M = 6 and 8: 2.3 instead of 2.7-2.9 ms per W4A16 pass; W4A4 M = 4: 2.8 instead of 2.8-4.2).
+static int gemm_min_rows(int mode) { return mode == QS_W4A16 ? 5 : 2; }
+static bool use_gemm(int mode, int M, const int32_t* acc_out) {
+  return M >= gemm_min_rows(mode) && acc_out == nullptr;
+}
 
 // Scratch of one linear: the standardised (W4A16) or quantized (W4A4) activations when they are
 // staged in memory, then the K-split partials of the batched kernel.  Sized for the case without
 // the per-group accumulator output (it only ever makes the need smaller).
 static size_t staging_bytes(int mode, int M, int K, bool norm_in) {
   if (mode == QS_W4A16)  // the batched kernel standardises inside the GEMM
-    return (norm_in && !w4a16_lds(M, K) && !use_gemm(M, nullptr)) ? align_up((size_t)M * K * 2, 256) : 0;
-  if (w4a4_fused(M, K)) return 0;
+    return (norm_in && !w4a16_lds(M, K) && !use_gemm(mode, M, nullptr)) ? align_up((size_t)M * K * 2, 256) : 0;
+  if (w4a4_fused(M, K) && !use_gemm(mode, M, nullptr)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
 }
 
 // Layout of a linear's workspace: [K-split arrival counters (batched kernel)] [staging] [K-split
 // partial slots].  The counters come first so that every linear of a chain finds them at the same
 // place: they are cleared once per chain call and every batched launch leaves them at zero.
-static size_t counter_bytes(int M) { return use_gemm(M, nullptr) ? gemm_counter_bytes() : 0; }
+static size_t counter_bytes(int mode, int M) { return use_gemm(mode, M, nullptr) ? gemm_counter_bytes() : 0; }
 
 size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
   const size_t stage = staging_bytes(mode, M, K, norm_in);
-  return counter_bytes(M) + stage + (use_gemm(M, nullptr) ? gemm_workspace(mode, M, N, K) : 0);
+  return counter_bytes(mode, M) + stage + (use_gemm(mode, M, nullptr) ? gemm_workspace(mode, M, N, K) : 0);
 }
 
-int linear_clear_counters(int M, void* ws, hipStream_t st) {
-  if (counter_bytes(M) == 0) return QS_OK;
+int linear_clear_counters(int mode, int M, void* ws, hipStream_t st) {
+  if (counter_bytes(mode, M) == 0) return QS_OK;
   return launch_gemm_clear(static_cast<unsigned*>(ws), st);
 }
 
@@ -616,10 +621,10 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   a.norm_in = io.norm_in;
   // the staging part is required; the batched kernel's split partials are optional (without them it
   // does not split K)
-  const size_t pre = counter_bytes(M);
+  const size_t pre = counter_bytes(mode, M);
   const size_t need = staging_bytes(mode, M, K, io.norm_in != 0);
   if (need > 0 && (ws == nullptr || ws_bytes < pre + need)) return QS_ERR_WORKSPACE;
-  const bool gemm = use_gemm(M, acc_out);
+  const bool gemm = use_gemm(mode, M, acc_out);
   unsigned char* stg = ws ? static_cast<unsigned char*>(ws) + pre : nullptr;
   unsigned* cnt = pre > 0 && ws != nullptr && ws_bytes >= pre ? static_cast<unsigned*>(ws) : nullptr;
   if (cnt && !io.counters_zero) {
@@ -647,7 +652,7 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
     }
     return launch_chunked<MODE_W4A16>(a, st);
   }
-  if (w4a4_fused(M, K)) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
+  if (w4a4_fused(M, K) && !gemm) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
   int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
   float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
   hipLaunchKernelGGL(act_quant_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,

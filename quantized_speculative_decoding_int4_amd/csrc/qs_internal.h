@@ -45,7 +45,7 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
 
 // Clears the K-split counters at the start of a linear's workspace (before the first linear of a
 // chain call); a no-op for row counts that never use the batched kernel.
-int linear_clear_counters(int M, void* ws, hipStream_t st);
+int linear_clear_counters(int mode, int M, void* ws, hipStream_t st);
 
 // Batched linear (gemm.hip), M >= 16 rows: x fp16 [M][ldx] (W4A16, standardised per row inside
 // the kernel when norm) or operand-ordered codes xq [M][K] with fp32 row scales sxf (W4A4); output
