@@ -336,6 +336,47 @@ def main():
         batched["M128_w4a16"]["pass_ms"], 100 * batched["M128_w4a16"]["mfma_util"],
         batched["M128_w4a4"]["pass_ms"], 100 * batched["M128_w4a4"]["mfma_util"]))
 
+    # ---------------- speculative timing model and draft-length choice (host-side planner)
+    # t_target: one plain decoding step = W4A16 pass at M = 1 (graph-replayed); t_draft: one draft
+    # pass + draft Top-1 of the iteration above; t_verify: its verify pass; t_overhead: its accept
+    # phase.  alpha = 0.96 (the pages' W4A4/W4A16 Top-1 agreement, rounded).
+    from quantized_speculative_decoding_int4_amd import planner as PL
+    ALPHA = 0.96
+    x1 = x_verify[:1].contiguous()
+    o1 = torch.empty((1, V), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(chain.workspace_bytes(qs.QS_W4A16, 1), dtype=torch.uint8, device=dev)
+    qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
+    target_ms = time_calls(g1.replay, reps=10)
+    del g1, ws1
+    t_draft1 = draft_ms / GAMMA
+    spec = {
+        "alpha": ALPHA, "gamma": GAMMA,
+        "expected_tokens": PL.expected_tokens(ALPHA, GAMMA),
+        "t_target_ms": target_ms, "t_draft_ms": t_draft1, "t_verify_ms": verify_ms, "t_overhead_ms": accept_ms,
+        "modelled_speedup": PL.modelled_speedup(ALPHA, GAMMA, target_ms, t_draft1, verify_ms, accept_ms),
+        "itl_ms": PL.inter_token_latency(ALPHA, GAMMA, ms_step),
+        "target_itl_ms": target_ms,
+    }
+    # per batch: draft step = W4A4 pass at M = B (B = 1: the draft pass above), verify = W4A16 pass at
+    # M = B (gamma + 1), both from the sweep; accept / Top-1 costs (tens of us) left out
+    pts = {(p_["mode"], p_["M"]): p_["pass_ms"] for p_ in batched["points"]}
+    choice = {}
+    for B in (1, 4, 16):
+        td = t_draft1 if B == 1 else pts.get(("w4a4", B))
+        tv = {G: pts[("w4a16", B * (G + 1))] for G in (3, 5, 7) if ("w4a16", B * (G + 1)) in pts}
+        if td is None or not tv:
+            continue
+        c = PL.choose_gamma(ALPHA, B, td, tv)
+        choice[f"B{B}"] = {"best_gamma": c["best_gamma"], "t_draft_ms": td,
+                           "tokens_per_s": {str(G): 1e3 * r["tokens_per_time"] for G, r in c["table"].items()}}
+    spec["gamma_choice"] = choice
+    log("speculative model: E[T] %.3f, t_target %.3f ms, speed-up %.3f, ITL %.3f ms (target alone %.3f); "
+        "best gamma by batch %s" % (spec["expected_tokens"], target_ms, spec["modelled_speedup"], spec["itl_ms"],
+                                    target_ms, {k: v["best_gamma"] for k, v in choice.items()}))
+
     # ---------------- rooflines of the pass kernels (HIP events on the launch stream)
     # Algorithmic bytes of one pass: packed weights (0.515625 B per weight) plus, per linear,
     # x = 2*M*K and y = 4*M*N bytes.  A pass runs as `launches` persistent launches, each
@@ -404,6 +445,7 @@ def main():
         "draft_verify_top1_agreement": agree,
         "accept_positions_per_s": accept,
         "batched_verify": batched,
+        "speculative_model": spec,
         "roofline": roof_draft,
         "roofline_verify": roof_verify,
         "cpu_baseline": cpu,
