@@ -18,6 +18,8 @@ reordering beyond what each definition states.
 Sources (pages; each function names the section it follows):
   [P1] qiita.com, "QSpec実行時の2つの量子化による推論の一致率を調べる"
        (measuring Top-1 agreement of QSpec's two quantized modes)
+  [P2] aibr.jp, summary of a paper on combining speculative decoding with
+       low-bit quantization
   [P3] kasblo.com, "Speculative Decodingとは？LLM生成を速くする方法"
        (tutorial on speculative decoding)
 Where the pages leave a detail open (grouping, rounding, tie rules), the
@@ -138,23 +140,64 @@ def linear_w4a4(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
     return {"xq": xq, "sx": sx, "acc": acc, "y": y}
 
 
+# --------------------------------------------------------------------------
+# W4A8: the same INT4 weights with 8-bit activations.  [P2] aibr.jp summary of
+# a paper on combining speculative decoding with quantization, section
+# "3.中核となる技術的要素": W4A16 and W4A8 are the weight/activation bit widths
+# whose memory-traffic/compute balance the work evaluates.  The page gives no
+# quantizer; the reading mirrors the W4A4 one with the int8 range.
+# --------------------------------------------------------------------------
+
+def quantize_activations_int8(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token symmetric INT8 activation quantization (reading, per token m):
+      s_m = fp16( fp32(max_k |x[m, k]|) / 127 )     (fp32 quotient, then RNE to fp16)
+      xq  = clamp(rint(x / s_m), -128, 127)         (round half to even of the exact quotient)
+      s_m == 0  ->  xq = 0
+    The float64 quotient of two fp16 values rounds to the same integer as the
+    exact quotient (same argument as for the 4-bit quantizer: a non-tie lies
+    at least 2**-12 from any j + 1/2 here).  Returns xq int8 [M, K], s fp16 [M].
+    """
+    assert x.dtype == np.float16 and x.ndim == 2
+    amax = np.abs(x.astype(np.float32)).max(axis=1)
+    s16 = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float16)
+    s64 = s16.astype(np.float64)
+    xq = np.zeros(x.shape, dtype=np.int8)
+    nz = s64 > 0
+    if nz.any():
+        quot = x[nz].astype(np.float64) / s64[nz, None]
+        xq[nz] = np.clip(np.rint(quot), -128, 127).astype(np.int8)
+    return xq, s16
+
+
+def linear_w4a8(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
+    """W4A8 mode: 8-bit per-token activations, exact integer group sums, rescale
+      y[m, n] = s_m * sum_g s[n, g] * acc[m, n, g]     (float64)
+    Returns dict(xq, sx, acc, y)."""
+    _check_weights(q, s)
+    xq, sx = quantize_activations_int8(x)
+    acc = group_accumulators(xq, q)
+    per_group = acc.astype(np.float64) * s.astype(np.float64)[None, :, :]
+    y = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
+    return {"xq": xq, "sx": sx, "acc": acc, "y": y}
+
+
 def lm_head(mode: str, x: np.ndarray, q: np.ndarray, s: np.ndarray,
             chunk: int = 8192) -> np.ndarray:
-    """LM-head logits: the same linear (mode 'w4a16' or 'w4a4') with N = vocab.
+    """LM-head logits: the same linear (mode 'w4a16', 'w4a4' or 'w4a8') with N = vocab.
 
     Processed in chunks of output rows only to bound memory; each chunk is the
     same definition as the full linear.  Returns float64 [M, V].
     """
     n = q.shape[0]
     out = np.empty((x.shape[0], n), dtype=np.float64)
-    if mode == "w4a4":
+    if mode in ("w4a4", "w4a8"):
         # one activation quantization for the whole row, shared by all chunks
-        xq, sx = quantize_activations(x)
+        xq, sx = quantize_activations(x) if mode == "w4a4" else quantize_activations_int8(x)
     for lo in range(0, n, chunk):
         hi = min(n, lo + chunk)
         if mode == "w4a16":
             out[:, lo:hi] = linear_w4a16(x, q[lo:hi], s[lo:hi])
-        elif mode == "w4a4":
+        elif mode in ("w4a4", "w4a8"):
             acc = group_accumulators(xq, q[lo:hi])
             per_group = acc.astype(np.float64) * s[lo:hi].astype(np.float64)[None]
             out[:, lo:hi] = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
@@ -204,6 +247,8 @@ def chain_forward(mode: str, x: np.ndarray, layers) -> np.ndarray:
             y = linear_w4a16(xin, q, s)
         elif mode == "w4a4":
             y = linear_w4a4(xin, q, s)["y"]
+        elif mode == "w4a8":
+            y = linear_w4a8(xin, q, s)["y"]
         else:
             raise ValueError(mode)
         if i + 1 < n_layers:

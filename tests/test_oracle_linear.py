@@ -223,3 +223,77 @@ def test_chain_single_stage_is_the_linear():
     x, _ = W.activations(rng, 3, 256)
     assert np.array_equal(O.chain_forward("w4a16", x, [(q, s)]), O.linear_w4a16(x, q, s))
     assert np.array_equal(O.chain_forward("w4a4", x, [(q, s)]), O.linear_w4a4(x, q, s)["y"])
+
+
+# ---------------------------------------------------------------- W4A8 (8-bit activations)
+
+@pytest.mark.parametrize("amax", [127.0, 1.0, 3.3, 0.0625, 1000.0, 20.5])
+def test_act_quant_int8_brute_force_all_fp16(amax):
+    """Every finite fp16 value v with |v| <= amax, quantized in a row whose
+    maximum is amax, against exact rational round-half-even and the int8 clamp."""
+    a16 = np.float16(amax)
+    vals = _all_finite_fp16()
+    vals = vals[np.abs(vals.astype(np.float64)) <= float(a16)]
+    x = np.stack([np.full(vals.shape, a16), vals], axis=1).astype(np.float16)
+    xq, sx = O.quantize_activations_int8(x)
+    s = sx[0]
+    assert np.all(sx == s)
+    s_fr = Fraction(float(s))
+    ref = np.array([max(-128, min(127, _round_half_even(Fraction(float(v)) / s_fr))) for v in vals])
+    assert np.array_equal(xq[:, 1].astype(np.int64), ref)
+    ties = [v for v in vals if (Fraction(float(v)) / s_fr).denominator == 2]
+    if amax in (127.0, 1.0, 20.5):
+        assert len(ties) > 0
+
+
+def test_act_quant_int8_scale_values():
+    # s = fp16(fp32(amax) / 127): exact cases, a zero row, and 1/127 rounded twice
+    x = np.array([[127.0, -1.0], [-63.5, 0.25], [0.0, 0.0], [254.0, 3.0]], dtype=np.float16)
+    xq, sx = O.quantize_activations_int8(x)
+    assert sx.tolist() == [1.0, 0.5, 0.0, 2.0]
+    assert xq.tolist() == [[127, -1], [-127, 0], [0, 0], [127, 2]]  # 3 / 2 = 1.5 -> 2 (half to even)
+    _, s1 = O.quantize_activations_int8(np.array([[1.0]], dtype=np.float16))
+    f32 = np.float32(1.0) / np.float32(127.0)
+    assert s1[0] == np.float16(f32) and abs(float(s1[0]) - 1.0 / 127.0) <= 2.0 ** -17
+
+
+def test_act_quant_int8_multiples_of_scale_and_invariants():
+    s = np.float16(0.125)
+    row = np.array([127 * s] + [j * s for j in range(-127, 128)], dtype=np.float16)
+    xq, sx = O.quantize_activations_int8(row[None, :])
+    assert sx[0] == s and xq[0, 1:].tolist() == list(range(-127, 128))
+    rng = W.rng_for(18)
+    x, _ = W.activations(rng, 32, 1024)
+    xq, sx = O.quantize_activations_int8(x)
+    s64 = sx.astype(np.float64)[:, None]
+    assert np.all(np.abs(xq).max(axis=1) >= 126)
+    assert np.all(np.abs(x.astype(np.float64) - xq * s64) <= s64 / 2 + 1e-300)
+
+
+def test_w4a8_accumulators_and_output_brute_force():
+    rng = W.rng_for(19)
+    q, s = W.int4_weights(rng, 3, 256)
+    x, _ = W.activations(rng, 2, 256, n_outliers=1)
+    r = O.linear_w4a8(x, q, s)
+    xq = r["xq"]
+    for m in range(2):
+        for n in range(3):
+            tot = Fraction(0)
+            for g in range(2):
+                ref = sum(int(xq[m, k]) * int(q[n, k]) for k in range(128 * g, 128 * g + 128))
+                assert r["acc"][m, n, g] == ref
+                tot += Fraction(float(s[n, g])) * ref
+            tot *= Fraction(float(r["sx"][m]))
+            assert abs(r["y"][m, n] - float(tot)) <= 1e-12 * max(1.0, abs(float(tot)))
+    assert np.abs(r["acc"]).max() <= 128 * 128 * 8
+
+
+def test_w4a8_is_closer_to_w4a16_than_w4a4():
+    # 8-bit activations: quantization error ~ s/2 with s = max|x| / 127 instead of / 7
+    rng = W.rng_for(20)
+    q, s = W.int4_weights(rng, 64, 1024)
+    x, _ = W.activations(rng, 4, 1024)
+    ref = O.linear_w4a16(x, q, s)
+    e8 = np.linalg.norm(O.linear_w4a8(x, q, s)["y"] - ref)
+    e4 = np.linalg.norm(O.linear_w4a4(x, q, s)["y"] - ref)
+    assert e8 < e4 / 8
