@@ -292,18 +292,19 @@ def main():
         del tg, dr, wsg
 
     # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
-    # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in both modes; each point is one
+    # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
+    # INT4 weights with 8-bit activations on the int8 MFMA); each point is one
     # graph-replayed pass, timed with HIP events.  MFMA utilisation = 2 M (weights) flop / time
     # against the dense peak of the mode's MFMA (fp16 2.5166 PFLOP/s, int8 5.0332 POP/s).
     n_weights = sum(n * k for (_, n, k) in shapes)
-    peaks = {qs.QS_W4A16: 2.5166e15, qs.QS_W4A4: 5.0332e15}
+    peaks = {qs.QS_W4A16: 2.5166e15, qs.QS_W4A4: 5.0332e15, qs.QS_W4A8: 5.0332e15}
     batched = {"points": []}
     rng_b = W.rng_for(21)
     for (B, G) in ((1, 3), (1, 5), (1, 7), (4, 3), (4, 5), (4, 7), (16, 3), (16, 5), (16, 7)):
         m = B * (G + 1)
         xb = torch.from_numpy(W.activations(rng_b, m, W.HIDDEN)[0]).to(dev)
         ob = torch.empty((m, V), dtype=torch.float32, device=dev)
-        for mode, mname in ((qs.QS_W4A16, "w4a16"), (qs.QS_W4A4, "w4a4")):
+        for mode, mname in ((qs.QS_W4A16, "w4a16"), (qs.QS_W4A4, "w4a4"), (qs.QS_W4A8, "w4a8")):
             wsb = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
             qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
             g = torch.cuda.CUDAGraph()

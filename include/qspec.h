@@ -55,7 +55,7 @@ extern "C" {
 #define QS_MAX_M 256   /* most activation rows per linear call */
 #define QS_MAX_VERIFY_SEQS 16384 /* sequences per verify launch block */
 
-typedef enum { QS_W4A16 = 0, QS_W4A4 = 1 } qs_mode;
+typedef enum { QS_W4A16 = 0, QS_W4A4 = 1, QS_W4A8 = 2 } qs_mode;
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* qs_status_string(int status);
@@ -120,10 +120,26 @@ int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
- * qs_lmhead -- the LM-head projection hidden -> vocabulary logits in either
+ * qs_linear_w4a8 -- the shared INT4 weights with 8-bit activations ([P2]
+ * "3.中核となる技術的要素" names W4A8 beside W4A16 as a studied bit-width
+ * configuration; the quantizer is this library's reading, the 4-bit one with
+ * the int8 range):
+ *     s_m = fp16(fp32(max_k |x[m][k]|) / 127),  xq = clamp(rint(x / s_m), -128, 127)
+ * then the same int8-MFMA group sums and fp32 epilogue as qs_linear_w4a4
+ * (|acc| <= 128 * 128 * 8).  Arguments, layouts, ownership and errors as for
+ * qs_linear_w4a4; ws of qs_linear_workspace_bytes(QS_W4A8, M, N, K) bytes
+ * (never 0: the codes are always staged).
+ */
+int qs_linear_w4a8(const uint16_t* x, const uint8_t* w_packed,
+                   const uint16_t* s_packed, float* y, int M, int N, int K,
+                   int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_lmhead -- the LM-head projection hidden -> vocabulary logits in any
  * mode (the pages' per-position next-token distributions, [P1] "結果", come from
  * it).  Same arithmetic as the linear of that mode with N = V.
- *   mode     QS_W4A16 or QS_W4A4
+ *   mode     QS_W4A16, QS_W4A4 or QS_W4A8
  *   x        fp16 [M][K];  logits fp32 [M][V] (out)
  *   ws       qs_linear_workspace_bytes(mode, M, V, K) bytes (NULL if 0)
  */

@@ -95,33 +95,48 @@ int qs_linear_w4a16(const uint16_t* x, const uint8_t* w_packed, const uint16_t* 
 }
 
 size_t qs_linear_workspace_bytes(int mode, int M, int N, int K) {
-  if ((mode != QS_W4A16 && mode != QS_W4A4) || !linear_shape_ok(M, N, K) || M > QS_MAX_M) return 0;
+  if ((mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) || !linear_shape_ok(M, N, K) || M > QS_MAX_M)
+    return 0;
   return linear_workspace(mode, M, N, K, false);
 }
 
-int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed, float* y, int M,
-                   int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
-                   size_t ws_bytes, void* stream) {
+static int linear_int_mode(int mode, const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed,
+                           float* y, int M, int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out,
+                           void* ws, size_t ws_bytes, void* stream) {
   if (!x || !w_packed || !s_packed || !y) return QS_ERR_INVALID_ARG;
   if (!linear_shape_ok(M, N, K)) return QS_ERR_INVALID_ARG;
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w_packed)) return QS_ERR_MISALIGNED;
   if (xq_out && ((reinterpret_cast<uintptr_t>(xq_out) & 7u) != 0)) return QS_ERR_MISALIGNED;
-  const size_t need = linear_workspace(QS_W4A4, M, N, K, false);
+  const size_t need = linear_workspace(mode, M, N, K, false);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QS_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return QS_ERR_MISALIGNED;
   if (!device_info()->ok) return QS_ERR_DEVICE;
-  return launch_linear(QS_W4A4, x, w_packed, s_packed, y, M, N, K, xq_out, sx_out, acc_out, ws, ws_bytes,
+  return launch_linear(mode, x, w_packed, s_packed, y, M, N, K, xq_out, sx_out, acc_out, ws, ws_bytes,
                        static_cast<hipStream_t>(stream));
+}
+
+int qs_linear_w4a4(const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed, float* y, int M,
+                   int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return linear_int_mode(QS_W4A4, x, w_packed, s_packed, y, M, N, K, xq_out, sx_out, acc_out, ws, ws_bytes,
+                         stream);
+}
+
+int qs_linear_w4a8(const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed, float* y, int M,
+                   int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return linear_int_mode(QS_W4A8, x, w_packed, s_packed, y, M, N, K, xq_out, sx_out, acc_out, ws, ws_bytes,
+                         stream);
 }
 
 int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed,
               float* logits, int M, int V, int K, void* ws, size_t ws_bytes, void* stream) {
-  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
   if (mode == QS_W4A16)
     return qs_linear_w4a16(x, w_packed, s_packed, logits, M, V, K, stream);
-  return qs_linear_w4a4(x, w_packed, s_packed, logits, M, V, K, nullptr, nullptr, nullptr, ws, ws_bytes,
-                        stream);
+  return linear_int_mode(mode, x, w_packed, s_packed, logits, M, V, K, nullptr, nullptr, nullptr, ws, ws_bytes,
+                         stream);
 }
 
 size_t qs_verify_workspace_bytes(int B, int gamma, int V) {

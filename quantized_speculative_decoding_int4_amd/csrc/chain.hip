@@ -50,12 +50,12 @@ using namespace qs;
 extern "C" {
 
 size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, int n) {
-  if ((mode != QS_W4A16 && mode != QS_W4A4) || M < 1 || M > QS_MAX_M || !chain_ok(chain, n)) return 0;
+  if ((mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) || M < 1 || M > QS_MAX_M || !chain_ok(chain, n)) return 0;
   return chain_workspace(mode, M, chain, n);
 }
 
 int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n) {
-  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
   if (!chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!device_info()->ok) return QS_ERR_DEVICE;
@@ -70,7 +70,7 @@ int qs_set_barrier_timeout_us(int us) {
 
 int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, void* ws, size_t ws_bytes,
                          int* timed_out, void* stream) {
-  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
   if (!timed_out || !chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < chain_workspace(mode, M, chain, n)) return QS_ERR_WORKSPACE;
@@ -89,7 +89,7 @@ int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, vo
 
 int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
                      void* ws, size_t ws_bytes, void* stream) {
-  if (mode != QS_W4A16 && mode != QS_W4A4) return QS_ERR_INVALID_ARG;
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
   if (!x || !out || !chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!aligned16(x)) return QS_ERR_MISALIGNED;

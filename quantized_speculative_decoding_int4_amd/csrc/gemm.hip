@@ -512,7 +512,7 @@ static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st)
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
                 const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
                 unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st) {
-  if (mode == QS_W4A4 && norm) return QS_ERR_INVALID_ARG;
+  if (mode != QS_W4A16 && norm) return QS_ERR_INVALID_ARG;
   // split K only when the caller's scratch holds the partial slots and the (zeroed) counters;
   // results then differ from the unsplit order by fp32 rounding only
   const size_t need = gemm_workspace(mode, M, N, K);

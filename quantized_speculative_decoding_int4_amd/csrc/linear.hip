@@ -100,8 +100,10 @@ __global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restric
   for (int i = threadIdx.x; i < nb; i += 256) o[i] = norm_block8(xr[i], mu_sh, inv_sh);
 }
 
-// Stand-alone quantizer for large M: one workgroup per row.  Writes operand-ordered codes and the
+// Stand-alone quantizer (INT4 codes for W4A4, QMAX = 7; INT8 codes for W4A8, QMAX = 127): one
+// workgroup per row.  Writes operand-ordered codes and the
 // fp32 value of the fp16 scale to the workspace, and optionally the logical codes / fp16 scales.
+template <int QMAX>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int K, int ldx,
                                                         int norm_in, int8_t* __restrict__ xq_op,
                                                         float* __restrict__ sx_f,
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     } else {
       amax = fmaxf(xmax, -xmin);
     }
-    const uint16_t s16 = f2h(amax / 7.0f);
+    const uint16_t s16 = f2h(amax / (float)QMAX);
     s_sh = h2f(s16);
     mu_sh = mu;
     inv_sh = inv;
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     uint2 op, lg;
     uint4 v = xr[i];
     if (norm_in) v = norm_block8(v, mu_sh, inv_sh);
-    quant_block8(v, s, op, lg);
+    quant_block8<QMAX>(v, s, op, lg);
     *reinterpret_cast<uint2*>(xq_op + (size_t)m * K + 8 * i) = op;
     if (xq_out) *reinterpret_cast<uint2*>(xq_out + (size_t)m * K + 8 * i) = lg;
   }
@@ -478,7 +480,7 @@ static bool w4a16_lds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= kMax
 // LDS-staged streaming kernel takes (W4A16, up to 4) or the single-row fused one (W4A4).  Measured
 // on the Llama-3-8B-shaped stack, the batched kernel's 16-row tile is faster from these row counts
 // on (M = 6 and 8: 2.3 instead of 2.7-2.9 ms per W4A16 pass; W4A4 M = 4: 2.8 instead of 2.8-4.2).
-static int gemm_min_rows(int mode) { return mode == QS_W4A16 ? 5 : 2; }
+static int gemm_min_rows(int mode) { return mode == QS_W4A16 ? 5 : mode == QS_W4A4 ? 2 : 1; }
 static bool use_gemm(int mode, int M, const int32_t* acc_out) {
   return M >= gemm_min_rows(mode) && acc_out == nullptr;
 }
@@ -489,7 +491,7 @@ static bool use_gemm(int mode, int M, const int32_t* acc_out) {
 static size_t staging_bytes(int mode, int M, int K, bool norm_in) {
   if (mode == QS_W4A16)  // the batched kernel standardises inside the GEMM
     return (norm_in && !w4a16_lds(M, K) && !use_gemm(mode, M, nullptr)) ? align_up((size_t)M * K * 2, 256) : 0;
-  if (w4a4_fused(M, K) && !use_gemm(mode, M, nullptr)) return 0;
+  if (mode == QS_W4A4 && w4a4_fused(M, K) && !use_gemm(mode, M, nullptr)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
 }
 
@@ -652,15 +654,21 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
     }
     return launch_chunked<MODE_W4A16>(a, st);
   }
-  if (w4a4_fused(M, K) && !gemm) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
+  // W4A4 and W4A8 share the integer kernels: only the activation codes' range differs (the fused
+  // quantization of the streaming kernel is INT4 only)
+  if (mode == QS_W4A4 && w4a4_fused(M, K) && !gemm) return launch_split<MODE_W4A4, 1, true>(a, (size_t)M * K, st);
   int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
   float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
-  hipLaunchKernelGGL(act_quant_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
-                     xq_out, sx_out);
+  if (mode == QS_W4A4)
+    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
+                       xq_out, sx_out);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
+                       xq_out, sx_out);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
   if (gemm)
-    return launch_gemm(QS_W4A4, false, nullptr, 0, xq_op, sxf, wp, sp, M, N, K, a.y, a.y16, a.y16 ? a.ldy : N,
+    return launch_gemm(mode, false, nullptr, 0, xq_op, sxf, wp, sp, M, N, K, a.y, a.y16, a.y16 ? a.ldy : N,
                        cnt, gws, gws_bytes, st);
   a.xq = xq_op;
   a.sxf = sxf;

@@ -688,7 +688,7 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   return true;
 }
 
-int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : 1; }
+int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : mode == QS_W4A4 ? 1 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   size_t b = 0;

@@ -7,8 +7,10 @@
 
 namespace qs {
 
-// Quantize one 8-element block (16 bytes of fp16) with scale s; returns the 8 codes in
-// operand byte order (low dword, high dword) and in logical order.
+// Quantize one 8-element block (16 bytes of fp16) with scale s to clamp(rint(x / s), -QMAX - 1,
+// QMAX) (QMAX = 7: INT4 codes; 127: INT8 codes); returns the 8 codes in operand byte order (low
+// dword, high dword) and in logical order.
+template <int QMAX = 7>
 __device__ __forceinline__ void quant_block8(const uint4 v, float s, uint2& op, uint2& logical) {
   const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
   uint32_t lo_op = 0, hi_op = 0, lo_lg = 0, hi_lg = 0;
@@ -17,7 +19,7 @@ __device__ __forceinline__ void quant_block8(const uint4 v, float s, uint2& op, 
     int qv = 0;
     if (s != 0.0f) {
       float r = __builtin_rintf(h2f(h[e]) / s);
-      r = fminf(7.0f, fmaxf(-8.0f, r));
+      r = fminf((float)QMAX, fmaxf(-(float)QMAX - 1.0f, r));
       qv = (int)r;
     }
     const uint32_t b = (uint32_t)(qv & 0xFF);

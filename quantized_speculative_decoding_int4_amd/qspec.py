@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libqspec.so")
 
 QS_W4A16 = 0
 QS_W4A4 = 1
+QS_W4A8 = 2
 GROUP = 128
 MAX_M = 256
 
@@ -41,6 +42,7 @@ _SIGS = {
     "qs_linear_w4a16": ([_p, _p, _p, _p, _i, _i, _i, _p], _i),
     "qs_linear_workspace_bytes": ([_i, _i, _i, _i], _sz),
     "qs_linear_w4a4": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
+    "qs_linear_w4a8": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
     "qs_lmhead": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p], _i),
     "qs_verify_workspace_bytes": ([_i, _i, _i], _sz),
     "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
@@ -142,18 +144,15 @@ def qs_linear_w4a16(x, w_packed, s_packed, n: int, y=None):
     return y
 
 
-def qs_linear_w4a4(x, w_packed, s_packed, n: int, y=None, xq_out=None, sx_out=None, acc_out=None,
-                   ws=None):
-    """x fp16 [M, K] -> y fp32 [M, N]; optional xq int8 [M, K], sx fp16 [M],
-    acc int32 [M, N, K/128] outputs; ws uint8 workspace (allocated if needed)."""
+def _linear_int(name, mode, x, w_packed, s_packed, n, y, xq_out, sx_out, acc_out, ws):
     m, k = x.shape
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    need = linear_workspace_bytes(QS_W4A4, m, n, k)
+    need = linear_workspace_bytes(mode, m, n, k)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     wp, sp = _wcheck(w_packed, s_packed, n, k)
-    _check("qs_linear_w4a4", _lib.qs_linear_w4a4(
+    _check(name, getattr(_lib, name)(
         _ptr(x, torch.float16, (m, k), "x"), wp, sp, _ptr(y, torch.float32, (m, n), "y"), m, n, k,
         _ptr(xq_out, torch.int8, (m, k), "xq_out", nullable=True),
         _ptr(sx_out, torch.float16, (m,), "sx_out", nullable=True),
@@ -162,8 +161,21 @@ def qs_linear_w4a4(x, w_packed, s_packed, n: int, y=None, xq_out=None, sx_out=No
     return y
 
 
+def qs_linear_w4a4(x, w_packed, s_packed, n: int, y=None, xq_out=None, sx_out=None, acc_out=None,
+                   ws=None):
+    """x fp16 [M, K] -> y fp32 [M, N] with INT4 activations; optional xq int8 [M, K],
+    sx fp16 [M], acc int32 [M, N, K/128] outputs; ws uint8 workspace (allocated if needed)."""
+    return _linear_int("qs_linear_w4a4", QS_W4A4, x, w_packed, s_packed, n, y, xq_out, sx_out, acc_out, ws)
+
+
+def qs_linear_w4a8(x, w_packed, s_packed, n: int, y=None, xq_out=None, sx_out=None, acc_out=None,
+                   ws=None):
+    """As qs_linear_w4a4 with INT8 activations (scale max|x| / 127)."""
+    return _linear_int("qs_linear_w4a8", QS_W4A8, x, w_packed, s_packed, n, y, xq_out, sx_out, acc_out, ws)
+
+
 def qs_lmhead(mode: int, x, w_packed, s_packed, v: int, logits=None, ws=None):
-    """x fp16 [M, K] -> logits fp32 [M, V] in mode QS_W4A16 or QS_W4A4."""
+    """x fp16 [M, K] -> logits fp32 [M, V] in mode QS_W4A16, QS_W4A4 or QS_W4A8."""
     m, k = x.shape
     if logits is None:
         logits = torch.empty((m, v), dtype=torch.float32, device=x.device)

@@ -103,7 +103,7 @@ def test_argument_errors_before_any_device_work(lib):
     pl.restype = i
     assert pl(0, 4, ctypes.addressof(desc), 2) == -1                  # 8192 > 4096 columns
     assert pl(0, 4, ctypes.addressof(desc), 1) in (-6, 0, 1)          # one linear: valid
-    assert pl(2, 4, ctypes.addressof(desc), 1) == -1                  # bad mode
+    assert pl(3, 4, ctypes.addressof(desc), 1) == -1                  # bad mode (0, 1, 2 are modes)
     assert pl(0, 300, ctypes.addressof(desc), 1) == -2                # M > 256
     to = lib.qs_set_barrier_timeout_us
     to.argtypes = [i]

@@ -1,4 +1,4 @@
-"""GPU parity of qs_pack_weights + qs_linear_w4a16 / qs_linear_w4a4 / qs_lmhead
+"""GPU parity of qs_pack_weights + qs_linear_w4a16 / qs_linear_w4a4 / qs_linear_w4a8 / qs_lmhead
 against the CPU oracle on the same seeded inputs."""
 
 import numpy as np
@@ -10,6 +10,9 @@ from quantized_speculative_decoding_int4_amd import workloads as W
 from tests.gpu_util import assert_linear_close, chain_rel_tolerance, dev, host, linear_errors
 
 pytestmark = pytest.mark.gpu
+
+
+MODE_NAMES = {0: "w4a16", 1: "w4a4", 2: "w4a8"}
 
 
 @pytest.fixture(scope="module")
@@ -150,9 +153,75 @@ def test_w4a4_and_w4a16_share_one_packed_buffer(qs):
     assert_linear_close(b, O.linear_w4a4(x, q, s)["y"], "shared w4a4")
 
 
+# ---------------------------------------------------------------- W4A8
+
+def _run_w4a8(qs, x, q, s, with_acc):
+    m, k = x.shape
+    n = q.shape[0]
+    wp, sp = _pack(qs, q, s)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    sx = torch.empty((m,), dtype=torch.float16, device="cuda")
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda") if with_acc else None
+    y = qs.qs_linear_w4a8(dev(x), wp, sp, n, xq_out=xq, sx_out=sx, acc_out=acc)
+    return host(y), host(xq), host(sx), (host(acc) if with_acc else None)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (4, 1040, 14336), (9, 200, 512), (33, 150, 384),
+                                   (130, 32, 256)])
+def test_w4a8_exact_parts_and_output(qs, m, n, k):
+    """With the accumulator output (streaming kernel): INT8 codes, scales and
+    per-group i32 sums bit-exact; y within the float bar."""
+    print(f"w4a8 m={m} n={n} k={k}", flush=True)
+    rng = W.rng_for(400 + m)
+    q, s = W.int4_weights(rng, n, k)
+    x, _ = W.activations(rng, m, k)
+    y, xq, sx, acc = _run_w4a8(qs, x, q, s, True)
+    ref = O.linear_w4a8(x, q, s)
+    assert np.array_equal(xq, ref["xq"]), "activation codes"
+    assert np.array_equal(sx.view(np.uint16), ref["sx"].view(np.uint16)), "activation scales"
+    assert np.array_equal(acc.astype(np.int64), ref["acc"]), "group accumulators"
+    assert_linear_close(y, ref["y"], f"w4a8 m={m}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (2, 1040, 1024), (16, 1040, 1024), (24, 300, 4096),
+                                   (70, 1040, 1024), (128, 4096, 4096), (200, 272, 512)])
+def test_w4a8_batched_output(qs, m, n, k):
+    """Without the accumulator output (batched kernel, K split over workgroups
+    where the grid is small): codes and scales bit-exact, y within the float bar."""
+    print(f"w4a8 batched m={m} n={n} k={k}", flush=True)
+    rng = W.rng_for(500 + m)
+    q, s = W.int4_weights(rng, n, k)
+    x, _ = W.activations(rng, m, k)
+    y, xq, sx, _ = _run_w4a8(qs, x, q, s, False)
+    ref = O.linear_w4a8(x, q, s)
+    assert np.array_equal(xq, ref["xq"]), "activation codes"
+    assert np.array_equal(sx.view(np.uint16), ref["sx"].view(np.uint16)), "activation scales"
+    assert_linear_close(y, ref["y"], f"w4a8 batched m={m}")
+
+
+def test_w4a8_rounding_ties_and_zero_row(qs):
+    """Exact half-integer multiples of the scale (round half to even) and an
+    all-zero row."""
+    rng = W.rng_for(301)
+    k = 512
+    q, s = W.int4_weights(rng, 64, k)
+    sc = np.float16(0.25)
+    j = rng.integers(-127, 127, size=(3, k)) + 0.5
+    x = (j * float(sc)).astype(np.float16)
+    x[:, 0] = np.float16(127 * float(sc))                 # amax = 127 s -> scale exactly s
+    x = np.concatenate([x, np.zeros((1, k), np.float16)])
+    y, xq, sx, acc = _run_w4a8(qs, x, q, s, True)
+    ref = O.linear_w4a8(x, q, s)
+    assert sx[0] == sc and sx[3] == 0
+    assert np.array_equal(xq, ref["xq"])
+    assert np.array_equal(acc.astype(np.int64), ref["acc"])
+    assert np.all(y[3] == 0)
+    assert_linear_close(y, ref["y"], "w4a8 ties")
+
+
 # ---------------------------------------------------------------- LM-head at full size
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (1, 4)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (1, 4), (2, 1), (2, 16)])
 def test_lmhead_full_vocab_sampled_rows(qs, mode, m):
     """LM-head 4096 -> 128256 on the GPU; the oracle recomputes 3000 sampled
     vocabulary rows (each output column is independent of the others)."""
@@ -167,8 +236,10 @@ def test_lmhead_full_vocab_sampled_rows(qs, mode, m):
     cols = np.unique(np.concatenate([cols, [0, V - 1]]))
     if mode == 0:
         ref = O.linear_w4a16(x, q[cols], s[cols])
-    else:
+    elif mode == 1:
         ref = O.linear_w4a4(x, q[cols], s[cols])["y"]
+    else:
+        ref = O.linear_w4a8(x, q[cols], s[cols])["y"]
     assert_linear_close(logits[:, cols], ref, f"lmhead mode={mode}")
     assert np.isfinite(logits).all()
 
@@ -207,7 +278,8 @@ def test_chain_exact_balanced_case(qs, mode):
     assert np.array_equal(y.astype(np.float64), O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers))
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20), (0, 20), (0, 70), (1, 70)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20), (0, 20), (0, 70), (1, 70),
+                                    (2, 1), (2, 4), (2, 20), (2, 70)])
 def test_chain_small_llama_like(qs, mode, m):
     """Two layers of q|k|v, o, gate|up, down at hidden 512 plus a 3000-way head;
     o reads the q columns, down reads the gate columns; M = 12 takes the
@@ -221,7 +293,7 @@ def test_chain_small_llama_like(qs, mode, m):
     layers = [W.int4_weights(rng, n, k) for n, k in shapes]
     x, _ = W.activations(rng, m, h)
     y = _gpu_chain(qs, mode, x, layers)
-    ref = O.chain_forward("w4a16" if mode == 0 else "w4a4", x, layers)
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
     assert_linear_close(y, ref, f"chain mode={mode} m={m}")
 
 
