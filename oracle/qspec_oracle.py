@@ -403,6 +403,63 @@ def verify_sample(tgt_logits: np.ndarray, drf_logits: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# Tree-shaped greedy verification.  [P2] aibr.jp summary, section
+# "3.中核となる技術的要素": verification can expand into a tree of candidates
+# (several branches scored in one target pass).  The page gives no rule; the
+# reading is the greedy prefix rule of [P3] "greedy decodingでは一致するprefixを
+# 採用する" applied along every root-to-node path.
+# --------------------------------------------------------------------------
+
+def verify_tree_greedy(tgt_logits: np.ndarray, tokens: np.ndarray, parent: np.ndarray) -> dict:
+    """Greedy acceptance over a tree of draft tokens per sequence.
+
+    tgt_logits fp32 [B, T, V]: row t is the target's next-token scores after
+    node t; node 0 is the root (the last committed token).  tokens [B, T]: the
+    draft token of node t >= 1 (tokens[:, 0] unused).  parent [B, T]: the
+    parent of node t >= 1, valid only in [0, t) (parent[:, 0] unused).
+    Node t >= 1 is accepted iff its parent is valid and accepted and tokens[t]
+    equals the target's Top-1 (first maximal index) of row parent[t]; the root
+    is accepted.  The deepest accepted node wins, the lowest index on equal
+    depth.  Committed: the tokens along the root-to-winner path, then the
+    target's Top-1 at the winner.
+    Returns dict(t [B, T], n_accept [B], out_tokens [B, T], out_nodes [B, T]),
+    out_* padded with -1; out_nodes lists the accepted path's nodes (root
+    excluded).
+    """
+    b_, t_, v_ = tgt_logits.shape
+    top = np.empty((b_, t_), dtype=np.int64)
+    for b in range(b_):
+        top[b], _ = top1(tgt_logits[b])
+    n_acc = np.zeros(b_, dtype=np.int64)
+    out = np.full((b_, t_), -1, dtype=np.int64)
+    nodes = np.full((b_, t_), -1, dtype=np.int64)
+    for b in range(b_):
+        acc = [True] + [False] * (t_ - 1)
+        depth = [0] * t_
+        for t in range(1, t_):
+            p = int(parent[b, t])
+            if 0 <= p < t and acc[p] and int(tokens[b, t]) == int(top[b, p]):
+                acc[t] = True
+                depth[t] = depth[p] + 1
+        win = 0
+        for t in range(1, t_):
+            if acc[t] and depth[t] > depth[win]:
+                win = t
+        path = []
+        node = win
+        while node != 0:
+            path.append(node)
+            node = int(parent[b, node])
+        path.reverse()
+        n_acc[b] = len(path)
+        for i, node in enumerate(path):
+            out[b, i] = tokens[b, node]
+            nodes[b, i] = node
+        out[b, len(path)] = top[b, win]
+    return {"t": top, "n_accept": n_acc, "out_tokens": out, "out_nodes": nodes}
+
+
+# --------------------------------------------------------------------------
 # Closed forms used as pins ([P3] "1回のtarget検証で何token進むか").
 # --------------------------------------------------------------------------
 

@@ -294,3 +294,83 @@ def test_bonus_token_follows_last_target_row():
     # greedy: bonus is the argmax of the last row
     r = O.verify_greedy(lp, np.array([[1, 0]]))
     assert r["out_tokens"][0].tolist() == [1, 0, 0]
+
+
+# ---------------------------------------------------------------- tree-shaped greedy verification
+
+def _tree_brute(top, tokens, parent):
+    """Independent statement: a node is committed-reachable iff every edge on
+    its explicit root path matches; winner = deepest such node, lowest index."""
+    t_ = len(top)
+    best, best_path = 0, []
+    for t in range(1, t_):
+        path, node, ok = [], t, True
+        seen = set()
+        while node != 0:
+            p = int(parent[node])
+            if not (0 <= p < node) or node in seen:
+                ok = False
+                break
+            seen.add(node)
+            if int(tokens[node]) != int(top[p]):
+                ok = False
+            path.append(node)
+            node = p
+        if ok and len(path) > len(best_path):
+            best, best_path = t, path[::-1]
+    return best, best_path
+
+
+def _random_tree(rng, t_):
+    parent = np.zeros(t_, dtype=np.int64)
+    parent[0] = -1
+    for t in range(1, t_):
+        parent[t] = rng.integers(0, t)
+    return parent
+
+
+def test_tree_greedy_brute_force_small_trees():
+    rng = np.random.default_rng(31)
+    v = 3
+    for _ in range(3000):
+        t_ = int(rng.integers(1, 8))
+        parent = _random_tree(rng, t_)
+        top = rng.integers(0, v, size=t_)
+        tokens = rng.integers(0, v, size=t_)
+        if rng.random() < 0.1 and t_ > 1:
+            parent[rng.integers(1, t_)] = rng.choice([-1, t_ + 3])    # invalid parents never accept
+        lg = _onehot_logits(top, v)[None]
+        r = O.verify_tree_greedy(lg, tokens[None], parent[None])
+        win, path = _tree_brute(top, tokens, parent)
+        assert r["n_accept"][0] == len(path)
+        assert r["out_nodes"][0].tolist() == path + [-1] * (t_ - len(path))
+        assert r["out_tokens"][0].tolist() == [int(tokens[n]) for n in path] + [int(top[win])] + [-1] * (t_ - len(path) - 1)
+
+
+def test_tree_greedy_chain_is_the_prefix_rule():
+    """A chain (parent[t] = t - 1) is the plain greedy verify over gamma = T - 1."""
+    rng = np.random.default_rng(32)
+    for _ in range(200):
+        t_ = int(rng.integers(1, 9))
+        lg = rng.normal(size=(2, t_, 7)).astype(np.float32)
+        tok = rng.integers(-1, 8, size=(2, t_))
+        par = np.tile(np.arange(-1, t_ - 1), (2, 1))
+        tree = O.verify_tree_greedy(lg, tok, par)
+        flat = O.verify_greedy(lg, tok[:, 1:])
+        assert np.array_equal(tree["n_accept"], flat["n_accept"])
+        assert np.array_equal(tree["out_tokens"], flat["out_tokens"])
+
+
+def test_tree_greedy_hand_example():
+    """Root's Top-1 is 2; branches 2->1 (matches the Top-1 of node 1, which is
+    1) and 2->3 (no match), plus a sibling 0 under the root: the path
+    root -> node 1 (2) -> node 3 (1) is accepted, and node 3's Top-1 (0) is
+    the bonus token."""
+    top = [2, 1, 0, 0, 3]
+    tokens = [9, 2, 0, 1, 3]
+    parent = [-1, 0, 0, 1, 1]
+    lg = _onehot_logits(top, 4)[None]
+    r = O.verify_tree_greedy(lg, np.array([tokens]) % 4, np.array([parent]))
+    assert r["n_accept"][0] == 2
+    assert r["out_nodes"][0].tolist() == [1, 3, -1, -1, -1]
+    assert r["out_tokens"][0].tolist() == [2, 1, 0, -1, -1]
