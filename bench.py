@@ -291,6 +291,31 @@ def main():
         }
         del tg, dr, wsg
 
+    # tree-shaped greedy verify: 16 sequences x 8-node random trees (parent uniform over earlier
+    # nodes; a node's token is its parent's Top-1 with probability 0.96), V = 128256
+    Bt, Tt = 16, 8
+    tgt_tree = torch.from_numpy(W.logits(rng, (Bt, Tt, V), sigma=5.24)).to(dev)
+    par_np = np.zeros((Bt, Tt), np.int32)
+    par_np[:, 0] = -1
+    for i in range(1, Tt):
+        par_np[:, i] = rng.integers(0, i, size=Bt)
+    tok_np = rng.integers(0, V, size=(Bt, Tt)).astype(np.int32)
+    tree_tok, tree_par = torch.from_numpy(tok_np).to(dev), torch.from_numpy(par_np).to(dev)
+    wst = torch.zeros(qs.verify_workspace_bytes(Bt, Tt - 1, V), dtype=torch.uint8, device=dev)
+    r0 = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
+    t1 = r0["tgt_top1"].cpu().numpy()
+    agree_t = rng.random((Bt, Tt)) < 0.96
+    for i in range(1, Tt):
+        tok_np[:, i] = np.where(agree_t[:, i], t1[np.arange(Bt), par_np[:, i]], tok_np[:, i])
+    tree_tok.copy_(torch.from_numpy(tok_np))
+    tr = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
+    ttms = time_calls(lambda: qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, out=tr, ws=wst))
+    accept[f"tree_B{Bt}_T{Tt}"] = {
+        "positions": Bt * Tt, "greedy_us": ttms * 1e3, "greedy_positions_per_s": Bt * Tt / (ttms * 1e-3),
+        "mean_accepted": float(tr["n_accept"].float().mean().item()),
+    }
+    del tgt_tree, wst
+
     # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
     # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
     # INT4 weights with 8-bit activations on the int8 MFMA); each point is one

@@ -249,6 +249,37 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qs_verify_tree_greedy -- greedy acceptance over a tree of draft candidates
+ * scored in one target pass ([P2] "3.中核となる技術的要素": verification that
+ * expands into a tree; the rule is this library's reading, the greedy prefix
+ * rule of [P3] "greedy decodingでは一致するprefixを採用する" applied along every
+ * root-to-node path).  Per sequence b, with T nodes, node 0 the root (the last
+ * committed token):
+ *   t[i]   = argmax_j tgt_logits[b][i][j] (lowest index among equal maxima),
+ *            the target's choice after node i
+ *   node i >= 1 is accepted iff 0 <= parent[b][i] < i, its parent is accepted
+ *            and tokens[b][i] == t[parent[b][i]]; the root is accepted
+ *   winner = the deepest accepted node (lowest index on equal depth); n = its depth
+ *   out_tokens[b] = the tokens along the root-to-winner path, t[winner], then -1
+ *   out_nodes[b]  = the path's nodes (root excluded), then -1
+ * A chain (parent[i] = i - 1) is qs_verify_greedy with gamma = T - 1.
+ *   tgt_logits fp32 [B][T][V];  tokens, parent int32 [B][T] (entry 0 unused;
+ *              out-of-range tokens or parents never match and are never used as
+ *              addresses; both may be NULL if T = 1)
+ *   tgt_top1   int32 [B][T] (out);  n_accept int32 [B] (out)
+ *   out_tokens int32 [B][T] (out);  out_nodes int32 [B][T] (out, nullable)
+ *   ws         >= qs_verify_workspace_bytes(B, T - 1, V) bytes, zero-filled
+ *              before its first use (see qs_verify_workspace_bytes)
+ * Errors: T < 1 or a NULL required pointer -> QS_ERR_INVALID_ARG; T > 64 ->
+ * QS_ERR_UNSUPPORTED; workspace too small -> QS_ERR_WORKSPACE.
+ */
+int qs_verify_tree_greedy(const float* tgt_logits, const int32_t* tokens,
+                          const int32_t* parent, int B, int T, int V,
+                          int32_t* tgt_top1, int32_t* n_accept,
+                          int32_t* out_tokens, int32_t* out_nodes,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qs_verify_sample -- sampling acceptance with residual resampling ([P3]
  * sampling section and its A/B/C example).  Per sequence b, with
  * p_i = softmax(tgt_logits[b][i]) (i <= gamma) and q_i = softmax(drf_logits[b][i]):

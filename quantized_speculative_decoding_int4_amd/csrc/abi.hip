@@ -168,6 +168,18 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids, int B, i
                               ws, static_cast<hipStream_t>(stream));
 }
 
+int qs_verify_tree_greedy(const float* tgt_logits, const int32_t* tokens, const int32_t* parent, int B, int T,
+                          int V, int32_t* tgt_top1, int32_t* n_accept, int32_t* out_tokens, int32_t* out_nodes,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (T < 1) return QS_ERR_INVALID_ARG;
+  int rc = verify_common_checks(tgt_logits, B, T - 1, V, ws, ws_bytes);
+  if (rc != QS_OK) return rc;
+  if (!tgt_top1 || !n_accept || !out_tokens || (T > 1 && (!tokens || !parent))) return QS_ERR_INVALID_ARG;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  return launch_verify_tree_greedy(tgt_logits, tokens, parent, B, T, V, tgt_top1, n_accept, out_tokens, out_nodes,
+                                   ws, static_cast<hipStream_t>(stream));
+}
+
 int qs_verify_sample(const float* tgt_logits, const float* drf_logits, const int32_t* draft_ids,
                      const float* u_accept, const float* u_final, int B, int gamma, int V, float* accept_prob,
                      int32_t* n_accept, int32_t* out_tokens, float* final_dist, void* ws, size_t ws_bytes,

@@ -79,6 +79,8 @@ size_t verify_workspace(int B, int gamma, int V);
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,
                          int32_t* t, float* p1, int32_t* n_acc, int32_t* out, void* ws,
                          hipStream_t st);
+int launch_verify_tree_greedy(const float* tgt, const int32_t* tok, const int32_t* par, int B, int T, int V,
+                              int32_t* t, int32_t* n_acc, int32_t* out, int32_t* nodes, void* ws, hipStream_t st);
 int launch_verify_sample(const float* tgt, const float* drf, const int32_t* d,
                          const float* u_acc, const float* u_fin, int B, int gamma, int V,
                          float* a, int32_t* n_acc, int32_t* out, float* fdist, void* ws,

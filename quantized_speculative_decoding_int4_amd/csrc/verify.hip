@@ -361,6 +361,73 @@ __global__ __launch_bounds__(kVThreads) void greedy_kernel(const float* __restri
   }
 }
 
+// Tree-shaped greedy verify, one launch: workgroup (row, chunk) of B * T rows (row t of a sequence
+// holds the target's scores after node t; node 0 is the root).  The last workgroup of a sequence
+// merges its rows' Top-1 and walks the tree in node order (a parent precedes its children): node
+// t >= 1 is accepted iff its parent is valid (in [0, t)) and accepted and its token equals the
+// parent row's Top-1.  The deepest accepted node wins (lowest index on equal depth); the committed
+// tokens are those along its root path, then its own Top-1 (the greedy prefix rule applied to every
+// root-to-node path).
+template <bool VEC>
+__global__ __launch_bounds__(kVThreads) void tree_greedy_kernel(const float* __restrict__ tgt, int T, int V, int C,
+                                                                Part* __restrict__ parts,
+                                                                unsigned* __restrict__ cnt,
+                                                                const int32_t* __restrict__ tokens,
+                                                                const int32_t* __restrict__ parent,
+                                                                int32_t* __restrict__ t_out,
+                                                                int32_t* __restrict__ n_acc,
+                                                                int32_t* __restrict__ out,
+                                                                int32_t* __restrict__ out_nodes) {
+  __shared__ int last_sh;
+  __shared__ int t_sh[kMaxGammaShared + 1];
+  __shared__ int depth[kMaxGammaShared + 1], par[kMaxGammaShared + 1], path[kMaxGammaShared + 1];
+  const size_t bid = blockIdx.x;
+  const int row = (int)(bid / C), c = (int)(bid % C);
+  const int b = row / T;
+  const int lo = c * kStatChunk;
+  const int n = V - lo < kStatChunk ? V - lo : kStatChunk;
+  const Msi r = chunk_stats<VEC>(tgt + (size_t)row * V, lo, n);
+  if (threadIdx.x == 0) store_part_coh(parts, bid, r);
+  if (!last_of_sequence(cnt + kCounterStride * b, (unsigned)(T * C), &last_sh)) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = w; i < T; i += kWaves) {
+    const size_t rr = (size_t)b * T + i;
+    const Msi t = merge_row_coh(parts, rr, C);
+    if (lane == 0) {
+      t_sh[i] = t.i;
+      t_out[rr] = t.i;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t* tok = tokens + (size_t)b * T;
+    const int32_t* pa = parent + (size_t)b * T;
+    depth[0] = 0;  // -1: not accepted
+    int win = 0;
+    for (int t = 1; t < T; ++t) {
+      const int p = pa[t];
+      par[t] = p;
+      depth[t] = -1;
+      if (p >= 0 && p < t && depth[p] >= 0 && tok[t] == t_sh[p]) {
+        depth[t] = depth[p] + 1;
+        if (depth[t] > depth[win]) win = t;
+      }
+    }
+    const int na = depth[win];
+    for (int node = win, i = na - 1; i >= 0; --i) {  // root path, filled from the end
+      path[i] = node;
+      node = par[node];
+    }
+    int32_t* o = out + (size_t)b * T;
+    int32_t* on = out_nodes ? out_nodes + (size_t)b * T : nullptr;
+    for (int i = 0; i < T; ++i) {
+      o[i] = i < na ? tok[path[i]] : i == na ? t_sh[win] : -1;
+      if (on) on[i] = i < na ? path[i] : -1;
+    }
+    n_acc[b] = na;
+  }
+}
+
 // Sampling verify, first launch: workgroup (row, chunk) of the B (gamma + 1) target rows, then
 // the B gamma draft rows; the last workgroup of a sequence merges its 2 gamma + 1 rows, computes
 // every a_i = min(1, p(d_i) / q(d_i)), finds the first rejection and records what the final token
@@ -758,6 +825,20 @@ static int greedy_block(const float* tgt, const int32_t* d, int B, int gamma, in
   return launch_status();
 }
 
+static int tree_block(const float* tgt, const int32_t* tok, const int32_t* par, int B, int T, int V, int32_t* t,
+                      int32_t* n_acc, int32_t* out, int32_t* nodes, void* ws, hipStream_t st) {
+  const int C = stat_chunks(V);
+  VerifyWs w = carve(ws, B, T - 1, V);
+  const size_t blocks = (size_t)B * T * C;
+  if (vec_ok(tgt, V))
+    hipLaunchKernelGGL(tree_greedy_kernel<true>, dim3((unsigned)blocks), dim3(kVThreads), 0, st, tgt, T, V, C,
+                       w.parts, w.cnt, tok, par, t, n_acc, out, nodes);
+  else
+    hipLaunchKernelGGL(tree_greedy_kernel<false>, dim3((unsigned)blocks), dim3(kVThreads), 0, st, tgt, T, V, C,
+                       w.parts, w.cnt, tok, par, t, n_acc, out, nodes);
+  return launch_status();
+}
+
 static int sample_block(const float* tgt, const float* drf, const int32_t* d, const float* u_acc,
                         const float* u_fin, int B, int gamma, int V, float* a, int32_t* n_acc,
                         int32_t* out, float* fdist, void* ws, hipStream_t st) {
@@ -811,6 +892,18 @@ int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, i
     const size_t r0 = (size_t)b0 * (gamma + 1);
     const int rc = greedy_block(tgt + r0 * V, d ? d + (size_t)b0 * gamma : d, nb, gamma, V, t + r0,
                                 p1 ? p1 + r0 : p1, n_acc + b0, out + r0, ws, st);
+    if (rc != QS_OK) return rc;
+  }
+  return QS_OK;
+}
+
+int launch_verify_tree_greedy(const float* tgt, const int32_t* tok, const int32_t* par, int B, int T, int V,
+                              int32_t* t, int32_t* n_acc, int32_t* out, int32_t* nodes, void* ws, hipStream_t st) {
+  for (int b0 = 0; b0 < B; b0 += QS_MAX_VERIFY_SEQS) {
+    const int nb = B - b0 < QS_MAX_VERIFY_SEQS ? B - b0 : QS_MAX_VERIFY_SEQS;
+    const size_t r0 = (size_t)b0 * T;
+    const int rc = tree_block(tgt + r0 * V, tok + r0, par + r0, nb, T, V, t + r0, n_acc + b0, out + r0,
+                              nodes ? nodes + r0 : nodes, ws, st);
     if (rc != QS_OK) return rc;
   }
   return QS_OK;

@@ -51,6 +51,7 @@ _SIGS = {
     "qs_set_barrier_timeout_us": ([_i], _i),
     "qs_chain_pass_status": ([_i, _i, _p, _i, _p, _sz, _p, _p], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
+    "qs_verify_tree_greedy": ([_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_sample": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -219,6 +220,32 @@ def qs_verify_greedy(tgt_logits, draft_ids, out=None, ws=None, want_prob=True):
         _ptr(out["top1_prob"], torch.float32, (b, gp1), "top1_prob", nullable=True),
         _ptr(out["n_accept"], torch.int32, (b,), "n_accept"),
         _ptr(out["out_tokens"], torch.int32, (b, gp1), "out_tokens"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
+    return out
+
+
+def qs_verify_tree_greedy(tgt_logits, tokens, parent, out=None, ws=None):
+    """tgt_logits fp32 [B, T, V] (row t: target scores after node t, node 0 the root), tokens and
+    parent int32 [B, T] -> dict(tgt_top1, n_accept, out_tokens, out_nodes)."""
+    b, t, v = tgt_logits.shape
+    dev = tgt_logits.device
+    if out is None:
+        out = {
+            "tgt_top1": torch.empty((b, t), dtype=torch.int32, device=dev),
+            "n_accept": torch.empty((b,), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((b, t), dtype=torch.int32, device=dev),
+            "out_nodes": torch.empty((b, t), dtype=torch.int32, device=dev),
+        }
+    ws = _ws_for(b, t - 1, v, ws, dev)
+    _check("qs_verify_tree_greedy", _lib.qs_verify_tree_greedy(
+        _ptr(tgt_logits, torch.float32, (b, t, v), "tgt_logits"),
+        _ptr(tokens, torch.int32, (b, t), "tokens", nullable=t == 1),
+        _ptr(parent, torch.int32, (b, t), "parent", nullable=t == 1),
+        b, t, v,
+        _ptr(out["tgt_top1"], torch.int32, (b, t), "tgt_top1"),
+        _ptr(out["n_accept"], torch.int32, (b,), "n_accept"),
+        _ptr(out["out_tokens"], torch.int32, (b, t), "out_tokens"),
+        _ptr(out.get("out_nodes"), torch.int32, (b, t), "out_nodes", nullable=True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
     return out
 

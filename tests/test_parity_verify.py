@@ -287,3 +287,73 @@ def test_workspace_reused_across_calls_and_shapes(qs):
             _, _, a = _check_sample(qs, tg, dr, d, ua, uf, want_final=(k + rep) % 2 == 0, ws=ws)
             amb += a
     assert amb <= 1
+
+
+# ---------------------------------------------------------------- tree-shaped greedy verify
+
+def _tree_case(rng, b, t, v, agree_p=0.85, bad_p=0.05):
+    """Random trees (parent[i] uniform in [0, i)); a node's token is its parent
+    row's Top-1 with probability agree_p, else uniform; a few invalid parents
+    and out-of-range tokens."""
+    tg = W.logits(rng, (b, t, v), sigma=5.24)
+    top, _ = O.top1(tg.reshape(-1, v))
+    top = top.reshape(b, t)
+    parent = np.zeros((b, t), np.int32)
+    tokens = np.zeros((b, t), np.int32)
+    for s in range(b):
+        parent[s, 0] = -1
+        for i in range(1, t):
+            parent[s, i] = rng.integers(0, i)
+            tokens[s, i] = top[s, parent[s, i]] if rng.random() < agree_p else rng.integers(0, v)
+            if rng.random() < bad_p:
+                parent[s, i] = rng.choice([-1, i, t + 5])
+            if rng.random() < bad_p:
+                tokens[s, i] = rng.choice([-1, v, v + 7])
+    return tg, tokens, parent
+
+
+def _check_tree(qs, tg, tokens, parent, ws=None):
+    r = qs.qs_verify_tree_greedy(dev(tg), dev(tokens), dev(parent), ws=ws)
+    ref = O.verify_tree_greedy(tg, tokens, parent)
+    assert np.array_equal(host(r["tgt_top1"]), ref["t"]), "Top-1"
+    assert np.array_equal(host(r["n_accept"]), ref["n_accept"]), "accepted depth"
+    assert np.array_equal(host(r["out_tokens"]), ref["out_tokens"]), "committed tokens"
+    assert np.array_equal(host(r["out_nodes"]), ref["out_nodes"]), "accepted path"
+    return r, ref
+
+
+@pytest.mark.parametrize("b,t,v", [(4, 1, 1000), (6, 2, 32), (5, 8, 5003), (3, 33, 1000), (2, 64, 2048),
+                                   (16, 8, 128256)])
+def test_tree_greedy_random(qs, b, t, v):
+    print(f"tree greedy b={b} t={t} v={v}", flush=True)
+    rng = W.rng_for(700 + t + v)
+    tg, tokens, parent = _tree_case(rng, b, t, v)
+    r, ref = _check_tree(qs, tg, tokens, parent)
+    if t >= 8:
+        assert ref["n_accept"].max() >= 2  # deep paths actually exercised
+
+
+def test_tree_greedy_chain_matches_greedy_verify(qs):
+    rng = W.rng_for(701)
+    b, t, v = 8, 6, 4096
+    tg = W.logits(rng, (b, t, v), sigma=5.24)
+    top, _ = O.top1(tg.reshape(-1, v))
+    d = W.agreeing_ids(rng, top.reshape(b, t)[:, :t - 1], v, agree_p=0.9)
+    tokens = np.concatenate([np.zeros((b, 1), np.int32), d.astype(np.int32)], axis=1)
+    parent = np.tile(np.arange(-1, t - 1, dtype=np.int32), (b, 1))
+    r, _ = _check_tree(qs, tg, tokens, parent)
+    g = qs.qs_verify_greedy(dev(tg), dev(d.astype(np.int32)))
+    assert np.array_equal(host(r["n_accept"]), host(g["n_accept"]))
+    assert np.array_equal(host(r["out_tokens"]), host(g["out_tokens"]))
+
+
+def test_tree_greedy_batch_beyond_one_launch_block_and_reuse(qs):
+    """More sequences than one launch block, then a second call on the same
+    workspace (its counters must have been left at zero)."""
+    rng = W.rng_for(702)
+    b, t, v = 16384 + 37, 3, 64  # one launch block holds 16384 sequences
+    tg, tokens, parent = _tree_case(rng, b, t, v)
+    ws = torch.zeros(qs.verify_workspace_bytes(b, t - 1, v), dtype=torch.uint8, device="cuda")
+    _check_tree(qs, tg, tokens, parent, ws=ws)
+    tg2, tokens2, parent2 = _tree_case(rng, 7, 5, 1000)
+    _check_tree(qs, tg2, tokens2, parent2, ws=ws)
