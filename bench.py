@@ -316,6 +316,33 @@ def main():
     }
     del tgt_tree, wst
 
+    # LM-head with the fused Top-1 epilogue against LM-head + a separate Top-1 launch (the head of
+    # the stack above; W4A4 at M = 1 as in a draft step, W4A16 at M = 4 as in the verify)
+    head_wp, head_sp, head_n, head_k = layers[-1]
+    lmtop = {}
+    for mode, mname, mm in ((qs.QS_W4A4, "w4a4_M1", 1), (qs.QS_W4A16, "w4a16_M4", 4)):
+        xh = x_verify[:mm].contiguous()
+        lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
+        wsl = torch.empty(max(1, qs.linear_workspace_bytes(mode, mm, V, head_k)), dtype=torch.uint8, device=dev)
+        wsg = torch.zeros(qs.verify_workspace_bytes(mm, 0, V), dtype=torch.uint8, device=dev)
+        go = qs.qs_verify_greedy(lg.view(mm, 1, V), None, ws=wsg, want_prob=True)
+        wst1 = torch.zeros(qs.lmhead_top1_workspace_bytes(mode, mm, V, head_k), dtype=torch.uint8, device=dev)
+        fo = qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, ws=wst1)
+
+        def separate():
+            qs.qs_lmhead(mode, xh, head_wp, head_sp, V, logits=lg, ws=wsl)
+            qs.qs_verify_greedy(lg.view(mm, 1, V), None, out=go, ws=wsg)
+
+        sep_ms = time_calls(separate)
+        fused_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, top1=fo["top1"],
+                                                        top1_prob=fo["top1_prob"], ws=wst1))
+        nolog_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, want_logits=False,
+                                                        top1=fo["top1"], top1_prob=fo["top1_prob"], ws=wst1))
+        assert bool((fo["top1"] == go["tgt_top1"].view(-1)).all()), "fused Top-1 differs from the verify kernel's"
+        lmtop[mname] = {"separate_us": sep_ms * 1e3, "fused_us": fused_ms * 1e3, "fused_no_logits_us": nolog_ms * 1e3}
+        del wsl, wsg, wst1, lg
+    accept["lmhead_top1"] = lmtop
+
     # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
     # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
     # INT4 weights with 8-bit activations on the int8 MFMA); each point is one

@@ -148,6 +148,30 @@ int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed,
               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qs_lmhead_top1 -- the LM-head with a fused Top-1 epilogue: the logits of
+ * qs_lmhead (written only if `logits` is not NULL) and, per row, the target's
+ * Top-1 ([P1] "結果": each mode's Top-1 token and its probability; [P3]
+ * greedy section) without a second pass over the logits:
+ *   top1[m]      = argmax_v logits[m][v]   (lowest index among equal maxima)
+ *   top1_prob[m] = 1 / sum_v exp(logits[m][v] - max)   (softmax, temperature 1)
+ * Each 256-column output tile reduces its rows to (max, sum of exp, first
+ * argmax); the last tile of a row block merges them in column order.
+ *   mode       QS_W4A16, QS_W4A4 or QS_W4A8 (arithmetic of that mode's linear)
+ *   x          fp16 [M][K];  logits fp32 [M][V] (out, nullable)
+ *   top1       int32 [M] (out);  top1_prob fp32 [M] (out, nullable)
+ *   ws         >= qs_lmhead_top1_workspace_bytes(mode, M, V, K) bytes,
+ *              zero-filled before its first use (its first bytes are arrival
+ *              counters that every call leaves at zero); calls that overlap in
+ *              time must not share it
+ * Errors as qs_linear_w4a4; a missing or short workspace -> QS_ERR_WORKSPACE.
+ */
+size_t qs_lmhead_top1_workspace_bytes(int mode, int M, int V, int K);
+int qs_lmhead_top1(int mode, const uint16_t* x, const uint8_t* w_packed,
+                   const uint16_t* s_packed, float* logits, int M, int V, int K,
+                   int32_t* top1, float* top1_prob,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One linear of a chain (see qs_chain_forward).  Weights come from
  * qs_pack_weights; the struct itself is read on the host during the call.
  */

@@ -139,6 +139,25 @@ int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed, const uint16
                          stream);
 }
 
+size_t qs_lmhead_top1_workspace_bytes(int mode, int M, int V, int K) {
+  if ((mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) || !linear_shape_ok(M, V, K) || M > QS_MAX_M)
+    return 0;
+  return lmhead_top1_workspace(mode, M, V, K);
+}
+
+int qs_lmhead_top1(int mode, const uint16_t* x, const uint8_t* w_packed, const uint16_t* s_packed, float* logits,
+                   int M, int V, int K, int32_t* top1, float* top1_prob, void* ws, size_t ws_bytes, void* stream) {
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
+  if (!x || !w_packed || !s_packed || !top1 || !linear_shape_ok(M, V, K)) return QS_ERR_INVALID_ARG;
+  if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_packed)) return QS_ERR_MISALIGNED;
+  if (!ws || ws_bytes < lmhead_top1_workspace(mode, M, V, K)) return QS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QS_ERR_MISALIGNED;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  return launch_lmhead_top1(mode, x, w_packed, s_packed, logits, M, V, K, top1, top1_prob, ws,
+                            static_cast<hipStream_t>(stream));
+}
+
 size_t qs_verify_workspace_bytes(int B, int gamma, int V) {
   if (B < 1 || gamma < 0 || gamma > kMaxGamma || V < 1 || V > kMaxVocab) return 0;
   return verify_workspace(B, gamma, V);

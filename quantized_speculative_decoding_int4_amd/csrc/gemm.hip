@@ -18,6 +18,7 @@
 // tiles for different rows run back to back and the second read is served by the caches.
 
 #include "qs_act.h"
+#include "qs_msi.h"
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -33,6 +34,7 @@ constexpr int kGemmBlocks = kGemmWaves * kGemmNt;  // row blocks per workgroup (
 constexpr int kGemmMaxSplits = 16;
 constexpr int kGemmMinGroupsPerSplit = 4;
 constexpr int kGemmMaxCounters = 1024;           // split runs have fewer than 256 output tiles
+constexpr int kGemmStatCounters = 64;            // Top-1 epilogue: one per row block (M <= 256)
 
 // Partial slot of one (K split, output tile) workgroup, device-coherent, read back only by the
 // tile's last-arriving workgroup: the accumulators in register order ([wave][mt][nt][lane] float4),
@@ -67,8 +69,14 @@ struct GemmArgs {
   unsigned char* slots;  // splits > 1: partial slots [split][tile]
   unsigned* cnt;         // splits > 1: arrival counter per output tile (zero at launch, left zero)
   float* y;            // fp32 output [M][N] ...
-  uint16_t* y16;       // ... or fp16 output with row stride ldy
+  uint16_t* y16;       // ... or fp16 output with row stride ldy (both NULL: not written)
   int ldy;
+  // Top-1 epilogue (LM-head): per-(row, column tile) softmax-statistics partials [M][tiles],
+  // arrival counter per row block (zero at launch, left zero), per-row Top-1 and its probability
+  unsigned char* stats;
+  unsigned* stats_cnt;
+  int32_t* top1;
+  float* top1_prob;
 };
 
 __device__ __forceinline__ void gemm_lds_barrier() {
@@ -112,15 +120,86 @@ __device__ __forceinline__ int fragment_code_sum(const uint4 w) {
   return (int)u - 32 * 8;
 }
 
+// Top-1 epilogue of one output tile (see STATS below); values as stored: acc times the W4A4 row
+// scale (the LM-head takes no standardisation).
+template <int MT>
+__device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const float4_t (&acc)[MT][kGemmNt], int m0,
+                                                   int rb0, int bx, int by, int lane, int wave) {
+  constexpr int kRows = MT * 16;
+  __shared__ Msi wst[kGemmWaves][kRows];
+  __shared__ int last_top1;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ml = mt * 16 + 4 * (lane >> 4) + j;
+      const int m = m0 + ml < a.M ? m0 + ml : a.M - 1;  // rows past M: computed, never stored
+      const float sx = a.sxf ? a.sxf[m] : 1.0f;
+      Msi t{-INFINITY, 0.0f, 0x7fffffff};
+#pragma unroll
+      for (int nt = 0; nt < kGemmNt; ++nt) {
+        const int n = (rb0 + nt) * 16 + (lane & 15);
+        if (n < a.N) t = msi_merge(t, Msi{acc[mt][nt][j] * sx, 1.0f, n});
+      }
+      // the 16 lanes holding this row: pairs, quads, halves of 8, rows of 16
+      t = msi_merge(t, msi_dpp<0xB1>(t));
+      t = msi_merge(t, msi_dpp<0x4E>(t));
+      t = msi_merge(t, msi_dpp<0x141>(t));
+      t = msi_merge(t, msi_dpp<0x140>(t));
+      if ((lane & 15) == 0) wst[wave][ml] = t;
+    }
+  }
+  __syncthreads();
+  const int tiles = (int)gridDim.y;
+  if ((int)threadIdx.x < kRows && m0 + (int)threadIdx.x < a.M) {
+    const int r = (int)threadIdx.x;
+    const Msi t = msi_merge(msi_merge(wst[0][r], wst[1][r]), msi_merge(wst[2][r], wst[3][r]));  // column order
+    const float4_t v{t.m, t.s, __int_as_float(t.i), 0.0f};
+    slot_store4(a.stats, (int)(((size_t)(m0 + r) * tiles + by) * 16), v);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are in memory
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(a.stats_cnt + bx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old + 1u == (unsigned)tiles;
+    if (last) __hip_atomic_store(a.stats_cnt + bx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_top1 = last;
+  }
+  __syncthreads();
+  if (!last_top1) return;
+  // the row block's last tile: one wave per row, lane-strided over the tiles, then a fixed-order
+  // wave merge
+  for (int r = wave; r < kRows && m0 + r < a.M; r += kGemmWaves) {
+    Msi t{-INFINITY, 0.0f, 0x7fffffff};
+    for (int c = lane; c < tiles; c += 64) {
+      const float4_t v = slot_load4(a.stats, (int)(((size_t)(m0 + r) * tiles + c) * 16));
+      const float vm = v[0], vs = v[1], vi = v[2];
+      t = msi_merge(t, Msi{vm, vs, __float_as_int(vi)});
+    }
+    t = wave_msi(t);
+    if (lane == 0) {
+      a.top1[m0 + r] = t.i;
+      if (a.top1_prob) a.top1_prob[m0 + r] = 1.0f / t.s;
+    }
+  }
+}
+
 // MODE 0 (W4A16) with NORM: the input rows are standardised over their K columns, applied after
 // the contraction as y = (sum_k x w - mu sum_k w) / sd.  The row sums come from the activations as
 // they are staged, the weight sums sum_k w from the packed codes, so no separate pass over the
 // activations is needed.  MT: 16-row tiles per workgroup; D: groups of weights in flight per wave
 // (a register ring: the weights do not depend on the activations, so they are fetched D groups
 // ahead of their use).
-template <int MODE, bool NORM, int MT, int D>
+//
+// STATS (the LM-head's Top-1 epilogue): besides (or instead of) storing the logits, each output
+// tile reduces every row's values to (max, sum of exp(v - max), first argmax) over its 256
+// columns and stores that partial; the last tile of a row block to finish merges the row's
+// partials in column order into its Top-1 and Top-1 probability 1 / sum exp(v - max).  So a greedy
+// step never reads the logits back.
+template <int MODE, bool NORM, int MT, int D, bool STATS>
 __global__ __launch_bounds__(kGemmWaves * 64, 2) void gemm_kernel(const GemmArgs a) {
   static_assert(MODE == 0 || !NORM, "standardisation is fused for W4A16 only");
+  static_assert(!(NORM && STATS), "the Top-1 epilogue serves the stand-alone LM-head");
   constexpr int kRows = MT * 16;
   constexpr int kRowB = MODE == 0 ? 256 : 128;  // activation bytes per row and group
   constexpr int kPitch = kRowB + 16;
@@ -451,11 +530,12 @@ __global__ __launch_bounds__(kGemmWaves * 64, 2) void gemm_kernel(const GemmArgs
         if constexpr (NORM) v = (v - mu * csum[nt]) * inv;
         if (a.y16)
           a.y16[(size_t)m * a.ldy + n] = f2h(v);
-        else
+        else if (a.y)
           a.y[(size_t)m * a.N + n] = v;
       }
     }
   }
+  if constexpr (STATS) gemm_top1_epilogue<MT>(a, acc, m0, rb0, bx, by, lane, wave);
 }
 
 __global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ cnt, int n) {
@@ -479,7 +559,13 @@ int gemm_splits(int mode, int M, int N, int K) {
   return s;
 }
 
-size_t gemm_counter_bytes() { return (size_t)kGemmMaxCounters * 4; }
+size_t gemm_counter_bytes() { return align_up((size_t)(kGemmMaxCounters + kGemmStatCounters) * 4, 256); }
+
+size_t gemm_top1_bytes(int mode, int M, int N) {
+  const size_t ntiles = (size_t)((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks;
+  (void)mode;
+  return align_up((size_t)M * ntiles * 16, 256);
+}
 
 size_t gemm_workspace(int mode, int M, int N, int K) {
   const int s = gemm_splits(mode, M, N, K);
@@ -488,13 +574,19 @@ size_t gemm_workspace(int mode, int M, int N, int K) {
 }
 
 int launch_gemm_clear(unsigned* cnt, hipStream_t st) {
-  hipLaunchKernelGGL(gemm_clear_kernel, dim3(1), dim3(256), 0, st, cnt, kGemmMaxCounters);
+  hipLaunchKernelGGL(gemm_clear_kernel, dim3(1), dim3(256), 0, st, cnt, kGemmMaxCounters + kGemmStatCounters);
   return launch_status();
 }
 
 template <int MODE, bool NORM, int MT, int D>
 static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D>), grid, dim3(kGemmWaves * 64), 0, st, a);
+  if constexpr (!NORM) {
+    if (a.stats) {
+      hipLaunchKernelGGL((gemm_kernel<MODE, false, MT, D, true>), grid, dim3(kGemmWaves * 64), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D, false>), grid, dim3(kGemmWaves * 64), 0, st, a);
 }
 
 // Weight ring depth per row tile: deeper where the accumulators leave room for it (two waves per
@@ -511,7 +603,8 @@ static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st)
 
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
                 const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
-                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st) {
+                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st, const GemmTop1* t1) {
+  if (t1 && (norm || !cnt || !t1->stats || !t1->top1)) return QS_ERR_INVALID_ARG;
   if (mode != QS_W4A16 && norm) return QS_ERR_INVALID_ARG;
   // split K only when the caller's scratch holds the partial slots and the (zeroed) counters;
   // results then differ from the unsplit order by fp32 rounding only
@@ -536,6 +629,12 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
   a.y = y;
   a.y16 = y16;
   a.ldy = ldy;
+  if (t1) {
+    a.stats = t1->stats;
+    a.stats_cnt = cnt + kGemmMaxCounters;
+    a.top1 = t1->top1;
+    a.top1_prob = t1->top1_prob;
+  }
   const int nrb = (N + 15) / 16;
   const dim3 grid((M + mt * 16 - 1) / (mt * 16), (nrb + kGemmBlocks - 1) / kGemmBlocks, a.splits);
   if (a.splits > 1 && (int)(grid.x * grid.y) > kGemmMaxCounters) return QS_ERR_UNSUPPORTED;

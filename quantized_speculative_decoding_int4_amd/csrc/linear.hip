@@ -592,6 +592,40 @@ static int launch_chunked(const LinearArgs& a, hipStream_t st) {
   return QS_OK;
 }
 
+// LM-head with the Top-1 epilogue: [counters (zero before the first call, left zero)] [INT4/INT8
+// codes and scales for the integer modes] [K-split slots] [per-tile softmax-statistics partials].
+static size_t top1_stage_bytes(int mode, int M, int K) {
+  return mode == QS_W4A16 ? 0 : align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
+}
+
+size_t lmhead_top1_workspace(int mode, int M, int V, int K) {
+  return gemm_counter_bytes() + top1_stage_bytes(mode, M, K) + gemm_workspace(mode, M, V, K) +
+         gemm_top1_bytes(mode, M, V);
+}
+
+int launch_lmhead_top1(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* logits, int M,
+                       int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st) {
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  unsigned* cnt = reinterpret_cast<unsigned*>(base);
+  unsigned char* stg = base + gemm_counter_bytes();
+  unsigned char* slots = stg + top1_stage_bytes(mode, M, K);
+  const size_t slot_bytes = gemm_workspace(mode, M, V, K);
+  GemmTop1 t1{slots + slot_bytes, top1, top1_prob};
+  if (mode == QS_W4A16)
+    return launch_gemm(QS_W4A16, false, x, K, nullptr, nullptr, wp, sp, M, V, K, logits, nullptr, V, cnt, slots,
+                       slot_bytes, st, &t1);
+  int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
+  float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
+  if (mode == QS_W4A4)
+    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(256), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(256), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+  const int rc = launch_status();
+  if (rc != QS_OK) return rc;
+  return launch_gemm(mode, false, nullptr, 0, xq_op, sxf, wp, sp, M, V, K, logits, nullptr, V, cnt, slots,
+                     slot_bytes, st, &t1);
+}
+
 int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* y,
                   int M, int N, int K, int8_t* xq_out, uint16_t* sx_out, int32_t* acc_out,
                   void* ws, size_t ws_bytes, hipStream_t st) {

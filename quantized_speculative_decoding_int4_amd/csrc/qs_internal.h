@@ -28,6 +28,11 @@ int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t
                   float* y, int M, int N, int K, int8_t* xq_out, uint16_t* sx_out,
                   int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t st);
 
+// LM-head with the fused Top-1 epilogue (batched kernel at any M): logits nullable.
+size_t lmhead_top1_workspace(int mode, int M, int V, int K);
+int launch_lmhead_top1(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* logits, int M,
+                       int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st);
+
 // Input/output placement of one linear inside a chain: x with row stride ldx, optionally
 // standardised per row; output either fp32 y [M][N] or fp16(y) into y16 with row stride ldy.
 struct LinearIO {
@@ -54,9 +59,17 @@ int linear_clear_counters(int mode, int M, void* ws, hipStream_t st);
 size_t gemm_counter_bytes();
 size_t gemm_workspace(int mode, int M, int N, int K);
 int launch_gemm_clear(unsigned* cnt, hipStream_t st);
+// Top-1 epilogue of the batched kernel (LM-head): stats holds gemm_top1_bytes of partials, top1 [M],
+// top1_prob [M] (nullable); the counters behind cnt must be zero and are left zero.
+struct GemmTop1 {
+  unsigned char* stats;
+  int32_t* top1;
+  float* top1_prob;
+};
+size_t gemm_top1_bytes(int mode, int M, int N);
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
                 const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
-                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st);
+                unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st, const GemmTop1* t1 = nullptr);
 
 // Persistent pass kernel (pass.hip): one resident workgroup per CU runs up to kMaxPassStages
 // linears of a chain per launch.

@@ -44,6 +44,8 @@ _SIGS = {
     "qs_linear_w4a4": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
     "qs_linear_w4a8": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
     "qs_lmhead": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p], _i),
+    "qs_lmhead_top1_workspace_bytes": ([_i, _i, _i, _i], _sz),
+    "qs_lmhead_top1": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "qs_verify_workspace_bytes": ([_i, _i, _i], _sz),
     "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
     "qs_chain_forward": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p], _i),
@@ -189,6 +191,33 @@ def qs_lmhead(mode: int, x, w_packed, s_packed, v: int, logits=None, ws=None):
         m, v, k, _ptr(ws, torch.uint8, None, "ws", nullable=True), 0 if ws is None else ws.numel(),
         _stream()))
     return logits
+
+
+def lmhead_top1_workspace_bytes(mode: int, m: int, v: int, k: int) -> int:
+    return _lib.qs_lmhead_top1_workspace_bytes(mode, m, v, k)
+
+
+def qs_lmhead_top1(mode: int, x, w_packed, s_packed, v: int, logits=None, want_logits=True, top1=None,
+                   top1_prob=None, ws=None):
+    """x fp16 [M, K] -> dict(logits fp32 [M, V] or None, top1 int32 [M], top1_prob fp32 [M]).
+    ws: uint8 workspace, zero-filled before its first use (allocated zeroed if None)."""
+    m, k = x.shape
+    dev = x.device
+    if logits is None and want_logits:
+        logits = torch.empty((m, v), dtype=torch.float32, device=dev)
+    if top1 is None:
+        top1 = torch.empty((m,), dtype=torch.int32, device=dev)
+    if top1_prob is None:
+        top1_prob = torch.empty((m,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.zeros(lmhead_top1_workspace_bytes(mode, m, v, k), dtype=torch.uint8, device=dev)
+    wp, sp = _wcheck(w_packed, s_packed, v, k)
+    _check("qs_lmhead_top1", _lib.qs_lmhead_top1(
+        mode, _ptr(x, torch.float16, (m, k), "x"), wp, sp,
+        _ptr(logits, torch.float32, (m, v), "logits", nullable=True), m, v, k,
+        _ptr(top1, torch.int32, (m,), "top1"), _ptr(top1_prob, torch.float32, (m,), "top1_prob", nullable=True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
+    return {"logits": logits, "top1": top1, "top1_prob": top1_prob}
 
 
 def _ws_for(b, gamma, v, ws, device):

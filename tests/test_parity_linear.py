@@ -358,3 +358,65 @@ def test_barrier_timeout_is_reported_and_cleared(qs):
     assert not qs.qs_chain_pass_status(0, 4, chain, ws)
     assert_linear_close(y, O.chain_forward("w4a16", x, layers), "chain after a time-out")
 
+
+
+# ---------------------------------------------------------------- LM-head with the fused Top-1 epilogue
+
+def _check_top1(r, logits_ref_cols, cols, mode):
+    lg = host(r["logits"])
+    t, p = O.top1(lg)  # the oracle's Top-1 on the very fp32 logits the GPU produced
+    assert np.array_equal(host(r["top1"]).astype(np.int64), t), "Top-1"
+    assert np.abs(host(r["top1_prob"]).astype(np.float64) - p).max() <= 1e-5, "Top-1 probability"
+    if logits_ref_cols is not None:
+        assert_linear_close(lg[:, cols], logits_ref_cols, f"lmhead_top1 mode={mode}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 1), (0, 4), (1, 1), (2, 4), (0, 16), (1, 70)])
+def test_lmhead_top1_full_vocab(qs, mode, m):
+    print(f"lmhead_top1 mode={mode} m={m}", flush=True)
+    rng = W.rng_for(6)
+    V, K = W.VOCAB, W.HIDDEN
+    q, s = W.int4_weights(rng, V, K)
+    x, _ = W.activations(rng, m, K)
+    wp, sp = _pack(qs, q, s)
+    ws = torch.zeros(qs.lmhead_top1_workspace_bytes(mode, m, V, K), dtype=torch.uint8, device="cuda")
+    r = qs.qs_lmhead_top1(mode, dev(x), wp, sp, V, ws=ws)
+    cols = np.unique(np.concatenate([np.sort(rng.choice(V, size=2000, replace=False)), [0, V - 1]]))
+    ref = {0: lambda: O.linear_w4a16(x, q[cols], s[cols]), 1: lambda: O.linear_w4a4(x, q[cols], s[cols])["y"],
+           2: lambda: O.linear_w4a8(x, q[cols], s[cols])["y"]}[mode]()
+    _check_top1(r, ref, cols, mode)
+    # the same call without writing the logits, on the same workspace: identical Top-1
+    r2 = qs.qs_lmhead_top1(mode, dev(x), wp, sp, V, want_logits=False, ws=ws)
+    assert r2["logits"] is None
+    assert np.array_equal(host(r2["top1"]), host(r["top1"]))
+    assert np.array_equal(host(r2["top1_prob"]), host(r["top1_prob"]))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_lmhead_top1_small_vocab_with_k_splits(qs, mode):
+    """Few output tiles, so K is split over workgroups before the Top-1 epilogue."""
+    rng = W.rng_for(7)
+    m, V, K = 20, 3000, 1024
+    q, s = W.int4_weights(rng, V, K)
+    x, _ = W.activations(rng, m, K)
+    wp, sp = _pack(qs, q, s)
+    r = qs.qs_lmhead_top1(mode, dev(x), wp, sp, V)
+    cols = np.arange(V)
+    ref = {0: lambda: O.linear_w4a16(x, q, s), 1: lambda: O.linear_w4a4(x, q, s)["y"],
+           2: lambda: O.linear_w4a8(x, q, s)["y"]}[mode]()
+    _check_top1(r, ref, cols, mode)
+
+
+def test_lmhead_top1_equal_logits(qs):
+    """Every weight code 1, every scale 2^-6, positive inputs: all logits of a row are the
+    same exact value, so the Top-1 is index 0 and its probability exactly 1/V."""
+    m, V, K = 3, 5000, 256
+    q = np.ones((V, K), np.int8)
+    s = np.full((V, K // 128), 2.0 ** -6, np.float16)
+    x = np.full((m, K), 0.5, np.float16)
+    wp, sp = _pack(qs, q, s)
+    r = qs.qs_lmhead_top1(0, dev(x), wp, sp, V)
+    lg = host(r["logits"])
+    assert np.all(lg == lg[:, :1])
+    assert np.all(host(r["top1"]) == 0)
+    assert np.abs(host(r["top1_prob"]) - 1.0 / V).max() <= 1e-9
