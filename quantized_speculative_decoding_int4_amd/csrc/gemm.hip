@@ -1,21 +1,24 @@
-// Batched linear (M >= 16 activation rows): the verify pass over many sequences, where the
-// target scores B * (gamma + 1) positions at once ([P3] "draft modelとtarget modelの処理フロー";
-// modes from [P1] "QSpec の W4A4 モードと W4A16 モード").  Same arithmetic as the streaming
-// linear: W4A16 expands the INT4 codes to fp16 in registers, multiplies them by their group scale
-// (q s rounded to fp16; exact when s is a power of two) and runs v_mfma_f32_16x16x32_f16 with one
-// fp32 accumulator over all of K; W4A4 runs v_mfma_i32_16x16x64_i8 on the quantized activations and
-// scales each 128-wide group's exact i32 sum in fp32.
+// Batched linear: the verify pass over many sequences, where the target scores B * (gamma + 1)
+// positions at once ([P3] "draft modelとtarget modelの処理フロー"; modes from [P1] "QSpec の W4A4
+// モードと W4A16 モード"), and every per-linear call from 5 rows (W4A16) or 2 rows (W4A4, W4A8) on.
+// W4A16 expands the INT4 codes to fp16 in registers, multiplies them by their group scale (q s
+// rounded to fp16; exact when s is a power of two) and runs v_mfma_f32_16x16x32_f16 with one fp32
+// accumulator over all of K; the integer modes run v_mfma_i32_16x16x64_i8 on the quantized
+// activations and scale each 128-wide group's exact i32 sum in fp32.
 //
-// Work split.  A workgroup of 4 waves owns an output tile of 64 rows (4 MFMA row tiles) x 256
-// columns (16 packed row blocks, 4 per wave) over a range of K, one 128-wide group at a time:
-//   * the 64 activation rows of the group are staged once in LDS (double-buffered, rows padded by
-//     16 bytes so the fragment reads of 16 rows hit distinct banks) and read by all 4 waves;
-//   * each wave keeps its 4 weight tiles of the group (and of the next one) in registers, expands
-//     each fragment once and feeds it to 4 MFMAs (one per row tile), while each activation
-//     fragment feeds 4 MFMAs (one per weight tile): per 16-cycle MFMA about 3 VALU operations and
-//     256 bytes of LDS reads, which the SIMD and LDS sustain together.
-// The row tile is the fastest-varying workgroup index, so the workgroups that read the same weight
-// tiles for different rows run back to back and the second read is served by the caches.
+// Work split.  A workgroup of 4 waves owns an output tile of MT * 16 rows (MT = 1, 2 or 4 MFMA
+// row tiles) x 256 columns (16 packed row blocks, 4 per wave) over a range of K, one 128-wide group
+// at a time:
+//   * the group's activation rows are staged once in LDS (double-buffered, rows padded by 16 bytes
+//     so the fragment reads of 16 rows hit distinct banks) and read by all 4 waves;
+//   * each wave keeps D groups of its 4 weight tiles in flight in a register ring, expands each
+//     fragment once and feeds it to MT MFMAs, while each activation fragment feeds 4 MFMAs;
+//   * linears with few output tiles split K over workgroups; the last workgroup of a tile to finish
+//     sums the splits' partials in split order (device-coherent slots, self-resetting counters);
+//   * the workgroup order is remapped so that the row tiles of one column block run on one XCD
+//     and share its L2;
+//   * optional epilogues: the row standardisation of a chain's input (W4A16, applied after the
+//     contraction) and the LM-head's Top-1 (per-tile softmax statistics merged by the last tile).
 
 #include "qs_act.h"
 #include "qs_msi.h"
