@@ -50,13 +50,15 @@ constexpr int kSlotBytes = kSlotStats + kGemmMaxRows * 8;
 static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
 
 // 16-row tiles per workgroup (measured over the Llama-3-8B-shaped stack at M = 16...128): the
-// smallest tile that covers M up to 32 rows; beyond that 64 rows for W4A16 (each expanded weight
-// fragment feeds four MFMAs) and 32 rows for W4A4 (its expansion is cheaper, and smaller tiles need
-// fewer K splits), except for vocabulary-wide linears, where 64 rows halve the weight re-reads.
+// smallest tile that covers M up to 32 rows, 32 rows beyond that (64-row tiles, where each expanded
+// weight fragment feeds four MFMAs, measured slower in both modes: W4A16 M = 64 4.26 ms per pass
+// against 3.66, M = 128 5.37 against 5.15), except for vocabulary-wide linears, where 64 rows
+// halve the weight re-reads.
 static int gemm_mt(int mode, int M, int N) {
+  (void)mode;
   if (M <= 16) return 1;
   if (M <= 32) return 2;
-  return (mode == QS_W4A16 || N >= 32768) ? 4 : 2;
+  return N >= 32768 ? 4 : 2;
 }
 
 struct GemmArgs {
