@@ -221,7 +221,7 @@ def test_w4a8_rounding_ties_and_zero_row(qs):
 
 # ---------------------------------------------------------------- LM-head at full size
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (1, 4), (2, 1), (2, 16)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (1, 4), (2, 1), (2, 16), (0, 70), (2, 40)])
 def test_lmhead_full_vocab_sampled_rows(qs, mode, m):
     """LM-head 4096 -> 128256 on the GPU; the oracle recomputes 3000 sampled
     vocabulary rows (each output column is independent of the others)."""
@@ -295,6 +295,21 @@ def test_chain_small_llama_like(qs, mode, m):
     y = _gpu_chain(qs, mode, x, layers)
     ref = O.chain_forward(MODE_NAMES[mode], x, layers)
     assert_linear_close(y, ref, f"chain mode={mode} m={m}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 40), (1, 40), (2, 33)])
+def test_chain_with_vocabulary_wide_head(qs, mode, m):
+    """A vocabulary-wide last stage (N >= 32768) takes the batched kernel's 64-row tiles beyond 32
+    rows (with the standardisation epilogue in W4A16)."""
+    print(f"chain wide head mode={mode} m={m}", flush=True)
+    rng = W.rng_for(850 + m + mode)
+    h = 256
+    shapes = [(h + 128, h), (h, h), (33000, h)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, h)
+    y = _gpu_chain(qs, mode, x, layers)
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
+    assert_linear_close(y, ref, f"chain wide head mode={mode} m={m}")
 
 
 @pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
