@@ -101,35 +101,42 @@ __global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restric
 }
 
 // Stand-alone quantizer (INT4 codes for W4A4, QMAX = 7; INT8 codes for W4A8, QMAX = 127): one
-// workgroup per row.  Writes operand-ordered codes and the
-// fp32 value of the fp16 scale to the workspace, and optionally the logical codes / fp16 scales.
+// workgroup of kAqThreads per row (wide, so the serial statistics and quantization of one row
+// are short).  Writes operand-ordered codes and the fp32 value of the fp16 scale to the workspace,
+// and optionally the logical codes / fp16 scales.
+constexpr int kAqThreads = 1024;
 template <int QMAX>
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int K, int ldx,
-                                                        int norm_in, int8_t* __restrict__ xq_op,
-                                                        float* __restrict__ sx_f,
-                                                        int8_t* __restrict__ xq_out,
-                                                        uint16_t* __restrict__ sx_out) {
-  __shared__ float red[4][4];
+__global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int K, int ldx,
+                                                               int norm_in, int8_t* __restrict__ xq_op,
+                                                               float* __restrict__ sx_f,
+                                                               int8_t* __restrict__ xq_out,
+                                                               uint16_t* __restrict__ sx_out) {
+  constexpr int kW = kAqThreads / 64;
+  __shared__ float red[4][kW];
   __shared__ float s_sh, mu_sh, inv_sh;
   const int m = blockIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * ldx);
   const int nb = K / 8;
   float sum = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-  for (int i = threadIdx.x; i < nb; i += 256) stats_block8(xr[i], sum, sq, mx, mn);
-  sum = wave_sum(sum);
-  sq = wave_sum(sq);
-  mx = wave_max(mx);
-  mn = wave_min(mn);
+  for (int i = threadIdx.x; i < nb; i += kAqThreads) stats_block8(xr[i], sum, sq, mx, mn);
+  sum = wave_sum_dpp(sum);
+  sq = wave_sum_dpp(sq);
+  mx = wave_max_dpp(mx);
+  mn = wave_min_dpp(mn);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { red[0][w] = sum; red[1][w] = sq; red[2][w] = mx; red[3][w] = mn; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float xmax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
-    const float xmin = fminf(fminf(red[3][0], red[3][1]), fminf(red[3][2], red[3][3]));
+    float tsum = red[0][0], tsq = red[1][0], xmax = red[2][0], xmin = red[3][0];
+    for (int j = 1; j < kW; ++j) {  // fixed order
+      tsum += red[0][j];
+      tsq += red[1][j];
+      xmax = fmaxf(xmax, red[2][j]);
+      xmin = fminf(xmin, red[3][j]);
+    }
     float mu = 0.f, inv = 0.f, amax;
     if (norm_in) {
-      norm_params(red[0][0] + red[0][1] + red[0][2] + red[0][3], red[1][0] + red[1][1] + red[1][2] + red[1][3],
-                  K, mu, inv);
+      norm_params(tsum, tsq, K, mu, inv);
       amax = fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)));
     } else {
       amax = fmaxf(xmax, -xmin);
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   }
   __syncthreads();
   const float s = s_sh;
-  for (int i = threadIdx.x; i < nb; i += 256) {
+  for (int i = threadIdx.x; i < nb; i += kAqThreads) {
     uint2 op, lg;
     uint4 v = xr[i];
     if (norm_in) v = norm_block8(v, mu_sh, inv_sh);
@@ -617,9 +624,9 @@ int launch_lmhead_top1(int mode, const uint16_t* x, const uint8_t* wp, const uin
   int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
   float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
   if (mode == QS_W4A4)
-    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(256), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(kAqThreads), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(256), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(kAqThreads), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
   return launch_gemm(mode, false, nullptr, 0, xq_op, sxf, wp, sp, M, V, K, logits, nullptr, V, cnt, slots,
@@ -694,10 +701,10 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
   float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
   if (mode == QS_W4A4)
-    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
+    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(kAqThreads), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
                        xq_out, sx_out);
   else
-    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(256), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
+    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(kAqThreads), 0, st, x, K, io.ldx, io.norm_in, xq_op, sxf,
                        xq_out, sx_out);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
