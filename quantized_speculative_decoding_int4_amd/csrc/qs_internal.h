@@ -73,7 +73,7 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
 
 // Persistent pass kernel (pass.hip): one resident workgroup per CU runs up to kMaxPassStages
 // linears of a chain per launch.
-constexpr int kMaxPassStages = 64;
+constexpr int kMaxPassStages = 72;
 constexpr int kMaxPassWorkgroups = 1024;
 // Control region of a persistent pass in the workspace: go word and error word, then one 128-byte
 // arrival flag per workgroup.

@@ -314,15 +314,15 @@ def test_chain_with_vocabulary_wide_head(qs, mode, m):
 
 @pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
-    """69 linears.  At M <= 4 (W4A16) / M = 1 (W4A4) the persistent pass splits
-    them over two launches, so the hand-over at the seam (fp16 activations in
+    """75 linears.  At M <= 4 (W4A16) / M = 1 (W4A4) the persistent pass splits
+    them over two launches (at most 72 per launch), so the hand-over at the seam (fp16 activations in
     the workspace) is covered; the other row counts run linear by linear
     (streaming kernel below 16 rows, batched kernel from 16).
     End to end the output must stay within the chain bound; the last stage,
     fed the GPU's own fp16 input to it, within the single-linear bound."""
     print(f"long chain mode={mode} m={m}", flush=True)
     rng = W.rng_for(900 + 10 * m + mode)
-    shapes = [(384, 256), (256, 384)] * 34 + [(1000, 256)]
+    shapes = [(384, 256), (256, 384)] * 37 + [(1000, 256)]
     layers = [W.int4_weights(rng, n, k) for n, k in shapes]
     x, _ = W.activations(rng, m, 256)
     packed = []
