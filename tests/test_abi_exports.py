@@ -129,3 +129,40 @@ def test_no_gpu_means_device_error(lib):
     lin.restype = i
     fake = 1 << 20
     assert lin(fake, fake, fake, fake, 4, 4096, 4096, None) == -6
+
+
+def test_new_entry_points_argument_errors(lib):
+    """W4A8 linear, LM-head with the fused Top-1 and tree verify: errors returned before any
+    device work (fake pointers are never dereferenced)."""
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fake = 1 << 20
+    w8 = lib.qs_linear_w4a8
+    w8.argtypes = [p, p, p, p, i, i, i, p, p, p, p, sz, p]
+    w8.restype = i
+    assert w8(None, fake, fake, fake, 4, 4096, 4096, None, None, None, fake, 1 << 30, None) == -1
+    assert w8(fake, fake, fake, fake, 4, 4096, 4000, None, None, None, fake, 1 << 30, None) == -1
+    assert w8(fake, fake, fake, fake, 300, 4096, 4096, None, None, None, fake, 1 << 30, None) == -2
+    assert w8(fake, fake, fake, fake, 1, 4096, 4096, None, None, None, None, 0, None) == -4  # always staged
+    lw = lib.qs_linear_workspace_bytes
+    lw.argtypes = [i, i, i, i]
+    lw.restype = sz
+    assert lw(2, 1, 4096, 4096) > 0 and lw(3, 1, 4096, 4096) == 0
+    tw = lib.qs_lmhead_top1_workspace_bytes
+    tw.argtypes = [i, i, i, i]
+    tw.restype = sz
+    assert tw(0, 4, 128256, 4096) >= 4 * 501 * 16 and tw(1, 1, 128256, 4096) > tw(0, 1, 128256, 4096)
+    assert tw(3, 4, 128256, 4096) == 0 and tw(0, 0, 128256, 4096) == 0
+    t1 = lib.qs_lmhead_top1
+    t1.argtypes = [i, p, p, p, p, i, i, i, p, p, p, sz, p]
+    t1.restype = i
+    assert t1(3, fake, fake, fake, None, 4, 1000, 512, fake, None, fake, 1 << 30, None) == -1   # bad mode
+    assert t1(0, fake, fake, fake, None, 4, 1000, 512, None, None, fake, 1 << 30, None) == -1   # top1 NULL
+    assert t1(0, fake, fake, fake, None, 257, 1000, 512, fake, None, fake, 1 << 30, None) == -2
+    assert t1(0, fake, fake, fake, None, 4, 1000, 512, fake, None, fake, 16, None) == -4        # short ws
+    tg = lib.qs_verify_tree_greedy
+    tg.argtypes = [p, p, p, i, i, i, p, p, p, p, p, sz, p]
+    tg.restype = i
+    assert tg(fake, fake, fake, 1, 0, 10, fake, fake, fake, None, fake, 1 << 30, None) == -1   # T < 1
+    assert tg(fake, fake, fake, 1, 65, 10, fake, fake, fake, None, fake, 1 << 30, None) == -2  # T > 64
+    assert tg(fake, None, fake, 1, 4, 10, fake, fake, fake, None, fake, 1 << 30, None) == -1   # tokens
+    assert tg(fake, fake, fake, 1, 4, 10, fake, fake, fake, None, fake, 0, None) == -4
