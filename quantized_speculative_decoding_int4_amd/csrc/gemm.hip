@@ -54,8 +54,7 @@ static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
 // weight fragment feeds four MFMAs, measured slower in both modes: W4A16 M = 64 4.26 ms per pass
 // against 3.66, M = 128 5.37 against 5.15), except for vocabulary-wide linears, where 64 rows
 // halve the weight re-reads.
-static int gemm_mt(int mode, int M, int N) {
-  (void)mode;
+static int gemm_mt(int M, int N) {
   if (M <= 16) return 1;
   if (M <= 32) return 2;
   return N >= 32768 ? 4 : 2;
@@ -551,13 +550,13 @@ __global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ 
 
 // K splits for an M x N x K linear: enough workgroups for a 256-CU part, at least
 // kGemmMinGroupsPerSplit groups per split.
-static int gemm_tiles(int mode, int M, int N) {
-  const int rows = gemm_mt(mode, M, N) * 16;
+static int gemm_tiles(int M, int N) {
+  const int rows = gemm_mt(M, N) * 16;
   return (((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks) * ((M + rows - 1) / rows);
 }
 
-int gemm_splits(int mode, int M, int N, int K) {
-  const int tiles = gemm_tiles(mode, M, N);
+int gemm_splits(int M, int N, int K) {
+  const int tiles = gemm_tiles(M, N);
   const int G = K / kGroup;
   int s = 1;
   while (s < kGemmMaxSplits && tiles * s < 256 && G / (2 * s) >= kGemmMinGroupsPerSplit) s *= 2;
@@ -566,16 +565,15 @@ int gemm_splits(int mode, int M, int N, int K) {
 
 size_t gemm_counter_bytes() { return align_up((size_t)(kGemmMaxCounters + kGemmStatCounters) * 4, 256); }
 
-size_t gemm_top1_bytes(int mode, int M, int N) {
+size_t gemm_top1_bytes(int M, int N) {
   const size_t ntiles = (size_t)((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks;
-  (void)mode;
   return align_up((size_t)M * ntiles * 16, 256);
 }
 
-size_t gemm_workspace(int mode, int M, int N, int K) {
-  const int s = gemm_splits(mode, M, N, K);
+size_t gemm_workspace(int M, int N, int K) {
+  const int s = gemm_splits(M, N, K);
   if (s <= 1) return 0;
-  return (size_t)s * gemm_tiles(mode, M, N) * kSlotBytes;
+  return (size_t)s * gemm_tiles(M, N) * kSlotBytes;
 }
 
 int launch_gemm_clear(unsigned* cnt, hipStream_t st) {
@@ -613,10 +611,10 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
   if (mode != QS_W4A16 && norm) return QS_ERR_INVALID_ARG;
   // split K only when the caller's scratch holds the partial slots and the (zeroed) counters;
   // results then differ from the unsplit order by fp32 rounding only
-  const size_t need = gemm_workspace(mode, M, N, K);
-  const int splits = need > 0 && cnt != nullptr && ws != nullptr && ws_bytes >= need ? gemm_splits(mode, M, N, K) : 1;
+  const size_t need = gemm_workspace(M, N, K);
+  const int splits = need > 0 && cnt != nullptr && ws != nullptr && ws_bytes >= need ? gemm_splits(M, N, K) : 1;
   const int G = K / kGroup;
-  const int mt = gemm_mt(mode, M, N);
+  const int mt = gemm_mt(M, N);
   GemmArgs a{};
   a.x = x;
   a.ldx = ldx;

@@ -57,7 +57,7 @@ int linear_clear_counters(int mode, int M, void* ws, hipStream_t st);
 // fp32 y [M][N] or fp16 y16 (row stride ldy).  K is split over workgroups when cnt (zeroed arrival
 // counters, left zero) and ws (partial slots of gemm_workspace bytes) are given.
 size_t gemm_counter_bytes();
-size_t gemm_workspace(int mode, int M, int N, int K);
+size_t gemm_workspace(int M, int N, int K);
 int launch_gemm_clear(unsigned* cnt, hipStream_t st);
 // Top-1 epilogue of the batched kernel (LM-head): stats holds gemm_top1_bytes of partials, top1 [M],
 // top1_prob [M] (nullable); the counters behind cnt must be zero and are left zero.
@@ -66,7 +66,7 @@ struct GemmTop1 {
   int32_t* top1;
   float* top1_prob;
 };
-size_t gemm_top1_bytes(int mode, int M, int N);
+size_t gemm_top1_bytes(int M, int N);
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
                 const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
                 unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st, const GemmTop1* t1 = nullptr);
