@@ -435,3 +435,58 @@ def test_lmhead_top1_equal_logits(qs):
     assert np.all(lg == lg[:, :1])
     assert np.all(host(r["top1"]) == 0)
     assert np.abs(host(r["top1_prob"]) - 1.0 / V).max() <= 1e-9
+
+
+# ---------------------------------------------------------------- full-size stack, the bench's launch configuration
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1)])
+def test_full_stack_last_stage_sampled(qs, mode, m):
+    """The 32-layer Llama-3-8B-shaped stack + 4096 -> 128256 LM-head as the bench runs it (the
+    persistent pass: W4A16 verify at M = 4, W4A4 draft at M = 1).  The same stack without its
+    head gives the GPU's own fp16 input to the head (stage arithmetic does not depend on how the
+    stages are grouped into launches); the oracle then recomputes 3000 sampled vocabulary columns of
+    the logits from it, held to the single-linear bar."""
+    print(f"full stack mode={mode} m={m}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    layers, head_q, head_s = [], None, None
+    for name, n, k in W.stack_shapes():
+        q, s = W.int4_weights_device(gen, n, k, device="cuda")
+        wp, sp = qs.qs_pack_weights(q, s)
+        if name == "lm_head":
+            head_q, head_s = q, s
+        del q, s
+        layers.append((wp, sp, n, k))
+    chain = qs.Chain(layers)
+    assert chain.pass_launches(mode, m) >= 2  # the persistent pass, more than one launch
+    x = dev(W.activations(W.rng_for(31), m, W.HIDDEN)[0])
+    logits = host(qs.qs_chain_forward(mode, x, chain))
+    body = host(qs.qs_chain_forward(mode, x, qs.Chain(layers[:-1]))).astype(np.float16)
+    assert np.isfinite(logits).all() and np.isfinite(body).all()
+    rng = W.rng_for(32)
+    cols = np.unique(np.concatenate([np.sort(rng.choice(W.VOCAB, size=3000, replace=False)), [0, W.VOCAB - 1]]))
+    idx = torch.from_numpy(cols).cuda()
+    q = host(head_q.index_select(0, idx))
+    s = host(head_s.index_select(0, idx))
+    xin = O.standardize_rows(body)
+    ref = O.linear_w4a16(xin, q, s) if mode == 0 else O.linear_w4a4(xin, q, s)["y"]
+    assert_linear_close(logits[:, cols], ref, f"full stack mode={mode} m={m}")
+
+
+def test_full_stack_rows_are_independent(qs):
+    """Full-size W4A16 verify pass at M = 4 against four M = 1 passes on the same rows: every row's
+    arithmetic (its statistics, K split and MFMA row) is its own, so the logits match bit for bit."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    layers = []
+    for name, n, k in W.stack_shapes():
+        q, s = W.int4_weights_device(gen, n, k, device="cuda")
+        wp, sp = qs.qs_pack_weights(q, s)
+        del q, s
+        layers.append((wp, sp, n, k))
+    chain = qs.Chain(layers)
+    x = dev(W.activations(W.rng_for(33), 4, W.HIDDEN)[0])
+    full = host(qs.qs_chain_forward(0, x, chain))
+    for i in range(4):
+        one = host(qs.qs_chain_forward(0, x[i:i + 1].contiguous(), chain))
+        assert np.array_equal(one[0], full[i]), f"row {i}"
