@@ -439,10 +439,11 @@ def test_lmhead_top1_equal_logits(qs):
 
 # ---------------------------------------------------------------- full-size stack, the bench's launch configuration
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 128), (1, 128), (2, 64)])
 def test_full_stack_last_stage_sampled(qs, mode, m):
     """The 32-layer Llama-3-8B-shaped stack + 4096 -> 128256 LM-head as the bench runs it (the
-    persistent pass: W4A16 verify at M = 4, W4A4 draft at M = 1).  The same stack without its
+    persistent pass: W4A16 verify at M = 4, W4A4 draft at M = 1; the batched verify, one launch of
+    the batched kernel per linear, at M = 64 and 128).  The same stack without its
     head gives the GPU's own fp16 input to the head (stage arithmetic does not depend on how the
     stages are grouped into launches); the oracle then recomputes 3000 sampled vocabulary columns of
     the logits from it, held to the single-linear bar."""
@@ -458,7 +459,7 @@ def test_full_stack_last_stage_sampled(qs, mode, m):
         del q, s
         layers.append((wp, sp, n, k))
     chain = qs.Chain(layers)
-    assert chain.pass_launches(mode, m) >= 2  # the persistent pass, more than one launch
+    assert chain.pass_launches(mode, m) == (0 if m > 4 else 2)  # persistent pass in 2 launches, or per linear
     x = dev(W.activations(W.rng_for(31), m, W.HIDDEN)[0])
     logits = host(qs.qs_chain_forward(mode, x, chain))
     body = host(qs.qs_chain_forward(mode, x, qs.Chain(layers[:-1]))).astype(np.float16)
@@ -469,7 +470,8 @@ def test_full_stack_last_stage_sampled(qs, mode, m):
     q = host(head_q.index_select(0, idx))
     s = host(head_s.index_select(0, idx))
     xin = O.standardize_rows(body)
-    ref = O.linear_w4a16(xin, q, s) if mode == 0 else O.linear_w4a4(xin, q, s)["y"]
+    ref = {0: lambda: O.linear_w4a16(xin, q, s), 1: lambda: O.linear_w4a4(xin, q, s)["y"],
+           2: lambda: O.linear_w4a8(xin, q, s)["y"]}[mode]()
     assert_linear_close(logits[:, cols], ref, f"full stack mode={mode} m={m}")
 
 
