@@ -201,7 +201,7 @@ __device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const floa
 // partials in column order into its Top-1 and Top-1 probability 1 / sum exp(v - max).  So a greedy
 // step never reads the logits back.
 template <int MODE, bool NORM, int MT, int D, bool STATS>
-__global__ __launch_bounds__(kGemmWaves * 64, (MT == 1 && !STATS) ? 3 : 2) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void gemm_kernel(const GemmArgs a) {
   static_assert(MODE == 0 || !NORM, "standardisation is fused for W4A16 only");
   static_assert(!(NORM && STATS), "the Top-1 epilogue serves the stand-alone LM-head");
   constexpr int kRows = MT * 16;
@@ -592,15 +592,15 @@ static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D, false>), grid, dim3(kGemmWaves * 64), 0, st, a);
 }
 
-// Weight ring depth per row tile: deeper where the accumulators leave room for it (two waves per
-// SIMD must fit; 16-row tiles take a 4-group ring and three waves per SIMD, about 2% faster over the
-// stack at M = 4...16 than a 6-group ring with two).
+// Weight ring depth per row tile: 16- and 32-row tiles take a 4- and a 2-group ring and three waves per
+// SIMD (2-3% faster over the stack than a 6-group ring with two); 64-row tiles, whose accumulators
+// need more registers, a 4- or 2-group ring and two waves per SIMD.
 template <int MODE, bool NORM>
 static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st) {
   if (mt == 1)
     gemm_launch_one<MODE, NORM, 1, 4>(a, grid, st);
   else if (mt == 2)
-    gemm_launch_one<MODE, NORM, 2, 6>(a, grid, st);
+    gemm_launch_one<MODE, NORM, 2, 2>(a, grid, st);
   else
     gemm_launch_one<MODE, NORM, 4, MODE == 0 ? 4 : 2>(a, grid, st);
 }
