@@ -386,7 +386,7 @@ def _check_top1(r, logits_ref_cols, cols, mode):
         assert_linear_close(lg[:, cols], logits_ref_cols, f"lmhead_top1 mode={mode}")
 
 
-@pytest.mark.parametrize("mode,m", [(0, 1), (0, 4), (1, 1), (2, 4), (0, 16), (1, 70)])
+@pytest.mark.parametrize("mode,m", [(0, 1), (0, 4), (1, 1), (2, 4), (0, 16), (1, 70), (0, 40), (2, 24)])
 def test_lmhead_top1_full_vocab(qs, mode, m):
     print(f"lmhead_top1 mode={mode} m={m}", flush=True)
     rng = W.rng_for(6)
