@@ -28,8 +28,9 @@
 //  * W4A16 (four rows, up to 112 KiB of input): a grid barrier, then one fetch.
 //    A premature fetch of that much data costs a second full round trip, which
 //    measured slower than the barrier.  Workgroup b stores an epoch into its own
-//    flag once its outputs are acknowledged; workgroup 0 gathers the flags and
-//    publishes the epoch in a `go` word.
+//    flag once its outputs are acknowledged, and every workgroup watches all the
+//    flags (one round trip; a relay through a `go` word published by workgroup 0
+//    measured 2.4% slower over the verify pass).
 // Every wait has a wall-clock deadline that sets an error word and makes the
 // workgroup exit, so no wave can wait forever.
 //
@@ -108,7 +109,6 @@ struct PassArgs {
   float* out;         // fp32 output of the launch's last stage when last_is_final
   int last_is_final;
   unsigned* flags;    // W4A16: per-workgroup arrival epochs (kFlagStride apart), zero at pass start
-  unsigned* go;       // W4A16: released epoch, zero at pass start
   unsigned epoch0;    // W4A16: epochs of this launch's boundaries are epoch0 + 1, epoch0 + 2, ...
   unsigned* error;    // set to 1 if a wait passed its deadline
   long long deadline; // wall-clock ticks allowed per wait
@@ -210,7 +210,8 @@ __device__ __forceinline__ void dma_to_lds_sc1(const void* g, uint32_t lds_addr)
 
 // LDS barriers every wave executes at a stage boundary:
 //   A partials parked |
-//   W4A16 grid barrier: B outputs stored | C arrivals seen (workgroup 0) | D go seen |
+//   W4A16 grid barrier: B outputs stored | C all arrivals seen | D (kept: the streaming waves
+//   count these barriers) |
 //   staging: W4A16 G activations in LDS; W4A4 E statistics | F row parameters | G codes in LDS
 // and the staging barriers once before the first stage.  The last stage ends after A.
 // Streaming waves only pass through them.
@@ -219,9 +220,9 @@ template <int MODE>
 constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
 
 // W4A16 grid barrier between stages, free of contended atomics: workgroup b stores the epoch into
-// its own flag (one 128-byte line each) once its outputs are acknowledged; the control threads of
-// workgroup 0 each watch flags and, once all have arrived, workgroup 0 stores the epoch into the
-// `go` word that every workgroup waits for.  All of these are device-coherent accesses.
+// its own flag (one 128-byte line each) once its outputs are acknowledged, and the control threads
+// of every workgroup each watch flags until all have arrived.  All of these are device-coherent
+// accesses.
 constexpr int kFlagStride = 32;  // uint32 words between flags (128 bytes)
 
 __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, const PassArgs& a) {
@@ -640,15 +641,10 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         const unsigned epoch = a.epoch0 + (unsigned)(s + 1);
         if (ct == 0)
           __hip_atomic_store(a.flags + (size_t)bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (bid == 0) {
-          for (int t = ct; t < grid; t += kCT)
-            if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
-        }
+        // every workgroup watches all flags itself: one round trip, no `go` relay
+        for (int t = ct; t < grid; t += kCT)
+          if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
         lds_barrier();  // C
-        if (ct == 0) {
-          if (bid == 0 && !fail_sh) __hip_atomic_store(a.go, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (!fail_sh && !wait_at_least(a.go, epoch, a)) fail_sh = 1;
-        }
         lds_barrier();  // D
       }
     }
@@ -656,7 +652,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
 }
 
 // Start of a pass: fills the stage outputs with kEmpty (W4A4; device-coherent stores) and zeroes the
-// control words (go and error word, then n_flags arrival flags kFlagStride apart).
+// control words (a reserved word and the error word, then n_flags arrival flags kFlagStride apart).
 __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags) {
   if (blockIdx.x == 0) {
     if (threadIdx.x < 2) __hip_atomic_store(ctrl + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -769,7 +765,6 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     }
     a.out = out;
     a.last_is_final = s0 + cnt == n;
-    a.go = ctrl;
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
     a.epoch0 = (unsigned)s0;

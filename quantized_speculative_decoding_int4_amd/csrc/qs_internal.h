@@ -75,8 +75,8 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
 // linears of a chain per launch.
 constexpr int kMaxPassStages = 72;
 constexpr int kMaxPassWorkgroups = 1024;
-// Control region of a persistent pass in the workspace: go word and error word, then one 128-byte
-// arrival flag per workgroup.
+// Control region of a persistent pass in the workspace: a reserved word and the error word, then
+// one 128-byte arrival flag per workgroup.
 constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
 int pass_max_rows(int mode);   // most rows a persistent pass takes in this mode
