@@ -210,12 +210,11 @@ __device__ __forceinline__ void dma_to_lds_sc1(const void* g, uint32_t lds_addr)
 
 // LDS barriers every wave executes at a stage boundary:
 //   A partials parked |
-//   W4A16 grid barrier: B outputs stored | C all arrivals seen | D (kept: the streaming waves
-//   count these barriers) |
+//   W4A16 grid barrier: B outputs stored | C all arrivals seen |
 //   staging: W4A16 G activations in LDS; W4A4 E statistics | F row parameters | G codes in LDS
 // and the staging barriers once before the first stage.  The last stage ends after A.
 // Streaming waves only pass through them.
-constexpr int kGridBarriers = 3;
+constexpr int kGridBarriers = 2;
 template <int MODE>
 constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
 
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       while (true) {
         lds_barrier();  // A
         if (cs + 1 >= a.n_stages) { cs = a.n_stages; return; }
-        if constexpr (MODE == 0) static_for<0, kGridBarriers>([&](auto) { lds_barrier(); });  // B C D
+        if constexpr (MODE == 0) static_for<0, kGridBarriers>([&](auto) { lds_barrier(); });  // B C
         static_for<0, kStagingBarriers<MODE>>([&](auto) { lds_barrier(); });
         if (__builtin_amdgcn_readfirstlane(fail_sh)) { cs = a.n_stages; return; }
         ++cs;
@@ -645,7 +644,6 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         for (int t = ct; t < grid; t += kCT)
           if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
         lds_barrier();  // C
-        lds_barrier();  // D
       }
     }
   }
