@@ -19,7 +19,9 @@ bytes per pass / verify-pass time), plus draft-pass rates, accept positions/s,
 the roofline of the dominant kernel (the persistent W4A4 pass kernel: the three
 draft passes take most of a step) and of the W4A16 verify pass kernel, each
 timed with HIP events around graph replays of one pass, and the CPU oracle
-baseline.
+baseline.  Per-call distributions (mean, median, p10, p90) are given for 100
+replays of the verify phase and for the accept kernels, warm (logits just read)
+and cold (L2 and MALL flushed by a 512 MiB write before each call).
 """
 
 from __future__ import annotations
@@ -270,6 +272,32 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    # Per-call HIP events: mean, median, p10 and p90 in us over `reps` calls.  `before` (untimed, on the
+    # same stream) runs ahead of each call, e.g. a 512 MiB write that evicts the inputs from L2 and MALL.
+    def time_dist(fn, reps=100, before=None):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            if before is not None:
+                before()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        return {"reps": reps, "mean_us": float(t.mean()), "median_us": float(np.median(t)),
+                "p10_us": float(np.percentile(t, 10)), "p90_us": float(np.percentile(t, 90))}
+
+    verify_dist = time_dist(runners[1], reps=100)
+    log(f"verify phase over 100 replays: median {verify_dist['median_us']:.1f} us, "
+        f"p10 {verify_dist['p10_us']:.1f}, p90 {verify_dist['p90_us']:.1f}")
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(1)  # noqa: E731
+    # A spin kernel that touches no memory keeps the GPU busy while the host marshals the next call, so
+    # a warm call's events bracket its kernels rather than the host's launch latency.
+    spin = lambda: torch.cuda._sleep(200_000)  # noqa: E731
+
     accept = {}
     for (B, G) in ((1, GAMMA), (16, 7)):
         tg = torch.from_numpy(W.logits(rng, (B, G + 1, V), sigma=5.24)).to(dev)
@@ -288,8 +316,16 @@ def main():
             "greedy_us": tgms * 1e3, "greedy_positions_per_s": pos / (tgms * 1e-3),
             "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
             "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
+            # per-call distributions: warm (logits just read, as in the pipeline) and cold (L2 and
+            # MALL flushed by a 512 MiB write before each call)
+            "greedy_warm": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), before=spin),
+            "greedy_cold": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), reps=30, before=flush),
+            "sample_warm": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), before=spin),
+            "sample_cold": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), reps=30,
+                                     before=flush),
         }
         del tg, dr, wsg
+    del flush_buf
 
     # tree-shaped greedy verify: 16 sequences x 8-node random trees (parent uniform over earlier
     # nodes; a node's token is its parent's Top-1 with probability 0.96), V = 128256
@@ -491,6 +527,7 @@ def main():
         },
         "hbm_frac": verify_gbs / HBM_PEAK_GBS,
         "verify_pass_ms": verify_ms,
+        "verify_phase_dist": verify_dist,
         "draft_pass_ms": draft_ms / GAMMA,
         "draft_pass_GBps": draft_gbs,
         "accept_phase_ms": accept_ms,
