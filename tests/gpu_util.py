@@ -13,8 +13,8 @@ PROB_ABS = 1e-5
 # u = 2^-11) on both sides.  Once the two sides differ by any rounding, a value near
 # an fp16 rounding boundary lands one ulp (2u) apart; such flips enter every stage
 # and add up like a random walk, so the end-to-end relative error of a chain grows
-# as about 2u * sqrt(n).  Each single stage is still held to REL_FRO / MAX_ABS when
-# it is fed the GPU's own input (see the chain tests).
+# as about 2u * sqrt(n).  The oracle always runs the whole chain from the shared
+# inputs; no GPU output is fed back into it.
 FP16_U = 2.0 ** -11
 
 
