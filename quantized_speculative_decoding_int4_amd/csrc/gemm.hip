@@ -52,8 +52,9 @@ static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
 // 16-row tiles per workgroup (measured over the Llama-3-8B-shaped stack at M = 16...128): the
 // smallest tile that covers M up to 32 rows, 32 rows beyond that (64-row tiles, where each expanded
 // weight fragment feeds four MFMAs, measured slower in both modes: W4A16 M = 64 4.26 ms per pass
-// against 3.66, M = 128 5.37 against 5.15), except for vocabulary-wide linears, where 64 rows
-// halve the weight re-reads.
+// against 3.66; M = 128 5.41 against 4.98 (W4A16) and 5.13 against 4.21 (W4A4); M = 96 5.32 against
+// 4.86 and 5.09 against 4.09), except for vocabulary-wide linears, where 64 rows halve the weight
+// re-reads.
 static int gemm_mt(int M, int N) {
   if (M <= 16) return 1;
   if (M <= 32) return 2;
