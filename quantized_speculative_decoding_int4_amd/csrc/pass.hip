@@ -1,7 +1,8 @@
 // Persistent pass kernel: one launch runs up to kMaxStages linears of a chain
 // (the W4A4 draft pass at M = batch rows or the W4A16 verify pass at M = 4 rows,
 // [P3] "draft modelとtarget modelの処理フロー"; modes from [P1] "QSpec の W4A4
-// モードと W4A16 モード").
+// モードと W4A16 モード"; W4A8 from [P2] "3.中核となる技術的要素").  The integer modes W4A4
+// and W4A8 share one kernel body and differ only in the activation code range (7 or 127).
 //
 // Why persistent: at decode sizes a linear moves 2-60 MB of weights, so a
 // stand-alone launch spends a large share of its time ramping up and draining
@@ -17,7 +18,7 @@
 // device-coherent loads (both go past the per-XCD L2 to memory), so no L2
 // write-back or invalidate is needed (an agent-scope release/acquire costs about
 // 3.5 us per boundary on MI355X).  Two ways to know the input is complete:
-//  * W4A4 (one row, 8-28 KiB of input): the data carries the signal.  The output
+//  * W4A4 and W4A8 (one row, 8-28 KiB of input): the data carries the signal.  The output
 //    buffers start filled with the pattern 0xFFFF (a NaN the epilogue never
 //    emits: it rewrites that one pattern as the canonical NaN 0x7E00).  A
 //    consumer fetches its input as soon as its own stage is done and reads again
@@ -217,6 +218,9 @@ __device__ __forceinline__ void dma_to_lds_sc1(const void* g, uint32_t lds_addr)
 constexpr int kGridBarriers = 2;
 template <int MODE>
 constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
+// Largest activation code of the integer modes: 7 (W4A4, INT4 codes), 127 (W4A8, INT8 codes).
+template <int MODE>
+constexpr int kPassQmax = MODE == 2 ? 127 : 7;
 
 // W4A16 grid barrier between stages, free of contended atomics: workgroup b stores the epoch into
 // its own flag (one 128-byte line each) once its outputs are acknowledged, and the control threads
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         row_b[m] = inv;
         const float amax = norm ? fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)))
                                 : fmaxf(xmax, -xmin);
-        row_c[m] = h2f(f2h(amax / 7.0f));
+        row_c[m] = h2f(f2h(amax / (float)kPassQmax<MODE>));
       }
     }
     lds_barrier();  // F
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
           uint4 w = v[j];
           if (norm) w = norm_block8(w, mu, inv);
           uint2 op, lg;
-          quant_block8(w, sc, op, lg);
+          quant_block8<kPassQmax<MODE>>(w, sc, op, lg);
           *reinterpret_cast<uint2*>(xq + j * (pstride / 2)) = op;
         }
       }
@@ -676,13 +680,13 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);  // control threads per input row
   for (int i = 0; i < n; ++i) {
     if ((size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1) > kPassLdsStage) return false;
-    if (mode == QS_W4A4 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
+    if (mode != QS_W4A16 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
     if (pick_pass_split(c[i].N, c[i].K, grid) < 0) return false;
   }
   return true;
 }
 
-int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : mode == QS_W4A4 ? 1 : 0; }
+int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : (mode == QS_W4A4 || mode == QS_W4A8) ? 1 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   size_t b = 0;
@@ -718,8 +722,11 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   const int grid = di->num_cus;
   auto fn0 = pass_kernel<0>;
   auto fn1 = pass_kernel<1>;
-  const void* fn = mode == QS_W4A16 ? reinterpret_cast<const void*>(fn0) : reinterpret_cast<const void*>(fn1);
-  static int lds_set[2] = {0, 0};
+  auto fn2 = pass_kernel<2>;
+  const void* fn = mode == QS_W4A16 ? reinterpret_cast<const void*>(fn0)
+                   : mode == QS_W4A4 ? reinterpret_cast<const void*>(fn1)
+                                     : reinterpret_cast<const void*>(fn2);
+  static int lds_set[3] = {0, 0, 0};
   if (!lds_set[mode]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPassLdsStage) != hipSuccess)
       return QS_ERR_HIP;
@@ -736,7 +743,7 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   // Stage outputs of the whole pass -> kEmpty, error word -> 0.
   const size_t sb = pass_stage_bytes(M, c, n);
   if (sb > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
-  const uint32_t n16 = mode == QS_W4A4 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
+  const uint32_t n16 = mode != QS_W4A16 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
   const unsigned rblocks = n16 == 0 ? 1u : (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024u;
   hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks), dim3(256), 0, st, reinterpret_cast<uint4*>(stage_out),
                      n16, ctrl, mode == QS_W4A16 ? grid : 0);
@@ -788,8 +795,10 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     }
     if (mode == QS_W4A16)
       hipLaunchKernelGGL(pass_kernel<0>, dim3(grid), dim3(kPThreads), lds, st, a);
-    else
+    else if (mode == QS_W4A4)
       hipLaunchKernelGGL(pass_kernel<1>, dim3(grid), dim3(kPThreads), lds, st, a);
+    else
+      hipLaunchKernelGGL(pass_kernel<2>, dim3(grid), dim3(kPThreads), lds, st, a);
     rc = launch_status();
     if (rc != QS_OK) return rc;
   }

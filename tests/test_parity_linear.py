@@ -312,7 +312,7 @@ def test_chain_with_vocabulary_wide_head(qs, mode, m):
     assert_linear_close(y, ref, f"chain wide head mode={mode} m={m}")
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     """75 linears.  At M <= 4 (W4A16) / M = 1 (W4A4) the persistent pass splits
     them over two launches (at most 72 per launch), so the hand-over at the seam (fp16 activations in
@@ -332,7 +332,7 @@ def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     persistent = (m <= 4) if mode == 0 else (m <= 1)
     assert chain.pass_launches(mode, m) == (2 if persistent else 0)
     y = host(qs.qs_chain_forward(mode, dev(x), chain))
-    name = "w4a16" if mode == 0 else "w4a4"
+    name = MODE_NAMES[mode]
     ref = O.chain_forward(name, x, layers)
     rel, mx = linear_errors(y, ref)
     tol = chain_rel_tolerance(len(layers))
@@ -469,7 +469,7 @@ def test_full_stack_against_the_oracle(qs, mode, m):
         del q, s
         layers.append((wp, sp, n, k))
     chain = qs.Chain(layers)
-    persistent_rows = {0: 4, 1: 1, 2: 0}[mode]  # W4A8 always runs one launch per linear
+    persistent_rows = {0: 4, 1: 1, 2: 1}[mode]
     assert chain.pass_launches(mode, m) == (0 if m > persistent_rows else 2)
     x = W.activations(W.rng_for(31), m, W.HIDDEN)[0]
     logits = host(qs.qs_chain_forward(mode, dev(x), chain))
