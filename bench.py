@@ -440,6 +440,14 @@ def main():
         qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
     target_ms = time_calls(g1.replay, reps=10)
     del g1, ws1
+    # the same one-row pass in W4A8 (8-bit activation codes on the same int8 MFMA), as a draft
+    ws8 = torch.empty(chain.workspace_bytes(qs.QS_W4A8, 1), dtype=torch.uint8, device=dev)
+    qs.qs_chain_forward(qs.QS_W4A8, x1, chain, out=o1, ws=ws8)
+    g8 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g8):
+        qs.qs_chain_forward(qs.QS_W4A8, x1, chain, out=o1, ws=ws8)
+    w4a8_draft_ms = time_calls(g8.replay, reps=10)
+    del g8, ws8
     t_draft1 = draft_ms / GAMMA
     spec = {
         "alpha": ALPHA, "gamma": GAMMA,
@@ -448,6 +456,8 @@ def main():
         "modelled_speedup": PL.modelled_speedup(ALPHA, GAMMA, target_ms, t_draft1, verify_ms, accept_ms),
         "itl_ms": PL.inter_token_latency(ALPHA, GAMMA, ms_step),
         "target_itl_ms": target_ms,
+        "w4a8_draft_pass_ms": w4a8_draft_ms,
+        "w4a8_draft_persistent_launches": chain.pass_launches(qs.QS_W4A8, 1),
     }
     # per batch: draft step = W4A4 pass at M = B (B = 1: the draft pass above), verify = W4A16 pass at
     # M = B (gamma + 1), both from the sweep; accept / Top-1 costs (tens of us) left out
