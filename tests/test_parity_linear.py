@@ -341,31 +341,33 @@ def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     assert rel <= tol and mx <= 10.0 * tol * rms, f"long chain mode={mode} m={m}: rel_fro={rel:.3e} max_abs={mx:.3e}"
 
 
-def test_barrier_timeout_is_reported_and_cleared(qs):
-    """A zero barrier time-out makes the first grid-barrier wait of a persistent
-    pass fail at once: every workgroup exits (no hang), the time-out word is
-    reported; the next call with the normal limit clears it and is correct."""
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1)])
+def test_barrier_timeout_is_reported_and_cleared(qs, mode, m):
+    """A zero time-out makes the first wait of a persistent pass fail at once (W4A16: the grid
+    barrier; W4A4 and W4A8: the poll for the next stage's input): every workgroup exits (no hang),
+    the time-out word is reported; the next call with the normal limit clears it and is correct."""
+    print(f"time-out mode={mode} m={m}", flush=True)
     rng = W.rng_for(950)
     shapes = [(384, 256), (256, 384), (512, 256)]
     layers = [W.int4_weights(rng, n, k) for n, k in shapes]
-    x, _ = W.activations(rng, 4, 256)
+    x, _ = W.activations(rng, m, 256)
     packed = []
     for q, sc in layers:
         wp, sp = _pack(qs, q, sc)
         packed.append((wp, sp, q.shape[0], q.shape[1]))
     chain = qs.Chain(packed)
-    assert chain.pass_launches(0, 4) == 1
-    ws = torch.zeros(chain.workspace_bytes(0, 4), dtype=torch.uint8, device="cuda")
+    assert chain.pass_launches(mode, m) == 1
+    ws = torch.zeros(chain.workspace_bytes(mode, m), dtype=torch.uint8, device="cuda")
     xd = dev(x)
     qs.qs_set_barrier_timeout_us(0)
     try:
-        qs.qs_chain_forward(0, xd, chain, ws=ws)
-        assert qs.qs_chain_pass_status(0, 4, chain, ws)
+        qs.qs_chain_forward(mode, xd, chain, ws=ws)
+        assert qs.qs_chain_pass_status(mode, m, chain, ws)
     finally:
         qs.qs_set_barrier_timeout_us(200000)
-    y = host(qs.qs_chain_forward(0, xd, chain, ws=ws))
-    assert not qs.qs_chain_pass_status(0, 4, chain, ws)
-    assert_linear_close(y, O.chain_forward("w4a16", x, layers), "chain after a time-out")
+    y = host(qs.qs_chain_forward(mode, xd, chain, ws=ws))
+    assert not qs.qs_chain_pass_status(mode, m, chain, ws)
+    assert_linear_close(y, O.chain_forward(MODE_NAMES[mode], x, layers), "chain after a time-out")
 
 
 
