@@ -57,8 +57,8 @@ def dequantize_weights(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     128-wide group that k falls in, within the same output row n.
     """
     n, k, g = _check_weights(q, s)
-    scale_per_k = np.repeat(s.astype(np.float64), GROUP, axis=1)  # [N, K]
-    return q.astype(np.float64) * scale_per_k
+    w = q.astype(np.float64).reshape(n, g, GROUP) * s.astype(np.float64)[:, :, None]
+    return w.reshape(n, k)
 
 
 def linear_w4a16(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
@@ -111,23 +111,39 @@ def group_accumulators(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
     The integer dot products that an int8 matrix engine accumulates in i32.
     Reading: the sums are per 128-wide group, because each group carries its
     own weight scale; a whole-K integer sum would mix scales.
+    The products are formed in float64 and summed by the matrix routine: every
+    product (|xq * q| <= 128 * 8) and every partial sum (|.| <= 128 * 1024 <
+    2**53) is an integer that float64 holds exactly, so the result is the exact
+    integer sum whatever order the routine adds in.
     """
     m, k = xq.shape
     n, k2 = q.shape
     assert k == k2 and k % GROUP == 0
+    assert np.abs(xq.astype(np.int64)).max(initial=0) <= 128
     g = k // GROUP
-    xg = xq.astype(np.int64).reshape(m, g, GROUP)
-    qg = q.astype(np.int64).reshape(n, g, GROUP)
+    xg = xq.astype(np.float64).reshape(m, g, GROUP)
+    qg = q.astype(np.float64).reshape(n, g, GROUP)
     acc = np.empty((m, n, g), dtype=np.int64)
     for gi in range(g):
-        acc[:, :, gi] = xg[:, gi, :] @ qg[:, gi, :].T
+        acc[:, :, gi] = (xg[:, gi, :] @ qg[:, gi, :].T).astype(np.int64)
     return acc
+
+
+def integer_output(xq: np.ndarray, sx: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """y[m, n] = s_m * sum_g s[n, g] * acc[m, n, g] = s_m * sum_k xq[m, k] * q[n, k] * s[n, k/128],
+    float64.  Written as the second form (one matrix product with the dequantized weights).  Every
+    term xq * q * s is exact in float64 (at most 8 + 4 + 11 significant bits); every partial sum,
+    and the product with s_m (11 bits), stays below 2**53 units of the smallest term's last bit
+    while log2(K / 128) + (binades spanned by the row's scales) <= 13 -- K <= 16384 with scales in
+    [0.005, 0.02] (2 binades) is well inside -- so the result is the exact value of either form,
+    whatever order the matrix routine adds in."""
+    return sx.astype(np.float64)[:, None] * (xq.astype(np.float64) @ dequantize_weights(q, s).T)
 
 
 def linear_w4a4(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
     """W4A4 mode: quantize activations per token, integer group sums, rescale.
 
-      y[m, n] = s_m * sum_g s[n, g] * acc[m, n, g]     (float64)
+      y[m, n] = s_m * sum_g s[n, g] * acc[m, n, g]     (float64, exact: integer_output)
 
     Returns dict(xq, sx, acc, y).  [P1] "W4A4" section: both weights and the
     activations are 4-bit, so a dedicated integer kernel can be used.
@@ -135,9 +151,7 @@ def linear_w4a4(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
     _check_weights(q, s)
     xq, sx = quantize_activations(x)
     acc = group_accumulators(xq, q)
-    per_group = acc.astype(np.float64) * s.astype(np.float64)[None, :, :]
-    y = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
-    return {"xq": xq, "sx": sx, "acc": acc, "y": y}
+    return {"xq": xq, "sx": sx, "acc": acc, "y": integer_output(xq, sx, q, s)}
 
 
 # --------------------------------------------------------------------------
@@ -176,9 +190,7 @@ def linear_w4a8(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> dict:
     _check_weights(q, s)
     xq, sx = quantize_activations_int8(x)
     acc = group_accumulators(xq, q)
-    per_group = acc.astype(np.float64) * s.astype(np.float64)[None, :, :]
-    y = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
-    return {"xq": xq, "sx": sx, "acc": acc, "y": y}
+    return {"xq": xq, "sx": sx, "acc": acc, "y": integer_output(xq, sx, q, s)}
 
 
 def lm_head(mode: str, x: np.ndarray, q: np.ndarray, s: np.ndarray,
@@ -198,41 +210,66 @@ def lm_head(mode: str, x: np.ndarray, q: np.ndarray, s: np.ndarray,
         if mode == "w4a16":
             out[:, lo:hi] = linear_w4a16(x, q[lo:hi], s[lo:hi])
         elif mode in ("w4a4", "w4a8"):
-            acc = group_accumulators(xq, q[lo:hi])
-            per_group = acc.astype(np.float64) * s[lo:hi].astype(np.float64)[None]
-            out[:, lo:hi] = sx.astype(np.float64)[:, None] * per_group.sum(axis=2)
+            out[:, lo:hi] = integer_output(xq, sx, q[lo:hi], s[lo:hi])
         else:
             raise ValueError(mode)
     return out
 
 
-def standardize_rows(y: np.ndarray) -> np.ndarray:
-    """Row-wise (y - mean) / std over the columns given (population std), then
-    rounded to fp16; a row with zero spread maps to zeros.  float64 arithmetic.
+def standardize_rows_exact(v: np.ndarray) -> np.ndarray:
+    """Row-wise (v - mean) / std over the columns given (population std), in
+    float64 and NOT rounded; a row with zero spread maps to zeros.
 
     Reading (the pages give no layer internals): this stands in for the
     normalisation between the linears of the synthetic stack, like a layer norm
     without learned affine parameters.  It keeps activations well scaled over
     many stages for weight codes uniform on [-8, 7], whose mean of -0.5 would
     otherwise amplify the all-ones direction stage after stage."""
-    y64 = np.asarray(y, dtype=np.float64)
-    mu = y64.mean(axis=1, keepdims=True)
-    sd = np.sqrt(((y64 - mu) ** 2).mean(axis=1, keepdims=True))
-    out = np.zeros_like(y64)
+    v64 = np.asarray(v, dtype=np.float64)
+    mu = v64.mean(axis=1, keepdims=True)
+    sd = np.sqrt(((v64 - mu) ** 2).mean(axis=1, keepdims=True))
+    out = np.zeros_like(v64)
     ok = sd[:, 0] > 0
-    out[ok] = (y64[ok] - mu[ok]) / sd[ok]
-    return out.astype(np.float16)
+    out[ok] = (v64[ok] - mu[ok]) / sd[ok]
+    return out
 
 
-def chain_forward(mode: str, x: np.ndarray, layers) -> np.ndarray:
+def standardize_rows(v: np.ndarray) -> np.ndarray:
+    """standardize_rows_exact, then rounded to fp16 (round to nearest even,
+    directly from float64): the 16-bit input that the integer modes quantize."""
+    return standardize_rows_exact(v).astype(np.float16)
+
+
+def _by_column_chunks(fn, n: int, workers: int, chunk: int = 2048) -> np.ndarray:
+    """[M, n] result of fn(lo, hi) (the output columns lo..hi-1) evaluated chunk by chunk, `workers`
+    chunks at a time on threads.  Each output column is computed by the same definition whatever
+    the chunk, so the chunking only bounds memory and time."""
+    spans = [(lo, min(n, lo + chunk)) for lo in range(0, n, chunk)]
+    if workers <= 1 or len(spans) == 1:
+        return np.concatenate([fn(lo, hi) for lo, hi in spans], axis=1)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return np.concatenate(list(ex.map(lambda sp: fn(*sp), spans)), axis=1)
+
+
+def chain_forward(mode: str, x: np.ndarray, layers, workers: int = 1) -> np.ndarray:
     """One forward pass of a stack of quantized linears in one mode.
 
     Reading for the synthetic stack (the pages give no layer internals):
-    stage 0 reads x; stage i > 0 reads the first K_i columns of the previous
-    stage's output, kept as fp16 and standardised per row (standardize_rows);
-    the last stage's output is returned unrounded.  layers: sequence of (q, s).
+    stage 0 reads x; stage i > 0 reads v = the first K_i columns of the
+    previous stage's output, kept as fp16 (rounded to nearest even from the
+    float64 value), and standardises each row of v; the last stage's output is
+    returned unrounded (float64).  layers: sequence of (q, s).
+      * W4A16 (verify): the 16-bit activations entering the product are the
+        fp16 stage outputs v themselves; the row standardisation is an affine
+        map of each row, applied exactly (standardize_rows_exact, no rounding):
+            y[m, n] = sum_k ((v[m, k] - mu_m) / sd_m) * W[n, k]
+      * W4A4 / W4A8 (draft): the standardised row is rounded to fp16
+        (standardize_rows) and that 16-bit row is quantized per token as in
+        the single linear of the mode.
     [P3] "draft modelとtarget modelの処理フロー": a pass scores all of its rows
-    (candidate positions) at once.
+    (candidate positions) at once.  workers > 1 evaluates each stage's output
+    columns in chunks on that many threads (same values, see _by_column_chunks).
     """
     cur = x
     n_layers = len(layers)
@@ -240,15 +277,14 @@ def chain_forward(mode: str, x: np.ndarray, layers) -> np.ndarray:
     for i, layer in enumerate(layers):
         q, s = layer[0], layer[1]
         k = q.shape[1]
-        xin = np.ascontiguousarray(cur[:, :k])
-        if i > 0:
-            xin = standardize_rows(xin)
+        v = np.ascontiguousarray(cur[:, :k])
         if mode == "w4a16":
-            y = linear_w4a16(xin, q, s)
-        elif mode == "w4a4":
-            y = linear_w4a4(xin, q, s)["y"]
-        elif mode == "w4a8":
-            y = linear_w4a8(xin, q, s)["y"]
+            z = v.astype(np.float64) if i == 0 else standardize_rows_exact(v)
+            y = _by_column_chunks(lambda lo, hi: z @ dequantize_weights(q[lo:hi], s[lo:hi]).T, q.shape[0], workers)
+        elif mode in ("w4a4", "w4a8"):
+            z16 = v if i == 0 else standardize_rows(v)
+            xq, sx = (quantize_activations if mode == "w4a4" else quantize_activations_int8)(z16)
+            y = _by_column_chunks(lambda lo, hi: integer_output(xq, sx, q[lo:hi], s[lo:hi]), q.shape[0], workers)
         else:
             raise ValueError(mode)
         if i + 1 < n_layers:

@@ -297,3 +297,25 @@ def test_w4a8_is_closer_to_w4a16_than_w4a4():
     e8 = np.linalg.norm(O.linear_w4a8(x, q, s)["y"] - ref)
     e4 = np.linalg.norm(O.linear_w4a4(x, q, s)["y"] - ref)
     assert e8 < e4 / 8
+
+
+def test_integer_output_equals_the_group_sum_form_exactly():
+    """The oracle's W4A4 / W4A8 output (one product with the dequantized weights) equals the
+    per-group form s_m * sum_g s[n, g] * acc[m, n, g] summed with exact rationals, bit for bit: the
+    float64 evaluation is exact for these magnitudes, so any summation order gives it."""
+    rng = W.rng_for(22)
+    q, s = W.int4_weights(rng, 6, 1024)
+    x, _ = W.activations(rng, 3, 1024)
+    for r in (O.linear_w4a4(x, q, s), O.linear_w4a8(x, q, s)):
+        for m in range(3):
+            for n in range(6):
+                tot = sum(Fraction(float(s[n, g])) * int(r["acc"][m, n, g]) for g in range(8))
+                assert Fraction(float(r["y"][m, n])) == tot * Fraction(float(r["sx"][m]))
+
+
+def test_dequantized_weights_group_mapping():
+    q = np.arange(-8, 8, dtype=np.int8).repeat(32).reshape(2, 256)
+    s = np.array([[1.0, 2.0], [4.0, 0.5]], np.float16)
+    w = O.dequantize_weights(q, s)
+    assert w[0, 5] == q[0, 5] * 1.0 and w[0, 130] == q[0, 130] * 2.0
+    assert w[1, 0] == q[1, 0] * 4.0 and w[1, 255] == q[1, 255] * 0.5
