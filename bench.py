@@ -256,6 +256,12 @@ def main():
     draft_gbs = GAMMA * pass_bytes / (draft_ms * 1e-3) / 1e9
     log(f"step {ms_step:.3f} ms (wall {wall / K * 1e3:.3f}); draft {draft_ms:.3f} verify {verify_ms:.3f} "
         f"accept {accept_ms:.3f} ms; verify {verify_gbs:.0f} GB/s, draft {draft_gbs:.0f} GB/s")
+    # a persistent pass whose wait timed out leaves NaN in its output and sets its workspace's time-out word:
+    # such a run is not a measurement
+    for mode, m, ws, name in ((qs.QS_W4A4, 1, ws_draft, "draft"), (qs.QS_W4A16, M_VERIFY, ws_verify, "verify")):
+        if qs.qs_chain_pass_status(mode, m, chain, ws):
+            log(f"the {name} pass reported a wait time-out: results invalid")
+            sys.exit(3)
     n_acc = int(greedy_out["n_accept"].item())
     assert bool(torch.isfinite(logits_p).all()) and bool(torch.isfinite(logits_q).all()), "non-finite logits"
     agree = float((greedy_out["tgt_top1"][:, :GAMMA] == d).float().mean().item())

@@ -82,7 +82,8 @@ int qs_pack_weights(const int8_t* q, const uint16_t* s, int N, int K,
  * qs_linear_w4a16 -- verify-mode linear ([P1] "W4A16"): 4-bit weights are
  * expanded inside the kernel and multiplied with fp16 activations on fp16
  * MFMA with fp32 accumulation; each 128-wide group's partial sum is scaled in
- * fp32.
+ * fp32 (every row count: the products are exact, only the fp32 summation
+ * order differs from the definition).
  *   x  fp16 [M][K];  y  fp32 [M][N] (out):  y[m][n] = sum_k x[m][k] * W[n][k]
  */
 int qs_linear_w4a16(const uint16_t* x, const uint8_t* w_packed,
@@ -106,7 +107,10 @@ size_t qs_linear_workspace_bytes(int mode, int M, int N, int K);
  * xq = 0), then multiplied with the weight codes on int8 MFMA with i32
  * accumulation per 128-wide group:
  *     acc[m][n][g] = sum_{k in g} xq[m][k] * q[n][k]
- *     y[m][n]      = s_m * sum_g s[n][g] * acc[m][n][g]        (fp32)
+ *     y[m][n]      = s_m * sum_g s[n][g] * acc[m][n][g]
+ * The group sums are exact i32; y is formed in fp64, where every term and sum
+ * is exact while log2(K/128) + (binades spanned by row n's scales) <= 17 (13
+ * for W4A8), and rounded once to fp32: y is the exact value correctly rounded.
  *   x        fp16 [M][K];  y fp32 [M][N] (out)
  *   xq_out   optional int8 [M][K]   (NULL: not written)
  *   sx_out   optional fp16 [M]      (NULL: not written)
@@ -192,12 +196,21 @@ size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, in
  * in a single pass ([P3] "draft modelとtarget modelの処理フロー"; [P1] mode tree).
  * The pages give no layer internals, so the chain is linears only:
  *   stage 0 reads x fp16 [M][chain[0].K];
- *   stage i > 0 reads the first chain[i].K columns (row stride chain[i-1].N) of
- *     stage i-1's output, kept as fp16(y) in the workspace, and
- *     standardises each row over those columns, fp16((v - mean) / std) with the
+ *   stage i > 0 reads v = the first chain[i].K columns (row stride
+ *     chain[i-1].N) of stage i-1's output, kept as fp16 in the workspace, and
+ *     standardises each row of v over those columns, (v - mean) / std with the
  *     population std (rows with zero spread become zeros), standing in for the
  *     normalisation between real layers (requires chain[i].K <= chain[i-1].N);
  *   the last stage writes fp32 out [M][chain[n-1].N].
+ * Arithmetic, the same for every row count and launch configuration:
+ *   W4A16: the fp16 rows v are the 16-bit activations of the product; the
+ *     standardisation is folded into the epilogue, y = (sum_k v w - mean *
+ *     sum_k w) / std, with fp32 row statistics; a stage output is fp16(y).
+ *   W4A4, W4A8: the standardised row is rounded to fp16 (statistics and value
+ *     in fp64, one correct rounding) and quantized as in the single linear;
+ *     y is exact (see qs_linear_w4a4) and rounded once to the fp16 stage
+ *     output or the fp32 result -- every code, group sum and stage value is
+ *     the float64 definition's own.
  * With chain = n_layers x {q|k|v, o, gate|up, down} + LM-head this is the
  * Llama-shaped pass: o reads the q columns, down reads the gate columns.
  *   ws  >= qs_chain_workspace_bytes(mode, M, chain, n) bytes of scratch
@@ -218,11 +231,14 @@ int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n);
 
 /*
  * Wall-clock limit, in microseconds, of every wait inside a persistent pass
- * (W4A16: a grid-barrier wait; W4A4: the wait for one stage's input to be
- * written) (process-wide; default 200000).  A wait that passes it sets
+ * (W4A16: a grid-barrier wait; W4A4 and W4A8: the wait for one stage's input
+ * to be written) (process-wide; default 200000).  A wait that passes it sets
  * the workspace's time-out word and the workgroup exits, so a pass can never
- * wait forever (its output is then undefined).  0 makes every wait fail at
- * once, which exercises that path.  QS_ERR_INVALID_ARG if us < 0.
+ * wait forever.  The output is then partly or wholly NaN: every value is
+ * either the correct one or NaN (the pass fills its output with NaN before it
+ * starts, and a workgroup writes only after all its waits succeeded), so no
+ * value from an earlier call survives.  0 makes every wait fail at once, which
+ * exercises that path.  QS_ERR_INVALID_ARG if us < 0.
  */
 int qs_set_barrier_timeout_us(int us);
 

@@ -1,10 +1,12 @@
 // Batched linear: the verify pass over many sequences, where the target scores B * (gamma + 1)
 // positions at once ([P3] "draft modelとtarget modelの処理フロー"; modes from [P1] "QSpec の W4A4
 // モードと W4A16 モード"), and every per-linear call from 5 rows (W4A16) or 2 rows (W4A4, W4A8) on.
-// W4A16 expands the INT4 codes to fp16 in registers, multiplies them by their group scale (q s
-// rounded to fp16; exact when s is a power of two) and runs v_mfma_f32_16x16x32_f16 with one fp32
-// accumulator over all of K; the integer modes run v_mfma_i32_16x16x64_i8 on the quantized
-// activations and scale each 128-wide group's exact i32 sum in fp32.
+// W4A16 expands the INT4 codes to fp16 in registers, runs v_mfma_f32_16x16x32_f16 over each
+// 128-wide group and scales the group's fp32 sum by its scale in fp32 (the products are exact, as
+// in the definition); the integer modes run v_mfma_i32_16x16x64_i8 on the quantized activations
+// and scale each group's exact i32 sum in fp64, where every term, every sum of terms and the
+// product with the row scale are exact while log2(K / 128) + the binades spanned by an output row's
+// scales <= 13, so the output is the exact value rounded once.
 //
 // Work split.  A workgroup of 4 waves owns an output tile of MT * 16 rows (MT = 1, 2 or 4 MFMA
 // row tiles) x 256 columns (16 packed row blocks, 4 per wave) over a range of K, one 128-wide group
@@ -30,7 +32,7 @@
 namespace qs {
 
 constexpr int kGemmWaves = 4;
-constexpr int kGemmMaxMt = 4;                   // 16-row MFMA tiles per workgroup: 1, 2 or 4
+constexpr int kGemmMaxMt = 2;                   // 16-row MFMA tiles per workgroup: 1 or 2
 constexpr int kGemmMaxRows = kGemmMaxMt * 16;
 constexpr int kGemmNt = 4;                      // 16-column row blocks per wave
 constexpr int kGemmBlocks = kGemmWaves * kGemmNt;  // row blocks per workgroup (256 columns)
@@ -40,26 +42,29 @@ constexpr int kGemmMaxCounters = 1024;           // split runs have fewer than 2
 constexpr int kGemmStatCounters = 64;            // Top-1 epilogue: one per row block (M <= 256)
 
 // Partial slot of one (K split, output tile) workgroup, device-coherent, read back only by the
-// tile's last-arriving workgroup: the accumulators in register order ([wave][mt][nt][lane] float4),
-// then the column sums of the expanded weights ([wave][nt][16 columns]) and the row sums (sum, sum
-// of squares) of the staged activations ([rows] float2).  Sized for the largest row tile.
-constexpr int kSlotAcc = kGemmWaves * kGemmMaxMt * kGemmNt * 64 * 16;
+// tile's last-arriving workgroup: the accumulators in register order ([wave][mt][nt][lane] float4 or,
+// for the integer modes, double4), then the column sums of the expanded weights ([wave][nt][16
+// columns]) and the row sums (sum, sum of squares) of the staged activations ([rows] float2).
+// Sized for the largest row tile.
+constexpr int kSlotAcc = kGemmWaves * kGemmMaxMt * kGemmNt * 64 * 32;
 constexpr int kSlotCs = kSlotAcc;
 constexpr int kSlotStats = kSlotCs + kGemmWaves * kGemmNt * 16 * 4;
 constexpr int kSlotBytes = kSlotStats + kGemmMaxRows * 8;
 static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
 
-// 16-row tiles per workgroup (measured over the Llama-3-8B-shaped stack at M = 16...128): the
-// smallest tile that covers M up to 32 rows, 32 rows beyond that (64-row tiles, where each expanded
-// weight fragment feeds four MFMAs, measured slower in both modes: W4A16 M = 64 4.26 ms per pass
-// against 3.66; M = 128 5.41 against 4.98 (W4A16) and 5.13 against 4.21 (W4A4); M = 96 5.32 against
-// 4.86 and 5.09 against 4.09), except for vocabulary-wide linears, where 64 rows halve the weight
-// re-reads.
+// 16-row tiles per workgroup: the smallest tile that covers M up to 32 rows, 32 rows beyond that.
+// (64-row tiles measured slower over the Llama-3-8B-shaped stack -- W4A16 M = 64 4.26 ms per pass
+// against 3.66, M = 128 5.41 against 4.98 -- and no longer fit the registers with per-group scaling
+// or fp64 accumulators.)  Rows past 32 are re-read weight tiles that hit the XCD's L2 (see the
+// XCD-aware order below).
 static int gemm_mt(int M, int N) {
-  if (M <= 16) return 1;
-  if (M <= 32) return 2;
-  return N >= 32768 ? 4 : 2;
+  (void)N;
+  return M <= 16 ? 1 : 2;
 }
+// Waves per SIMD the register budget allows: W4A16 and 16-row integer tiles fit three (at most 168
+// registers), the 32-row integer tile's fp64 accumulators and the Top-1 epilogue need two.
+template <int MODE, int MT, bool STATS>
+constexpr int kGemmOcc = (!STATS && (MODE == 0 || MT == 1)) ? 3 : 2;
 
 struct GemmArgs {
   const uint16_t* x;   // W4A16: fp16 activations [M][ldx]
@@ -115,6 +120,28 @@ __device__ __forceinline__ void slot_store1(unsigned char* base, int off, float 
 __device__ __forceinline__ float slot_load1(const unsigned char* base, int off) {
   return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(gemm_rsrc(base), off, 0, kGemmSc1));
 }
+// Accumulators of either width: float4 in 16 bytes, double4 in 32.
+__device__ __forceinline__ void slot_store_acc(unsigned char* base, int idx, float4_t v) { slot_store4(base, idx * 16, v); }
+__device__ __forceinline__ float4_t slot_load_acc(const unsigned char* base, int idx, float4_t) {
+  return slot_load4(base, idx * 16);
+}
+__device__ __forceinline__ void slot_store_acc(unsigned char* base, int idx, double4_t v) {
+  const int4_t* p = reinterpret_cast<const int4_t*>(&v);
+  __builtin_amdgcn_raw_buffer_store_b128(p[0], gemm_rsrc(base), idx * 32, 0, kGemmSc1);
+  __builtin_amdgcn_raw_buffer_store_b128(p[1], gemm_rsrc(base), idx * 32 + 16, 0, kGemmSc1);
+}
+__device__ __forceinline__ double4_t slot_load_acc(const unsigned char* base, int idx, double4_t) {
+  int4_t p[2];
+  p[0] = __builtin_amdgcn_raw_buffer_load_b128(gemm_rsrc(base), idx * 32, 0, kGemmSc1);
+  p[1] = __builtin_amdgcn_raw_buffer_load_b128(gemm_rsrc(base), idx * 32 + 16, 0, kGemmSc1);
+  return __builtin_bit_cast(double4_t, p);
+}
+// Output value of an accumulator: W4A16 as accumulated; the integer modes' exact fp64 value times the
+// row scale, rounded once (to fp32 here, or to fp16 by out16).
+__device__ __forceinline__ float out32(float v, float) { return v; }
+__device__ __forceinline__ float out32(double v, float sx) { return (float)(v * (double)sx); }
+__device__ __forceinline__ uint16_t out16(float v, float) { return f2h(v); }
+__device__ __forceinline__ uint16_t out16(double v, float sx) { return f64_to_f16_rn(v * (double)sx); }
 
 // Sum of the 32 codes q of one lane's fragment (four packed dwords, offset-binary nibbles).
 __device__ __forceinline__ int fragment_code_sum(const uint4 w) {
@@ -125,10 +152,10 @@ __device__ __forceinline__ int fragment_code_sum(const uint4 w) {
   return (int)u - 32 * 8;
 }
 
-// Top-1 epilogue of one output tile (see STATS below); values as stored: acc times the W4A4 row
-// scale (the LM-head takes no standardisation).
-template <int MT>
-__device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const float4_t (&acc)[MT][kGemmNt], int m0,
+// Top-1 epilogue of one output tile (see STATS below); values as stored (out32: the integer modes'
+// row scale applied; the LM-head takes no standardisation).
+template <int MT, typename Acc>
+__device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const Acc (&acc)[MT][kGemmNt], int m0,
                                                    int rb0, int bx, int by, int lane, int wave) {
   constexpr int kRows = MT * 16;
   __shared__ Msi wst[kGemmWaves][kRows];
@@ -144,7 +171,7 @@ __device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const floa
 #pragma unroll
       for (int nt = 0; nt < kGemmNt; ++nt) {
         const int n = (rb0 + nt) * 16 + (lane & 15);
-        if (n < a.N) t = msi_merge(t, Msi{acc[mt][nt][j] * sx, 1.0f, n});
+        if (n < a.N) t = msi_merge(t, Msi{out32(acc[mt][nt][j], sx), 1.0f, n});
       }
       // the 16 lanes holding this row: pairs, quads, halves of 8, rows of 16
       t = msi_merge(t, msi_dpp<0xB1>(t));
@@ -202,9 +229,10 @@ __device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const floa
 // partials in column order into its Top-1 and Top-1 probability 1 / sum exp(v - max).  So a greedy
 // step never reads the logits back.
 template <int MODE, bool NORM, int MT, int D, bool STATS>
-__global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void gemm_kernel(const GemmArgs a) {
   static_assert(MODE == 0 || !NORM, "standardisation is fused for W4A16 only");
   static_assert(!(NORM && STATS), "the Top-1 epilogue serves the stand-alone LM-head");
+  using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
   constexpr int kRows = MT * 16;
   constexpr int kRowB = MODE == 0 ? 256 : 128;  // activation bytes per row and group
   constexpr int kPitch = kRowB + 16;
@@ -310,11 +338,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
     }
   };
 
-  float4_t acc[MT][kGemmNt];
+  Acc acc[MT][kGemmNt];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < kGemmNt; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kGemmNt; ++nt) acc[mt][nt] = Acc{0, 0, 0, 0};
   float csum[kGemmNt];  // NORM: this lane's share of sum_k w for column lane & 15 of each block
 #pragma unroll
   for (int nt = 0; nt < kGemmNt; ++nt) csum[nt] = 0.0f;
@@ -336,8 +364,12 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
         a_load(gi + 1);  // next group's activations, stored after this group's math
         const unsigned char* ab = abuf[cur];
         if constexpr (MODE == 0) {
-          // the group scale is folded into the expanded weights (q s rounded to fp16), so the MFMAs
-          // accumulate across groups directly
+          // each group's exact products summed in fp32 by the MFMAs, then scaled by the group's scale
+          float4_t dg[MT][kGemmNt];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < kGemmNt; ++nt) dg[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < kSteps; ++t) {
             half8_t b[kGemmNt];
@@ -345,15 +377,21 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
             for (int nt = 0; nt < kGemmNt; ++nt) {
               const uint4 wv = wr[i][nt];
               const uint32_t wt = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
-              b[nt] = unpack_f16x8(wt, magic) * __builtin_bit_cast(_Float16, sr[i][nt]);
+              b[nt] = unpack_f16x8(wt, magic);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               const half8_t av = *reinterpret_cast<const half8_t*>(ab + lane_off + mt * 16 * kPitch + 16 * t);
 #pragma unroll
               for (int nt = 0; nt < kGemmNt; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], acc[mt][nt], 0, 0, 0);
+                dg[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], dg[mt][nt], 0, 0, 0);
             }
+          }
+#pragma unroll
+          for (int nt = 0; nt < kGemmNt; ++nt) {
+            const float s = h2f(sr[i][nt]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][nt] += s * dg[mt][nt];
           }
           if constexpr (NORM) {
 #pragma unroll
@@ -384,11 +422,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
           }
 #pragma unroll
           for (int nt = 0; nt < kGemmNt; ++nt) {
-            const float s = h2f(sr[i][nt]) * 0.0625f;  // operands carry 16 q: exact rescale
+            const double s = (double)h2f(sr[i][nt]) * 0.0625;  // operands carry 16 q: exact rescale
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mt][nt][j] += s * (float)dg[mt][nt][j];
+              for (int j = 0; j < 4; ++j) acc[mt][nt][j] += s * (double)dg[mt][nt][j];  // exact in fp64
           }
         }
         w_issue(i, gi + D);  // refill this slot after consuming it
@@ -432,7 +470,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < kGemmNt; ++nt)
-        slot_store4(my, (((wave * MT + mt) * kGemmNt + nt) * 64 + lane) * 16, acc[mt][nt]);
+        slot_store_acc(my, ((wave * MT + mt) * kGemmNt + nt) * 64 + lane, acc[mt][nt]);
     if constexpr (NORM) {
       if (lane < 16) {
 #pragma unroll
@@ -467,9 +505,9 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kGemmNt; ++nt) {
-          const int off = (((wave * MT + mt) * kGemmNt + nt) * 64 + lane) * 16;
-          const float4_t v0 = slot_load4(p0, off), v1 = slot_load4(p1, off);
-          float4_t t = s == 0 ? v0 : acc[mt][nt] + v0;
+          const int idx = ((wave * MT + mt) * kGemmNt + nt) * 64 + lane;
+          const Acc v0 = slot_load_acc(p0, idx, Acc{}), v1 = slot_load_acc(p1, idx, Acc{});
+          Acc t = s == 0 ? v0 : acc[mt][nt] + v0;
           if (two) t += v1;
           acc[mt][nt] = t;
         }
@@ -530,17 +568,22 @@ __global__ __launch_bounds__(kGemmWaves * 64, (MT <= 2 && !STATS) ? 3 : 2) void 
       for (int nt = 0; nt < kGemmNt; ++nt) {
         const int n = (rb0 + nt) * 16 + (lane & 15);
         if (n >= a.N) continue;
-        float v = acc[mt][nt][j];
-        if constexpr (MODE == 1) v *= sx;
-        if constexpr (NORM) v = (v - mu * csum[nt]) * inv;
-        if (a.y16)
-          a.y16[(size_t)m * a.ldy + n] = f2h(v);
-        else if (a.y)
-          a.y[(size_t)m * a.N + n] = v;
+        if constexpr (NORM) {
+          const float v = (acc[mt][nt][j] - mu * csum[nt]) * inv;
+          if (a.y16)
+            a.y16[(size_t)m * a.ldy + n] = f2h(v);
+          else if (a.y)
+            a.y[(size_t)m * a.N + n] = v;
+        } else {
+          if (a.y16)
+            a.y16[(size_t)m * a.ldy + n] = out16(acc[mt][nt][j], sx);
+          else if (a.y)
+            a.y[(size_t)m * a.N + n] = out32(acc[mt][nt][j], sx);
+        }
       }
     }
   }
-  if constexpr (STATS) gemm_top1_epilogue<MT>(a, acc, m0, rb0, bx, by, lane, wave);
+  if constexpr (STATS) gemm_top1_epilogue<MT, Acc>(a, acc, m0, rb0, bx, by, lane, wave);
 }
 
 __global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ cnt, int n) {
@@ -593,17 +636,14 @@ static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D, false>), grid, dim3(kGemmWaves * 64), 0, st, a);
 }
 
-// Weight ring depth per row tile: 16- and 32-row tiles take a 4- and a 2-group ring and three waves per
-// SIMD (2-3% faster over the stack than a 6-group ring with two); 64-row tiles, whose accumulators
-// need more registers, a 4- or 2-group ring and two waves per SIMD.
+// Weight ring depth per row tile: 16-row tiles a 3-group (W4A16, whose per-group sums take registers)
+// or 4-group ring, 32-row tiles a 2-group ring.
 template <int MODE, bool NORM>
 static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st) {
   if (mt == 1)
-    gemm_launch_one<MODE, NORM, 1, 4>(a, grid, st);
-  else if (mt == 2)
-    gemm_launch_one<MODE, NORM, 2, 2>(a, grid, st);
+    gemm_launch_one<MODE, NORM, 1, MODE == 0 ? 3 : 4>(a, grid, st);
   else
-    gemm_launch_one<MODE, NORM, 4, MODE == 0 ? 4 : 2>(a, grid, st);
+    gemm_launch_one<MODE, NORM, 2, 2>(a, grid, st);
 }
 
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,

@@ -8,7 +8,8 @@
 //                   scale applied in fp32 to each 128-wide partial sum.
 //   W4A4  (draft) : activations quantized per token to INT4, codes expanded to
 //                   int8, int8 MFMA (v_mfma_i32_16x16x64_i8) with exact i32
-//                   group sums, fp32 epilogue.  gfx950 has no int4 MFMA.
+//                   group sums, scaled and summed in fp64 (exact) and rounded
+//                   once to the fp32 output.  gfx950 has no int4 MFMA.
 //
 // At decode sizes (M <= 16 rows) the kernel is a weight stream: each 64-lane
 // wave pulls whole 1 KiB tiles (one 16 B global_load_dwordx4 per lane, 1 KiB
@@ -21,6 +22,8 @@
 #include "qs_act.h"
 #include "qs_device.h"
 #include "qs_internal.h"
+
+#include <type_traits>
 
 namespace qs {
 
@@ -75,31 +78,6 @@ int launch_pack(const int8_t* q, const uint16_t* s, int N, int K, uint8_t* wp, u
 // correctly rounded fp32 quotient (exact for the rounding decision: the quotient of two fp16 values
 // is either an exact half-integer tie or at least 2^-13 away from one) and round-half-even rint.
 
-// Stand-alone row standardisation (W4A16 chains at large M): one workgroup per row.
-__global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restrict__ x, int K, int ldx,
-                                                       uint16_t* __restrict__ out) {
-  __shared__ float r0[4], r1[4];
-  __shared__ float mu_sh, inv_sh;
-  const int m = blockIdx.x;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * ldx);
-  const int nb = K / 8;
-  float sum = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-  for (int i = threadIdx.x; i < nb; i += 256) stats_block8(xr[i], sum, sq, mx, mn);
-  sum = wave_sum(sum);
-  sq = wave_sum(sq);
-  if ((threadIdx.x & 63) == 0) { r0[threadIdx.x >> 6] = sum; r1[threadIdx.x >> 6] = sq; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float mu, inv;
-    norm_params(r0[0] + r0[1] + r0[2] + r0[3], r1[0] + r1[1] + r1[2] + r1[3], K, mu, inv);
-    mu_sh = mu;
-    inv_sh = inv;
-  }
-  __syncthreads();
-  uint4* o = reinterpret_cast<uint4*>(out + (size_t)m * K);
-  for (int i = threadIdx.x; i < nb; i += 256) o[i] = norm_block8(xr[i], mu_sh, inv_sh);
-}
-
 // Stand-alone quantizer (INT4 codes for W4A4, QMAX = 7; INT8 codes for W4A8, QMAX = 127): one
 // workgroup of kAqThreads per row (wide, so the serial statistics and quantization of one row
 // are short).  Writes operand-ordered codes and the fp32 value of the fp16 scale to the workspace,
@@ -112,32 +90,37 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint16_t* _
                                                                int8_t* __restrict__ xq_out,
                                                                uint16_t* __restrict__ sx_out) {
   constexpr int kW = kAqThreads / 64;
-  __shared__ float red[4][kW];
-  __shared__ float s_sh, mu_sh, inv_sh;
+  __shared__ double red64[2][kW];
+  __shared__ float red[2][kW];
+  __shared__ float s_sh;
+  __shared__ double mu_sh, inv_sh;
   const int m = blockIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * ldx);
   const int nb = K / 8;
-  float sum = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-  for (int i = threadIdx.x; i < nb; i += kAqThreads) stats_block8(xr[i], sum, sq, mx, mn);
-  sum = wave_sum_dpp(sum);
-  sq = wave_sum_dpp(sq);
+  double sum = 0.0, sq = 0.0;
+  float mx = -INFINITY, mn = INFINITY;
+  for (int i = threadIdx.x; i < nb; i += kAqThreads) stats_block8_64(xr[i], sum, sq, mx, mn);
+  sum = wave_sum_dpp64(sum);
+  sq = wave_sum_dpp64(sq);
   mx = wave_max_dpp(mx);
   mn = wave_min_dpp(mn);
   const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { red[0][w] = sum; red[1][w] = sq; red[2][w] = mx; red[3][w] = mn; }
+  if ((threadIdx.x & 63) == 0) { red64[0][w] = sum; red64[1][w] = sq; red[0][w] = mx; red[1][w] = mn; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float tsum = red[0][0], tsq = red[1][0], xmax = red[2][0], xmin = red[3][0];
+    double tsum = red64[0][0], tsq = red64[1][0];
+    float xmax = red[0][0], xmin = red[1][0];
     for (int j = 1; j < kW; ++j) {  // fixed order
-      tsum += red[0][j];
-      tsq += red[1][j];
-      xmax = fmaxf(xmax, red[2][j]);
-      xmin = fminf(xmin, red[3][j]);
+      tsum += red64[0][j];
+      tsq += red64[1][j];
+      xmax = fmaxf(xmax, red[0][j]);
+      xmin = fminf(xmin, red[1][j]);
     }
-    float mu = 0.f, inv = 0.f, amax;
+    double mu = 0.0, inv = 0.0;
+    float amax;
     if (norm_in) {
-      norm_params(tsum, tsq, K, mu, inv);
-      amax = fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)));
+      norm_params64(tsum, tsq, xmax, xmin, K, mu, inv);
+      amax = fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)));
     } else {
       amax = fmaxf(xmax, -xmin);
     }
@@ -153,7 +136,7 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint16_t* _
   for (int i = threadIdx.x; i < nb; i += kAqThreads) {
     uint2 op, lg;
     uint4 v = xr[i];
-    if (norm_in) v = norm_block8(v, mu_sh, inv_sh);
+    if (norm_in) v = norm_block8_64(v, mu_sh, inv_sh);
     quant_block8<QMAX>(v, s, op, lg);
     *reinterpret_cast<uint2*>(xq_op + (size_t)m * K + 8 * i) = op;
     if (xq_out) *reinterpret_cast<uint2*>(xq_out + (size_t)m * K + 8 * i) = lg;
@@ -204,11 +187,15 @@ struct LinearArgs {
 template <int MODE, int MT, int S, bool XLDS>
 __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   constexpr int R = kNW / S;
+  // W4A16 accumulates in fp32; the integer modes scale their exact i32 group sums in fp64 (exact).
+  using Acc = std::conditional_t<MODE == MODE_W4A16, float4_t, double4_t>;
   extern __shared__ __align__(16) unsigned char dyn_lds[];
-  __shared__ float4_t red[S > 1 ? kNW : 1][64];
-  __shared__ float sx_lds[16];
+  __shared__ Acc red[S > 1 ? kNW : 1][64];
+  __shared__ float sx_lds[16];     // W4A4: row scales; W4A16 with norm_in: row mean [0, 8), 1/std [8, 16)
   __shared__ float amax_red[8][kNW];
+  __shared__ double row64[2][8];   // W4A4 with norm_in: row mean, 1/std (fp64)
   __shared__ __align__(16) uint32_t zero_pad[16];  // A-operand source for lanes beyond M
+  __shared__ __align__(16) uint32_t ones_pad[16];  // W4A16 with norm_in: fp16 1.0 pairs (row sums of W)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -225,7 +212,10 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   const int total = (my_sets * per + kPF - 1) / kPF * kPF;  // padded to whole rings
   const size_t set_stride = (size_t)grid * R * G;              // tiles between consecutive sets
 
-  if (threadIdx.x < 16) zero_pad[threadIdx.x] = 0u;
+  if (threadIdx.x < 16) {
+    zero_pad[threadIdx.x] = 0u;
+    ones_pad[threadIdx.x] = 0x3C003C00u;
+  }
 
   // ---- load cursor (scalar): set index, item within set, tile index
   int l_gi = 0, l_si = 0;
@@ -272,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
           if (lane == 0) { amax_red[r2][wave] = su; amax_red[4 + r2][wave] = sq; }
         }
         __syncthreads();
-        if (threadIdx.x < M) {
+        if (threadIdx.x < M) {  // applied in the epilogue: (sum_k x w - mu sum_k w) * inv
           float su = 0.f, sq = 0.f;
 #pragma unroll
           for (int w = 0; w < kNW; ++w) { su += amax_red[threadIdx.x][w]; sq += amax_red[4 + threadIdx.x][w]; }
@@ -281,52 +271,51 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
           sx_lds[threadIdx.x] = mu;
           sx_lds[8 + threadIdx.x] = inv;
         }
-        __syncthreads();
-        for (int i = threadIdx.x; i < n16; i += kThreads) {
-          const int m = i / per_row;
-          dst[i] = norm_block8(dst[i], sx_lds[m], sx_lds[8 + m]);
-        }
       }
     } else {
       const int nb = K / 8;
-      __shared__ float stat_red[4][8][kNW];
+      __shared__ double stat_sum[2][8][kNW];
+      __shared__ float stat_mm[2][8][kNW];
       for (int m = 0; m < M; ++m) {
         const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.ldx);
-        float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
-        for (int i = threadIdx.x; i < nb; i += kThreads) stats_block8(xr[i], su, sq, mx, mn);
-        su = wave_sum(su);
-        sq = wave_sum(sq);
+        double su = 0.0, sq = 0.0;
+        float mx = -INFINITY, mn = INFINITY;
+        for (int i = threadIdx.x; i < nb; i += kThreads) stats_block8_64(xr[i], su, sq, mx, mn);
+        su = wave_sum_dpp64(su);
+        sq = wave_sum_dpp64(sq);
         mx = wave_max(mx);
         mn = wave_min(mn);
         if (lane == 0) {
-          stat_red[0][m][wave] = su;
-          stat_red[1][m][wave] = sq;
-          stat_red[2][m][wave] = mx;
-          stat_red[3][m][wave] = mn;
+          stat_sum[0][m][wave] = su;
+          stat_sum[1][m][wave] = sq;
+          stat_mm[0][m][wave] = mx;
+          stat_mm[1][m][wave] = mn;
         }
       }
       __syncthreads();
       if (threadIdx.x < M) {
         const int m = threadIdx.x;
-        float su = 0.f, sq = 0.f, xmax = -INFINITY, xmin = INFINITY;
+        double su = 0.0, sq = 0.0;
+        float xmax = -INFINITY, xmin = INFINITY;
 #pragma unroll
         for (int w = 0; w < kNW; ++w) {
-          su += stat_red[0][m][w];
-          sq += stat_red[1][m][w];
-          xmax = fmaxf(xmax, stat_red[2][m][w]);
-          xmin = fminf(xmin, stat_red[3][m][w]);
+          su += stat_sum[0][m][w];
+          sq += stat_sum[1][m][w];
+          xmax = fmaxf(xmax, stat_mm[0][m][w]);
+          xmin = fminf(xmin, stat_mm[1][m][w]);
         }
-        float mu = 0.f, inv = 0.f, amax;
+        double mu = 0.0, inv = 0.0;
+        float amax;
         if (a.norm_in) {
-          norm_params(su, sq, K, mu, inv);
-          amax = fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)));
+          norm_params64(su, sq, xmax, xmin, K, mu, inv);
+          amax = fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)));
         } else {
           amax = fmaxf(xmax, -xmin);
         }
         const uint16_t s16 = f2h(amax / 7.0f);
         sx_lds[m] = h2f(s16);
-        amax_red[0][m] = mu;
-        amax_red[1][m] = inv;
+        row64[0][m] = mu;
+        row64[1][m] = inv;
         if (blockIdx.x == 0 && a.sx_out) a.sx_out[m] = s16;
       }
       __syncthreads();
@@ -334,11 +323,11 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
       for (int m = 0; m < M; ++m) {
         const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.ldx);
         const float s = sx_lds[m];
-        const float mu = amax_red[0][m], inv = amax_red[1][m];
+        const double mu = row64[0][m], inv = row64[1][m];
         for (int i = threadIdx.x; i < nb; i += kThreads) {
           uint2 op, lg;
           uint4 v = xr[i];
-          if (a.norm_in) v = norm_block8(v, mu, inv);
+          if (a.norm_in) v = norm_block8_64(v, mu, inv);
           quant_block8(v, s, op, lg);
           *reinterpret_cast<uint2*>(xq_lds + (size_t)m * K + 8 * i) = op;
           if (blockIdx.x == 0 && a.xq_out)
@@ -349,9 +338,9 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   }
   __syncthreads();
 
-  float4_t acc[MT];
+  Acc acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = Acc{0, 0, 0, 0};
 
   const int arow = lane & 15;       // A-operand row (activation row within a 16-row tile)
   const int kq = 32 * (lane >> 4);  // lane's k offset inside a group
@@ -359,7 +348,10 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
   const uint32_t zero_addr = (uint32_t)(uintptr_t)zero_pad;
   const uint32_t lds_base = (uint32_t)(uintptr_t)dyn_lds;
   constexpr int kElt = MODE == MODE_W4A16 ? 2 : 1;  // bytes per staged activation element
-  const uint32_t a_lane = arow < M ? lds_base + (uint32_t)((arow * K + kq) * kElt) : zero_addr;
+  // W4A16 with norm_in: operand row M reads all-ones, so output row M is sum_k w[n, k] (M <= 4 here)
+  const bool ones_row = MODE == MODE_W4A16 && XLDS && a.norm_in && arow == M;
+  const uint32_t a_lane = arow < M ? lds_base + (uint32_t)((arow * K + kq) * kElt)
+                                   : ones_row ? (uint32_t)(uintptr_t)ones_pad : zero_addr;
   const uint32_t a_step = arow < M ? (uint32_t)(kGroup * kElt) : 0u;  // per group
 
   const uint32_t magic = fp16_magic_vgpr();
@@ -429,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int gsum = dg[mt][j] >> 4;  // operands carry 16 * q: exact
-              acc[mt][j] += s * (float)gsum;
+              acc[mt][j] += (double)s * (double)gsum;  // exact in fp64
               if (a.acc_out) {
                 const int m = mt * 16 + 4 * (lane >> 4) + j;
                 if (m < M && n < N) a.acc_out[((size_t)m * N + n) * G + g] = gsum;
@@ -443,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
         c_gi = 0;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          float4_t v = acc[mt];
+          Acc v = acc[mt];
           if constexpr (S > 1) {
             red[wave][lane] = v;
             __syncthreads();
@@ -455,18 +447,37 @@ __global__ __launch_bounds__(kThreads) void linear_stream_kernel(LinearArgs a) {
           }
           if (sidx == 0 && c_si < my_sets && rb < nrb) {
             const int n = rb * 16 + (lane & 15);
+            float rowsum = 0.f;  // W4A16 with norm_in: sum_k w[n, k] from operand row M
+            if constexpr (MODE == MODE_W4A16 && XLDS) {
+              if (a.norm_in) {
+                const int q = M & 3;
+                const float vq = q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3];
+                rowsum = __shfl(vq, (lane & 15) + 16 * (M >> 2), 64);
+              }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int m = mt * 16 + 4 * (lane >> 4) + j;
               if (m < M && n < N) {
-                float out = v[j];
-                if constexpr (MODE == MODE_W4A4) out *= XLDS ? sx_lds[m] : a.sxf[m];
-                if (a.y16) a.y16[(size_t)m * a.ldy + n] = f2h(out);
+                float out;
+                uint16_t h;
+                if constexpr (MODE == MODE_W4A4) {  // exact product, rounded once
+                  const double o64 = v[j] * (double)(XLDS ? sx_lds[m] : a.sxf[m]);
+                  out = (float)o64;
+                  h = f64_to_f16_rn(o64);
+                } else {
+                  out = v[j];
+                  if constexpr (XLDS) {
+                    if (a.norm_in) out = (out - sx_lds[m] * rowsum) * sx_lds[8 + m];
+                  }
+                  h = f2h(out);
+                }
+                if (a.y16) a.y16[(size_t)m * a.ldy + n] = h;
                 else a.y[(size_t)m * N + n] = out;
               }
             }
           }
-          acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+          acc[mt] = Acc{0, 0, 0, 0};
         }
         ++c_si;
       }
@@ -496,8 +507,8 @@ static bool use_gemm(int mode, int M, const int32_t* acc_out) {
 // staged in memory, then the K-split partials of the batched kernel.  Sized for the case without
 // the per-group accumulator output (it only ever makes the need smaller).
 static size_t staging_bytes(int mode, int M, int K, bool norm_in) {
-  if (mode == QS_W4A16)  // the batched kernel standardises inside the GEMM
-    return (norm_in && !w4a16_lds(M, K) && !use_gemm(mode, M, nullptr)) ? align_up((size_t)M * K * 2, 256) : 0;
+  (void)norm_in;
+  if (mode == QS_W4A16) return 0;  // both W4A16 kernels standardise in their epilogue
   if (mode == QS_W4A4 && w4a4_fused(M, K) && !use_gemm(mode, M, nullptr)) return 0;
   return align_up((size_t)M * K, 256) + align_up((size_t)M * 4, 256);
 }
@@ -530,9 +541,11 @@ static int launch_one(const LinearArgs& a, size_t lds, hipStream_t st) {
     // Raise the dynamic-LDS limit once per instance (before any graph capture uses it).
     static int lds_limit = 0;
     if ((int)lds > lds_limit) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsStage) != hipSuccess)
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMaxLdsStage) != hipSuccess) {
+        (void)hipGetLastError();  // report it here, not at the caller's next HIP call
         return QS_ERR_HIP;
+      }
       lds_limit = (int)kMaxLdsStage;
     }
   }
@@ -563,16 +576,16 @@ static int launch_split(const LinearArgs& a, size_t lds, hipStream_t st) {
   }
 }
 
-// Activation rows per launch of the streaming kernel (larger M is processed in chunks).
-constexpr int kMaxRowsPerLaunch = 128;
+// Activation rows per launch of the streaming kernel (larger M is processed in chunks; 128-row
+// launches would not fit the registers).
+constexpr int kMaxRowsPerLaunch = 64;
 
 template <int MODE>
 static int launch_mt(const LinearArgs& a, hipStream_t st) {
   const int mt = (a.M + 15) / 16;
   if (mt <= 1) return launch_split<MODE, 1, false>(a, 0, st);
   if (mt <= 2) return launch_split<MODE, 2, false>(a, 0, st);
-  if (mt <= 4) return launch_split<MODE, 4, false>(a, 0, st);
-  return launch_split<MODE, 8, false>(a, 0, st);
+  return launch_split<MODE, 4, false>(a, 0, st);
 }
 
 // Rows [m0, m0 + rows) of a linear without LDS staging.
@@ -681,18 +694,11 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   const size_t gws_bytes = ws && ws_bytes > pre + need ? ws_bytes - pre - need : 0;
   if (mode == QS_W4A16) {
     if (w4a16_lds(M, K)) return launch_split<MODE_W4A16, 1, true>(a, (size_t)M * K * 2, st);
-    if (gemm)
+    // the batched kernel also takes the standardised rows that do not fit the LDS stage (it
+    // standardises in its epilogue; without a workspace it does not split K)
+    if (gemm || io.norm_in)
       return launch_gemm(QS_W4A16, io.norm_in != 0, a.x, a.ldx, nullptr, nullptr, wp, sp, M, N, K, a.y, a.y16,
                          a.y16 ? a.ldy : N, cnt, gws, gws_bytes, st);
-    if (io.norm_in) {
-      uint16_t* xn = reinterpret_cast<uint16_t*>(stg);
-      hipLaunchKernelGGL(row_norm_kernel, dim3(M), dim3(256), 0, st, x, K, io.ldx, xn);
-      const int rc = launch_status();
-      if (rc != QS_OK) return rc;
-      a.x = xn;
-      a.ldx = K;
-      a.norm_in = 0;
-    }
     return launch_chunked<MODE_W4A16>(a, st);
   }
   // W4A4 and W4A8 share the integer kernels: only the activation codes' range differs (the fused

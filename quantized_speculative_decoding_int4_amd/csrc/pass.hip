@@ -33,22 +33,29 @@
 //    flags (one round trip; a relay through a `go` word published by workgroup 0
 //    measured 2.4% slower over the verify pass).
 // Every wait has a wall-clock deadline that sets an error word and makes the
-// workgroup exit, so no wave can wait forever.
+// workgroup exit, so no wave can wait forever.  The final output is filled with
+// NaN before the pass starts: a workgroup writes its part of it only after every
+// wait it made succeeded, so after a time-out each output value is either the
+// correct one or NaN -- never a value left from an earlier call.
 //
 // Tile math per stage is the one of linear.hip: a wave's share of a 16-row block
 // (S waves split K), expansion of the nibbles in VGPRs, MFMA with the staged
 // activations as A operand, fp32 group scaling, fixed-order reduction over the
 // S waves through LDS.
 //
-// W4A16 stages take the raw fp16 input and apply the row standardisation after
-// the contraction: with mean mu and 1/std inv of input row m,
+// W4A16 stages take the raw fp16 input (the 16-bit activations of the product)
+// and apply the row standardisation after the contraction: with mean mu and 1/std
+// inv of input row m,
 //   sum_k w[n,k] (x[m,k] - mu) inv = (sum_k w[n,k] x[m,k] - mu sum_k w[n,k]) inv,
 // and sum_k w[n,k] comes for free from an all-ones row placed in the zero padding
 // of the 16-row A operand.  The input therefore goes to LDS as it arrives and its
-// statistics are computed while the contraction runs.  This skips the fp16
-// rounding of the standardised input (a relative 2^-12 per term).  W4A4 stages
-// must quantise the standardised row first, so they stage through registers:
-// statistics, scale, quantisation, then LDS.
+// statistics are computed while the contraction runs.  The integer modes must
+// quantise the standardised row first, so they stage through registers:
+// statistics, scale, quantisation, then LDS -- all exact: fp64 statistics and a
+// correctly rounded fp16 standardised value (qs_act.h), and fp64 group scaling of
+// the exact i32 sums (each term s * acc is exact in fp64, and so are their sums
+// and the product with the row scale while log2(K / 128) + the binades spanned by
+// a row's scales <= 13), rounded once to the fp16 stage output or the fp32 result.
 
 #include "qs_act.h"
 #include "qs_device.h"
@@ -87,7 +94,13 @@ constexpr int kPW = kSW;                   // waves sharing the tiles of a row-b
 constexpr int kCT = 64 * kCW;              // control threads
 constexpr int kPThreads = 64 * (kSW + kCW);
 constexpr int kPRing = QS_PASS_RING;       // tiles in flight per streaming wave (two loads each)
-constexpr size_t kPassLdsStage = 114688;   // activations staged per stage: M * K * element bytes
+constexpr size_t kPassLdsStage = 114688;   // W4A16: activations staged per stage, M * K * 2 bytes
+// Integer modes: their fp64 partials take 64 KiB of static LDS, so the staged codes (M * K bytes)
+// get at most this much dynamic LDS.
+constexpr size_t kPassLdsStageInt = 81920;
+// At least this much dynamic LDS per workgroup: with the static arrays no two workgroups fit on one
+// CU, so the launch spreads one workgroup per CU.
+constexpr size_t kPassLdsMin = 81920;
 constexpr int kPassSlots = 4;              // row-block sets a workgroup may own per stage
 constexpr int kPiecesMax4 = 8;             // W4A4: 16-byte input pieces a control thread holds per stage
 constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
@@ -246,10 +259,14 @@ __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, con
 
 template <int MODE>
 __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
+  // Partials of the streaming waves: fp32 (W4A16) or fp64 (the integer modes: exact sums).
+  using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
   extern __shared__ __align__(16) unsigned char dyn_lds[];
-  __shared__ float4_t red[kPassSlots][kSW][64];  // per-set partials of one stage
-  __shared__ float row_a[8], row_b[8], row_c[8];   // per-row mean, 1/std, W4A4 scale
-  __shared__ float stat_red[4][2 * kCW];           // staging statistics per reduction unit
+  __shared__ Acc red[kPassSlots][kSW][64];         // per-set partials of one stage
+  __shared__ float row_a[8], row_b[8], row_c[8];   // W4A16: per-row mean, 1/std; integer modes: scale
+  __shared__ double row_mu64[8], row_inv64[8];     // integer modes: per-row mean, 1/std (fp64)
+  __shared__ double stat_sum[2][2 * kCW];          // integer staging: fp64 sum, sum of squares per unit
+  __shared__ float stat_mm[2][2 * kCW];            // integer staging: max, min per unit
   __shared__ __align__(16) uint32_t zero_pad[16];
   __shared__ __align__(16) uint32_t ones_pad[16];  // fp16 1.0 pairs: the W4A16 row-sum operand
   __shared__ int fail_sh;
@@ -342,7 +359,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     if (cv.my_sets == 0) next_stage();
 
     const uint32_t magic = fp16_magic_vgpr();
-    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+    Acc acc = Acc{0, 0, 0, 0};
     while (cs < a.n_stages) {
       static_for<0, kPRing>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
@@ -375,15 +392,16 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
                     *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
                 dg = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, dg, 0, 0, 0);
               }
+              const double s16 = (double)s * 0.0625;  // operands carry 16 q: exact rescale
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[j] += s * (float)(dg[j] >> 4);  // operands carry 16 q
+              for (int j = 0; j < 4; ++j) acc[j] += s16 * (double)dg[j];  // exact in fp64
             }
           }
           if (__builtin_expect(++c_gi == cv.per, 0)) {
             // end of a set: park the partial in LDS slot c_si (read by the control waves)
             c_gi = 0;
             red[c_si][wave][lane] = acc;
-            acc = float4_t{0.f, 0.f, 0.f, 0.f};
+            acc = Acc{0, 0, 0, 0};
             if (++c_si == cv.my_sets) {
               c_si = 0;
               stage_done = true;
@@ -520,21 +538,22 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         }
       }
     }
-    float su = 0.f, sq = 0.f, mx = -INFINITY, mn = INFINITY;
+    double su = 0.0, sq = 0.0;
+    float mx = -INFINITY, mn = INFINITY;
     if (active) {
 #pragma unroll
       for (int j = 0; j < P; ++j)
-        if (j < np) stats_block8(v[j], su, sq, mx, mn);
+        if (j < np) stats_block8_64(v[j], su, sq, mx, mn);
     }
-    su = wave_sum_dpp(su);
-    sq = wave_sum_dpp(sq);
+    su = wave_sum_dpp64(su);
+    sq = wave_sum_dpp64(sq);
     mx = wave_max_dpp(mx);
     mn = wave_min_dpp(mn);
     if (lane == 0) {
-      stat_red[0][cw] = su;
-      stat_red[1][cw] = sq;
-      stat_red[2][cw] = mx;
-      stat_red[3][cw] = mn;
+      stat_sum[0][cw] = su;
+      stat_sum[1][cw] = sq;
+      stat_mm[0][cw] = mx;
+      stat_mm[1][cw] = mn;
     }
     lds_barrier();  // E
     // Row parameters, one wave per row: lane u reads the statistics of the row's u-th wave.
@@ -542,16 +561,16 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       const int m = cw;
       const bool mine = lane < units_per_row;
       const int u = m * units_per_row + (mine ? lane : 0);
-      const float tsu = lanes8_reduce_dpp(mine ? stat_red[0][u] : 0.f, [](float p, float q) { return p + q; });
-      const float tsq = lanes8_reduce_dpp(mine ? stat_red[1][u] : 0.f, [](float p, float q) { return p + q; });
-      const float xmax = lanes8_reduce_dpp(mine ? stat_red[2][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
-      const float xmin = lanes8_reduce_dpp(mine ? stat_red[3][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
+      const double tsu = lanes8_sum_dpp64(mine ? stat_sum[0][u] : 0.0);
+      const double tsq = lanes8_sum_dpp64(mine ? stat_sum[1][u] : 0.0);
+      const float xmax = lanes8_reduce_dpp(mine ? stat_mm[0][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
+      const float xmin = lanes8_reduce_dpp(mine ? stat_mm[1][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
       if (lane == 0) {
-        float mu = 0.f, inv = 0.f;
-        if (norm) norm_params(tsu, tsq, K, mu, inv);
-        row_a[m] = mu;
-        row_b[m] = inv;
-        const float amax = norm ? fmaxf(h2f(norm_h(xmax, mu, inv)), -h2f(norm_h(xmin, mu, inv)))
+        double mu = 0.0, inv = 0.0;
+        if (norm) norm_params64(tsu, tsq, xmax, xmin, K, mu, inv);
+        row_mu64[m] = mu;
+        row_inv64[m] = inv;
+        const float amax = norm ? fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)))
                                 : fmaxf(xmax, -xmin);
         row_c[m] = h2f(f2h(amax / (float)kPassQmax<MODE>));
       }
@@ -559,12 +578,13 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     lds_barrier();  // F
     if (active) {
       int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K + 8 * row_tid;
-      const float mu = row_a[my_row], inv = row_b[my_row], sc = row_c[my_row];
+      const double mu = row_mu64[my_row], inv = row_inv64[my_row];
+      const float sc = row_c[my_row];
 #pragma unroll
       for (int j = 0; j < P; ++j) {
         if (j < np) {
           uint4 w = v[j];
-          if (norm) w = norm_block8(w, mu, inv);
+          if (norm) w = norm_block8_64(w, mu, inv);
           uint2 op, lg;
           quant_block8<kPassQmax<MODE>>(w, sc, op, lg);
           *reinterpret_cast<uint2*>(xq + j * (pstride / 2)) = op;
@@ -605,7 +625,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       for (int p = cw; p < sets * R; p += kCW) {
         const int si = p / R, r2 = p - si * R;
         const int rb = (bid + si * grid) * R + r2;
-        float4_t v = red[si][r2 * S][lane];
+        Acc v = red[si][r2 * S][lane];
         for (int s2 = 1; s2 < S; ++s2) v += red[si][r2 * S + s2][lane];
         float rowsum = 0.f;  // W4A16: sum_k w[n,k] from the all-ones operand row M
         if constexpr (MODE == 0) {
@@ -619,16 +639,20 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
           for (int j = 0; j < 4; ++j) {
             const int m = 4 * (lane >> 4) + j;
             if (m < M) {
-              float outv = v[j];
+              float outv;
+              uint16_t h;
               if constexpr (MODE == 0) {
+                outv = v[j];
                 if (norm) outv = (outv - row_a[m] * rowsum) * row_b[m];
-              } else {
-                outv *= row_c[m];
+                h = f2h(outv);
+              } else {  // exact product, rounded once
+                const double o64 = v[j] * (double)row_c[m];
+                outv = (float)o64;
+                h = f64_to_f16_rn(o64);
               }
               if (final_out) {
                 a.out[(size_t)m * N + n] = outv;
               } else {  // device-coherent store, read by other workgroups in the next stage
-                uint16_t h = f2h(outv);
                 if (h == kEmpty) h = 0x7E00u;
                 __hip_atomic_store(ps.y16 + (size_t)m * N + n, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
@@ -653,9 +677,11 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   }
 }
 
-// Start of a pass: fills the stage outputs with kEmpty (W4A4; device-coherent stores) and zeroes the
-// control words (a reserved word and the error word, then n_flags arrival flags kFlagStride apart).
-__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags) {
+// Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores) and the
+// final output with NaN, and zeroes the control words (a reserved word and the error word, then
+// n_flags arrival flags kFlagStride apart).
+__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags,
+                                                         float* out, uint32_t n_out) {
   if (blockIdx.x == 0) {
     if (threadIdx.x < 2) __hip_atomic_store(ctrl + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = threadIdx.x; i < n_flags; i += 256)
@@ -665,6 +691,8 @@ __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n
   const int4_t e = int4_t{-1, -1, -1, -1};
   for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += gridDim.x * 256u)
     __builtin_amdgcn_raw_buffer_store_b128(e, r, (int)(i * 16u), 0, kSc1);
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n_out; i += gridDim.x * 256u)
+    out[i] = __builtin_nanf("");
 }
 
 // ------------------------------------------------------------------ host side
@@ -679,7 +707,8 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   if (grid < 1 || grid > kMaxPassWorkgroups) return false;
   const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);  // control threads per input row
   for (int i = 0; i < n; ++i) {
-    if ((size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1) > kPassLdsStage) return false;
+    if ((size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1) > (mode == QS_W4A16 ? kPassLdsStage : kPassLdsStageInt))
+      return false;
     if (mode != QS_W4A16 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
     if (pick_pass_split(c[i].N, c[i].K, grid) < 0) return false;
   }
@@ -728,13 +757,14 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
                                      : reinterpret_cast<const void*>(fn2);
   static int lds_set[3] = {0, 0, 0};
   if (!lds_set[mode]) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPassLdsStage) != hipSuccess)
+    const int limit = (int)(mode == QS_W4A16 ? kPassLdsStage : kPassLdsStageInt);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, limit) != hipSuccess) {
+      (void)hipGetLastError();  // report it here, not at the caller's next HIP call
       return QS_ERR_HIP;
+    }
     lds_set[mode] = 1;
   }
-  // At least 80 KiB of dynamic LDS: together with the static arrays no two workgroups fit on one
-  // CU, so the num_cus workgroups spread one per CU.
-  size_t lds = 81920;
+  size_t lds = kPassLdsMin;
   for (int i = 0; i < n; ++i) {
     const size_t b = (size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1);
     lds = b > lds ? b : lds;
@@ -744,9 +774,13 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   const size_t sb = pass_stage_bytes(M, c, n);
   if (sb > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
   const uint32_t n16 = mode != QS_W4A16 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
-  const unsigned rblocks = n16 == 0 ? 1u : (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024u;
-  hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks), dim3(256), 0, st, reinterpret_cast<uint4*>(stage_out),
-                     n16, ctrl, mode == QS_W4A16 ? grid : 0);
+  const size_t n_out = (size_t)M * c[n - 1].N;
+  if (n_out > 0xFFFFFFFFu) return QS_ERR_UNSUPPORTED;
+  const size_t work = (size_t)n16 + n_out / 4;
+  const unsigned rblocks = (unsigned)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
+  hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(stage_out), n16, ctrl, mode == QS_W4A16 ? grid : 0, out,
+                     (uint32_t)n_out);
   int rc = launch_status();
   if (rc != QS_OK) return rc;
 

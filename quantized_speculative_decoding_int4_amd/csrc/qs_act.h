@@ -1,6 +1,15 @@
 // Device helpers for activations: per-token INT4 quantization (W4A4) and the row
 // standardisation between the linears of a chain.  Shared by the per-linear kernels
-// (linear.hip) and the persistent pass kernel (pass.hip).
+// (linear.hip), the batched kernel (gemm.hip) and the persistent pass kernel (pass.hip).
+//
+// Two arithmetics of the standardisation, one per kind of mode:
+//  * W4A16 folds it into the epilogue, y = (sum_k v w - mu sum_k w) / sd, with the row statistics
+//    in fp32 (its products are fp32 anyway);
+//  * the integer modes quantize the standardised fp16 row, so its rounding decides codes: the
+//    statistics, the standardised value and its rounding to fp16 are computed in fp64 and rounded
+//    once, correctly, to fp16 -- the float64 definition's own result, whatever the summation order
+//    (a different order moves the fp64 value by ~1e-16, which changes an fp16 rounding only for a
+//    value within that distance of a midpoint).
 #pragma once
 
 #include "qs_device.h"
@@ -63,6 +72,55 @@ __device__ __forceinline__ void stats_block8(const uint4 v, float& sum, float& s
     mn = fminf(mn, f);
   }
 }
+// ---- exact (fp64) standardisation of the integer modes
+
+// Correctly rounded fp64 -> fp16 (round to nearest even).  Converting through fp32 with two
+// round-to-nearest steps is wrong whenever the fp32 value lands exactly on an fp16 midpoint; rounding
+// the first step to odd instead (truncate, then set the last bit if anything was dropped) makes the
+// second step exact, since fp32 keeps at least two more bits than fp16 (24 >= 11 + 2), normal or not.
+__device__ __forceinline__ uint16_t f64_to_f16_rn(double d) {
+  const float f = (float)d;  // round to nearest even
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != d) {                           // inexact (or NaN, which stays NaN)
+    if (__builtin_fabs(back) > __builtin_fabs(d)) b -= 1u;  // was rounded away from zero: one step back
+    b |= 1u;                                 // sticky bit: round to odd
+  }
+  return f2h(__uint_as_float(b));
+}
+
+// Per-thread fp64 sum and sum of squares (exact products) and fp32 max / min of 8 fp16 values.
+__device__ __forceinline__ void stats_block8_64(const uint4 v, double& sum, double& sq, float& mx, float& mn) {
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = h2f(h[e]);
+    const double d = (double)f;
+    sum += d;
+    sq += d * d;
+    mx = fmaxf(mx, f);
+    mn = fminf(mn, f);
+  }
+}
+// Row mean and 1/std (population) in fp64.  A row with zero spread (max == min, the exact test)
+// maps to zeros: inv = 0.
+__device__ __forceinline__ void norm_params64(double sum, double sq, float mx, float mn, int K, double& mu,
+                                              double& inv) {
+  mu = sum / (double)K;
+  double var = sq / (double)K - mu * mu;
+  var = var > 0.0 ? var : 0.0;
+  inv = (mx != mn && var > 0.0) ? 1.0 / __builtin_sqrt(var) : 0.0;
+}
+__device__ __forceinline__ uint16_t norm_h64(float x, double mu, double inv) {
+  return inv == 0.0 ? (uint16_t)0 : f64_to_f16_rn(((double)x - mu) * inv);
+}
+__device__ __forceinline__ uint4 norm_block8_64(uint4 v, double mu, double inv) {
+  uint16_t* h = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = norm_h64(h2f(h[e]), mu, inv);
+  return v;
+}
+
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));

@@ -23,6 +23,7 @@ namespace qs {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef double double4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;
@@ -89,6 +90,27 @@ __host__ __device__ __forceinline__ int xq_pos(int j) {
   return (j & 8) | ((j & 3) << 1) | ((j >> 2) & 1);
 }
 
+// ---- lane moves of 32- and 64-bit values (a double moves as its two halves) -------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_v(float x) { return __int_as_float(dpp_i<CTRL>(__float_as_int(x))); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_v(double x) {
+  const long long b = __double_as_longlong(x);
+  const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)b), hi = (unsigned)dpp_i<CTRL>((int)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ float readlane_v(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_v(double x, int l) {
+  const long long b = __double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // ---- wave (64-lane) reductions -------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -131,6 +153,21 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 }
 __device__ __forceinline__ float wave_min_dpp(float v) {
   return wave_reduce_dpp(v, [](float a, float b) { return fminf(a, b); });
+}
+// fp64 sum over the 64 lanes, same fixed order as wave_reduce_dpp; result in every lane.
+__device__ __forceinline__ double wave_sum_dpp64(double v) {
+  v += dpp_v<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_v<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_v<0x141>(v);  // row_half_mirror
+  v += dpp_v<0x140>(v);  // row_mirror
+  return (readlane_v(v, 0) + readlane_v(v, 16)) + (readlane_v(v, 32) + readlane_v(v, 48));
+}
+// fp64 sum over lanes 0..7 (first three in-row steps), returned from lane 0.
+__device__ __forceinline__ double lanes8_sum_dpp64(double v) {
+  v += dpp_v<0xB1>(v);
+  v += dpp_v<0x4E>(v);
+  v += dpp_v<0x141>(v);
+  return readlane_v(v, 0);
 }
 // Result of op over lanes 0..7 (after the first three in-row steps), returned from lane 0.
 template <typename Op>

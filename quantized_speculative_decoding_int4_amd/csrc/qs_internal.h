@@ -89,6 +89,7 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
                 unsigned* ctrl, uint16_t* stage_out, hipStream_t st);
 
 size_t verify_workspace(int B, int gamma, int V);
+size_t verify_counter_bytes();  // the arrival counters at the start of a verify workspace
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,
                          int32_t* t, float* p1, int32_t* n_acc, int32_t* out, void* ws,
                          hipStream_t st);

@@ -10,26 +10,6 @@
 
 namespace qs {
 
-// Lane moves of 32- and 64-bit values (a double moves as its two halves).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
-template <int CTRL>
-__device__ __forceinline__ float dpp_v(float x) { return __int_as_float(dpp_i<CTRL>(__float_as_int(x))); }
-template <int CTRL>
-__device__ __forceinline__ double dpp_v(double x) {
-  const long long b = __double_as_longlong(x);
-  const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)b), hi = (unsigned)dpp_i<CTRL>((int)(b >> 32));
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-__device__ __forceinline__ float readlane_v(float x, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-__device__ __forceinline__ double readlane_v(double x, int l) {
-  const long long b = __double_as_longlong(x);
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), l);
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
 // (max, sum of exp(l - max), lowest index attaining max) of a set of logits, and its merge.
 struct Msi {
   float m, s;

@@ -79,6 +79,7 @@ static inline int draw_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 // chunk sums of the draw.
 constexpr int kCounterStride = 64;  // 32-bit words per sequence: one 256-byte line each
 constexpr size_t kCounterBytes = (size_t)QS_MAX_VERIFY_SEQS * kCounterStride * 4;
+size_t verify_counter_bytes() { return kCounterBytes; }
 size_t verify_workspace(int B, int gamma, int V) {
   if (B > QS_MAX_VERIFY_SEQS) B = QS_MAX_VERIFY_SEQS;  // larger batches run block by block
   const size_t Cs = (size_t)stat_chunks(V), Cd = (size_t)draw_chunks(V);

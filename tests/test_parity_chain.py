@@ -1,0 +1,317 @@
+"""GPU parity of qs_chain_forward (the draft and verify passes through a stack of linears) and of
+one speculative iteration, against the CPU oracle on the same seeded inputs.
+
+Bars: the integer modes (W4A4, W4A8) are exact end to end -- every code, group sum, fp16 stage
+value and the fp32 output equal the oracle's -- so their chains are compared bit for bit.  W4A16
+chains are held per stage to the single-linear bar and end to end to the chain bound pinned on the
+CPU (tests/gpu_util.chain_bound)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qspec_oracle as O
+from quantized_speculative_decoding_int4_amd import workloads as W
+from tests.gpu_util import (MAX_ABS, PROB_ABS, TIE_TAU, assert_chain_close, assert_exact, assert_linear_close,
+                            chain_bound, dev, host, oracle_chain)
+
+pytestmark = pytest.mark.gpu
+
+MODE_NAMES = {0: "w4a16", 1: "w4a4", 2: "w4a8"}
+
+
+@pytest.fixture(scope="module")
+def qs():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from quantized_speculative_decoding_int4_amd import qspec
+    return qspec
+
+
+def _pack_chain(qs, layers):
+    packed = []
+    for q, s in layers:
+        wp, sp = qs.qs_pack_weights(dev(q), dev(s))
+        packed.append((wp, sp, q.shape[0], q.shape[1]))
+    return qs.Chain(packed)
+
+
+def _check(y, ref, mode, key, what):
+    if mode == 0:
+        assert_chain_close(y, ref, key, what)
+    else:
+        assert_exact(y, ref, what)
+
+
+# ---------------------------------------------------------------- small chains
+
+def _balanced_chain_case(rng):
+    """Stage 1 maps a one-hot input to outputs of exactly +-2^-6, balanced within the 128 columns
+    stage 2 reads, so standardisation yields exactly +-1 and every step is exact: the GPU must match
+    bit for bit in every mode."""
+    k1, n1 = 128, 256
+    q1 = np.zeros((n1, k1), np.int8)
+    half = np.array([1, -1] * 64, np.int8)
+    q1[:, 0] = np.concatenate([rng.permutation(half), rng.permutation(half)])
+    q1[:, 1:] = rng.integers(-8, 8, size=(n1, k1 - 1), dtype=np.int8)
+    s1 = np.full((n1, 1), 2.0 ** -6, np.float16)
+    x = np.zeros((2, k1), np.float16)
+    x[:, 0] = 1.0
+    q2, s2 = W.integer_case_weights(rng, 8, 128, exponents=(-5,))
+    return x, [(q1, s1), (q2, s2)]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_chain_exact_balanced_case(qs, mode):
+    x, layers = _balanced_chain_case(W.rng_for(19))
+    y = host(qs.qs_chain_forward(mode, dev(x), _pack_chain(qs, layers)))
+    assert np.array_equal(y.astype(np.float64), O.chain_forward(MODE_NAMES[mode], x, layers))
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (0, 1), (1, 4), (0, 12), (1, 20), (0, 20), (0, 70), (1, 70),
+                                    (2, 1), (2, 4), (2, 20), (2, 70), (0, 256), (1, 256), (2, 256)])
+def test_chain_small_llama_like(qs, mode, m):
+    """Two layers of q|k|v, o, gate|up, down at hidden 512 plus a 3000-way head; o reads the q
+    columns, down reads the gate columns.  Row counts cover the persistent pass (W4A16 <= 4, integer
+    modes 1), the LDS-staged streaming kernel and the batched kernel with K splits."""
+    print(f"chain mode={mode} m={m}", flush=True)
+    rng = W.rng_for(800 + m)
+    h, inter = 512, 1024
+    shapes = [(h + 256, h), (h, h), (2 * inter, h), (h, inter)] * 2 + [(3000, h)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, h)
+    y = host(qs.qs_chain_forward(mode, dev(x), _pack_chain(qs, layers)))
+    _check(y, O.chain_forward(MODE_NAMES[mode], x, layers), mode, "small_llama", f"chain mode={mode} m={m}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 40), (1, 40), (2, 33)])
+def test_chain_with_vocabulary_wide_head(qs, mode, m):
+    """A vocabulary-wide last stage (N >= 32768) through the batched kernel."""
+    print(f"chain wide head mode={mode} m={m}", flush=True)
+    rng = W.rng_for(850 + m + mode)
+    h = 256
+    shapes = [(h + 128, h), (h, h), (33000, h)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, h)
+    y = host(qs.qs_chain_forward(mode, dev(x), _pack_chain(qs, layers)))
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
+    if mode == 0:
+        assert_linear_close(y, ref, f"chain wide head mode={mode} m={m}")
+    else:
+        assert_exact(y, ref, f"chain wide head mode={mode} m={m}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
+def test_chain_longer_than_one_persistent_launch(qs, mode, m):
+    """75 linears.  At M <= 4 (W4A16) / M = 1 (integer modes) the persistent pass splits them over
+    two launches (at most 72 per launch), so the hand-over at the seam is covered; the other row
+    counts run linear by linear."""
+    print(f"long chain mode={mode} m={m}", flush=True)
+    rng = W.rng_for(900 + 10 * m + mode)
+    shapes = [(384, 256), (256, 384)] * 37 + [(1000, 256)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 256)
+    chain = _pack_chain(qs, layers)
+    persistent = (m <= 4) if mode == 0 else (m <= 1)
+    assert chain.pass_launches(mode, m) == (2 if persistent else 0)
+    y = host(qs.qs_chain_forward(mode, dev(x), chain))
+    _check(y, O.chain_forward(MODE_NAMES[mode], x, layers), mode, "long75", f"long chain mode={mode} m={m}")
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1)])
+def test_barrier_timeout_is_reported_and_cleared(qs, mode, m):
+    """A zero time-out makes the first wait of a persistent pass fail at once (W4A16: the grid
+    barrier; the integer modes: the poll for the next stage's input): every workgroup exits (no
+    hang), the time-out word is reported and the output is all NaN, so nothing downstream can take
+    it for logits; the next call with the normal limit clears the word and is correct."""
+    print(f"time-out mode={mode} m={m}", flush=True)
+    rng = W.rng_for(950)
+    shapes = [(384, 256), (256, 384), (512, 256)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 256)
+    chain = _pack_chain(qs, layers)
+    assert chain.pass_launches(mode, m) == 1
+    ws = torch.zeros(chain.workspace_bytes(mode, m), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    qs.qs_set_barrier_timeout_us(0)
+    try:
+        out = qs.qs_chain_forward(mode, xd, chain, ws=ws)
+        assert qs.qs_chain_pass_status(mode, m, chain, ws)
+        assert torch.isnan(out).all(), "a timed-out pass must leave NaN in its output"
+    finally:
+        qs.qs_set_barrier_timeout_us(200000)
+    y = host(qs.qs_chain_forward(mode, xd, chain, ws=ws))
+    assert not qs.qs_chain_pass_status(mode, m, chain, ws)
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
+    if mode == 0:
+        assert_linear_close(y, ref, "chain after a time-out")
+    else:
+        assert_exact(y, ref, "chain after a time-out")
+
+
+# ---------------------------------------------------------------- full-size stack, the bench's launch configurations
+
+_STACK = {}
+
+
+def _stack(qs):
+    """The 32-layer Llama-3-8B-shaped stack + 4096 -> 128256 head, weights drawn on the device by the
+    seeded generator (seed 0), packed, and copied to the host for the oracle; built once."""
+    if not _STACK:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        layers, host_layers = [], []
+        for name, n, k in W.stack_shapes():
+            q, s = W.int4_weights_device(gen, n, k, device="cuda")
+            wp, sp = qs.qs_pack_weights(q, s)
+            host_layers.append((host(q), host(s)))
+            del q, s
+            layers.append((wp, sp, n, k))
+        cols = np.unique(np.concatenate([np.sort(W.rng_for(32).choice(W.VOCAB, size=3000, replace=False)),
+                                         [0, W.VOCAB - 1]]))
+        _STACK.update(layers=layers, host=host_layers, chain=qs.Chain(layers), cols=cols)
+    return _STACK
+
+
+def _sampled_head(st):
+    hq, hs = st["host"][-1]
+    return st["host"][:-1] + [(hq[st["cols"]], hs[st["cols"]])]
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 128), (1, 128), (2, 64)])
+def test_full_stack_against_the_oracle(qs, mode, m):
+    """The whole stack in the bench's launch configurations: the persistent pass (W4A16 verify at
+    M = 4, W4A4 / W4A8 draft at M = 1) and one launch of the batched kernel per linear (M = 64, 128,
+    config 4's batched verify).  The oracle runs the whole stack itself from the same inputs, its
+    head restricted to 3000 sampled vocabulary rows (which gives exactly those logit columns).
+    Integer modes: bit-exact.  W4A16: the chain bound of the full stack.  Top-1 over the sampled
+    columns: the same in every row, except (W4A16) where the oracle's two best sampled logits are
+    within twice the max-abs bound of each other."""
+    print(f"full stack mode={mode} m={m}", flush=True)
+    st = _stack(qs)
+    chain = st["chain"]
+    persistent_rows = {0: 4, 1: 1, 2: 1}[mode]
+    assert chain.pass_launches(mode, m) == (0 if m > persistent_rows else 2)
+    x = W.activations(W.rng_for(31), m, W.HIDDEN)[0]
+    logits = host(qs.qs_chain_forward(mode, dev(x), chain))
+    assert np.isfinite(logits).all()
+    ref = oracle_chain(MODE_NAMES[mode], x, _sampled_head(st))
+    y = logits[:, st["cols"]]
+    key = f"llama_full_m{4 if m <= 4 else 128}"
+    _check(y, ref, mode, key, f"full stack mode={mode} m={m}")
+    t_gpu, t_ref = np.argmax(y, axis=1), np.argmax(ref, axis=1)
+    srt = np.sort(ref, axis=1)
+    rb, ab = chain_bound(key)
+    tol = 2 * max(MAX_ABS, ab * float(np.sqrt(np.mean(ref ** 2)))) if mode == 0 else 0.0
+    agree = t_gpu == t_ref
+    near = (srt[:, -1] - srt[:, -2] <= tol) & (ref[np.arange(m), t_gpu] >= srt[:, -1] - tol)
+    print(f"  Top-1 agreement over the sampled columns: {int(agree.sum())}/{m}", flush=True)
+    assert (agree | near).all(), "Top-1 differs where the oracle's top-2 gap exceeds the bound"
+
+
+@pytest.mark.parametrize("m", [4, 128])
+def test_full_stack_w4a16_stage_by_stage(qs, m):
+    """Each W4A16 stage of the full stack, given the GPU's own input, against the oracle's stage on
+    that input, held to the single-linear bar (this separates a wrong stage from the drift a chain
+    accumulates).  The GPU chain cut after stage i gives stage i's fp32 output; its fp16 rounding is
+    exactly what stage i + 1 reads inside the full chain (the kernel rounds the same fp32 value).
+    Checked stages: the first layer, the seam between the two persistent launches, the last layer and
+    the head (on 3000 sampled vocabulary rows)."""
+    st = _stack(qs)
+    layers, hl = st["layers"], st["host"]
+    n = len(layers)
+    x = W.activations(W.rng_for(34), m, W.HIDDEN)[0]
+    xd = dev(x)
+
+    def prefix(i):  # fp32 output of stages 0..i
+        return host(qs.qs_chain_forward(0, xd, qs.Chain(layers[:i + 1])))
+
+    for i in (0, 1, 2, 3, 63, 64, 65, 125, 126, 127, 128):
+        prev = x if i == 0 else prefix(i - 1).astype(np.float16)
+        q, s = hl[i]
+        if i == n - 1:
+            q, s = q[st["cols"]], s[st["cols"]]
+        v = np.ascontiguousarray(prev[:, :q.shape[1]])
+        z = v.astype(np.float64) if i == 0 else O.standardize_rows_exact(v)
+        ref = z @ O.dequantize_weights(q, s).T
+        got = prefix(i)
+        if i == n - 1:
+            got = got[:, st["cols"]]
+        assert_linear_close(got, ref, f"stage {i} m={m}")
+
+
+def test_full_stack_rows_are_independent(qs):
+    """Full-size W4A16 verify pass at M = 4 against four M = 1 passes on the same rows: every row's
+    arithmetic (its statistics, K split and MFMA row) is its own, so the logits match bit for bit."""
+    st = _stack(qs)
+    x = dev(W.activations(W.rng_for(33), 4, W.HIDDEN)[0])
+    full = host(qs.qs_chain_forward(0, x, st["chain"]))
+    for i in range(4):
+        one = host(qs.qs_chain_forward(0, x[i:i + 1].contiguous(), st["chain"]))
+        assert np.array_equal(one[0], full[i]), f"row {i}"
+
+
+# ---------------------------------------------------------------- one speculative iteration
+
+@pytest.mark.parametrize("draft_mode", [1, 2])
+@pytest.mark.parametrize("B", [1, 3])
+def test_speculative_iteration(qs, draft_mode, B):
+    """One iteration of [P3] "draft modelとtarget modelの処理フロー" on a small stack, GPU against
+    the oracle step by step, gamma = 3:
+      1. draft: gamma passes of the draft mode at M = B (row i of sequence b is the input of its
+         draft step i), each followed by the draft's Top-1 (greedy verify with gamma = 0);
+      2. verify: one W4A16 pass over the B (gamma + 1) rows;
+      3. accept: greedy prefix match and sampling acceptance over the target and draft logits.
+    The draft logits and tokens are exact (integer modes).  Target logits meet the chain bound; the
+    accept step is compared with the oracle on the GPU's logits (decisions bit-exact, probabilities
+    within 1e-5), and end to end the oracle's own iteration must commit the same tokens wherever the
+    target's Top-1 is not within the logit bound of a tie.  W4A8 drafts agree with the target
+    often enough to exercise accepted prefixes."""
+    gamma, V, h = 3, 3000, 512
+    rng = W.rng_for(970 + B + 10 * draft_mode)
+    shapes = [(h + 256, h), (h, h), (2 * h, h), (h, 2 * h)] * 2 + [(V, h)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    chain = _pack_chain(qs, layers)
+    # rows of the verify pass; row (b, i) with i < gamma is also draft step i's input of sequence b
+    xv = W.activations(rng, B * (gamma + 1), h)[0].reshape(B, gamma + 1, h)
+    ua, uf = W.uniforms(rng, (B, gamma)), W.uniforms(rng, (B,))
+
+    # ---- GPU
+    dname = MODE_NAMES[draft_mode]
+    drf = np.empty((B, gamma, V), np.float32)
+    d = np.empty((B, gamma), np.int32)
+    for i in range(gamma):
+        lq = qs.qs_chain_forward(draft_mode, dev(np.ascontiguousarray(xv[:, i])), chain)
+        g = qs.qs_verify_greedy(lq.view(B, 1, V), None)
+        drf[:, i] = host(lq)
+        d[:, i] = host(g["out_tokens"])[:, 0]
+    tgt = host(qs.qs_chain_forward(0, dev(xv.reshape(-1, h)), chain)).reshape(B, gamma + 1, V)
+    dd = dev(d)
+    gr = qs.qs_verify_greedy(dev(tgt), dd)
+    sm = qs.qs_verify_sample(dev(tgt), dev(drf), dd, dev(ua), dev(uf))
+
+    # ---- oracle, step for step
+    for i in range(gamma):
+        ref_q = O.chain_forward(dname, np.ascontiguousarray(xv[:, i]), layers)
+        assert_exact(drf[:, i], ref_q, f"draft step {i}")
+        t_q, _ = O.top1(ref_q.astype(np.float32))
+        assert np.array_equal(d[:, i], t_q), f"draft token {i}"
+    ref_p = O.chain_forward("w4a16", xv.reshape(-1, h), layers).reshape(B, gamma + 1, V)
+    assert_chain_close(tgt.reshape(-1, V), ref_p.reshape(-1, V), "small_llama", "target logits")
+    # accept on the GPU's logits: exact decisions
+    og = O.verify_greedy(tgt, d)
+    assert np.array_equal(host(gr["n_accept"]), og["n_accept"])
+    assert np.array_equal(host(gr["out_tokens"]), og["out_tokens"])
+    os_ = O.verify_sample(tgt, drf, d, ua, uf)
+    assert np.abs(host(sm["accept_prob"]) - os_["accept_prob"]).max() <= PROB_ABS
+    amb = np.abs(ua - os_["accept_prob"]) <= TIE_TAU
+    if not amb.any():
+        assert np.array_equal(host(sm["n_accept"]), os_["n_accept"])
+    # end to end: the oracle's own iteration (its logits throughout)
+    oe = O.verify_greedy(ref_p.astype(np.float32), d)
+    srt = np.sort(ref_p, axis=2)
+    rb, ab = chain_bound("small_llama")
+    tol = 2 * max(MAX_ABS, ab * float(np.sqrt(np.mean(ref_p ** 2))))
+    clear = (srt[:, :, -1] - srt[:, :, -2] > tol).all(axis=1)
+    print(f"  greedy: accepted {host(gr['n_accept']).tolist()} (oracle end to end {oe['n_accept'].tolist()}), "
+          f"sampling accepted {host(sm['n_accept']).tolist()}", flush=True)
+    assert np.array_equal(host(gr["out_tokens"])[clear], oe["out_tokens"][clear])
