@@ -289,6 +289,26 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qs_verify_greedy_noalloc -- qs_verify_greedy for callers that cannot
+ * allocate or pass device memory of their own: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * outputs and errors, without the workspace: its scratch (arrival counters and
+ * statistics partials) is a fixed device array inside the library, one per
+ * GPU, of qs_verify_greedy_noalloc_max_bytes() bytes (8 MiB), held until the
+ * process ends.  A call whose qs_verify_workspace_bytes(B, gamma, V) exceeds
+ * that returns QS_ERR_UNSUPPORTED before any device work.  The call allocates
+ * nothing; a device's first call also clears the counters (with a kernel on
+ * `stream`), and every call leaves them cleared.  All calls on one GPU share
+ * the array: calls that overlap in time on the same GPU race.
+ */
+size_t qs_verify_greedy_noalloc_max_bytes(void);
+int qs_verify_greedy_noalloc(const float* tgt_logits, const int32_t* draft_ids,
+                             int B, int gamma, int V,
+                             int32_t* tgt_top1, float* top1_prob,
+                             int32_t* n_accept, int32_t* out_tokens,
+                             void* stream);
+
+/*
  * qs_verify_tree_greedy -- greedy acceptance over a tree of draft candidates
  * scored in one target pass ([P2] "3.中核となる技術的要素": verification that
  * expands into a tree; the rule is this library's reading, the greedy prefix

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqspec.so")
-SOURCES = ("abi.hip", "linear.hip", "gemm.hip", "verify.hip", "chain.hip", "pass.hip")
+SOURCES = ("abi.hip", "linear.hip", "gemm.hip", "verify.hip", "chain.hip", "pass.hip", "noalloc.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

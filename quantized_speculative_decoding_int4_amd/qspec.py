@@ -53,6 +53,8 @@ _SIGS = {
     "qs_set_barrier_timeout_us": ([_i], _i),
     "qs_chain_pass_status": ([_i, _i, _p, _i, _p, _sz, _p, _p], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
+    "qs_verify_greedy_noalloc": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
+    "qs_verify_greedy_noalloc_max_bytes": ([], _sz),
     "qs_verify_tree_greedy": ([_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_sample": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
 }
@@ -250,6 +252,35 @@ def qs_verify_greedy(tgt_logits, draft_ids, out=None, ws=None, want_prob=True):
         _ptr(out["n_accept"], torch.int32, (b,), "n_accept"),
         _ptr(out["out_tokens"], torch.int32, (b, gp1), "out_tokens"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
+    return out
+
+
+def verify_greedy_noalloc_max_bytes() -> int:
+    return _lib.qs_verify_greedy_noalloc_max_bytes()
+
+
+def qs_verify_greedy_noalloc(tgt_logits, draft_ids, out=None, want_prob=True):
+    """qs_verify_greedy without a workspace argument: its scratch is the library's own fixed device
+    array (calls that overlap in time on one GPU race).  Same arguments and outputs."""
+    b, gp1, v = tgt_logits.shape
+    gamma = gp1 - 1
+    dev = tgt_logits.device
+    if out is None:
+        out = {
+            "tgt_top1": torch.empty((b, gp1), dtype=torch.int32, device=dev),
+            "top1_prob": torch.empty((b, gp1), dtype=torch.float32, device=dev) if want_prob else None,
+            "n_accept": torch.empty((b,), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((b, gp1), dtype=torch.int32, device=dev),
+        }
+    _check("qs_verify_greedy_noalloc", _lib.qs_verify_greedy_noalloc(
+        _ptr(tgt_logits, torch.float32, (b, gp1, v), "tgt_logits"),
+        _ptr(draft_ids, torch.int32, (b, gamma), "draft_ids", nullable=gamma == 0),
+        b, gamma, v,
+        _ptr(out["tgt_top1"], torch.int32, (b, gp1), "tgt_top1"),
+        _ptr(out["top1_prob"], torch.float32, (b, gp1), "top1_prob", nullable=True),
+        _ptr(out["n_accept"], torch.int32, (b,), "n_accept"),
+        _ptr(out["out_tokens"], torch.int32, (b, gp1), "out_tokens"),
+        _stream()))
     return out
 
 

@@ -166,3 +166,26 @@ def test_new_entry_points_argument_errors(lib):
     assert tg(fake, fake, fake, 1, 65, 10, fake, fake, fake, None, fake, 1 << 30, None) == -2  # T > 64
     assert tg(fake, None, fake, 1, 4, 10, fake, fake, fake, None, fake, 1 << 30, None) == -1   # tokens
     assert tg(fake, fake, fake, 1, 4, 10, fake, fake, fake, None, fake, 0, None) == -4
+
+
+def test_noalloc_greedy_refuses_before_any_device_work(lib):
+    """The greedy verify without a workspace: argument errors and sizes beyond its fixed scratch are
+    refused on the host (fake pointers are never dereferenced)."""
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fake = 1 << 20
+    mx = lib.qs_verify_greedy_noalloc_max_bytes
+    mx.argtypes = []
+    mx.restype = sz
+    assert mx() == 8 << 20
+    vw = lib.qs_verify_workspace_bytes
+    vw.argtypes = [i, i, i]
+    vw.restype = sz
+    f = lib.qs_verify_greedy_noalloc
+    f.argtypes = [p, p, i, i, i, p, p, p, p, p]
+    f.restype = i
+    assert f(None, fake, 1, 3, 1000, fake, None, fake, fake, None) == -1            # logits NULL
+    assert f(fake, None, 1, 3, 1000, fake, None, fake, fake, None) == -1            # draft ids NULL, gamma > 0
+    assert f(fake, fake, 0, 3, 1000, fake, None, fake, fake, None) == -1            # B < 1
+    assert vw(4096, 63, 1 << 20) > mx()
+    assert f(fake, fake, 4096, 63, 1 << 20, fake, None, fake, fake, None) == -2     # beyond the scratch
+    assert f(fake, fake, 1, 64, 1000, fake, None, fake, fake, None) == -2           # gamma out of range
