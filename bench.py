@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device to device twice (a plain copy kernel of known "
                          "size, to scale memory-traffic counters under a profiler)")
@@ -123,6 +123,155 @@ def cpu_baseline(budget_s: float):
                    f"down and an 8192-row LM-head block) in {t_used:.1f} s; float64 NumPy, "
                    f"BLAS threads {threads}, affinity cores {cores}"),
     }
+
+
+def linear_rates(qs, W, torch, E):
+    """Configs 0-2 measured one linear at a time: each shape's packed weights are copied until the
+    copies exceed 512 MiB (twice the 256 MiB MALL), and a HIP graph of one call per copy is replayed,
+    so every call streams its weights from HBM and the host's launch latency is not timed.  Rate =
+    packed weight bytes (0.515625 B per weight) / time per call; the fused LM-head Top-1 is timed
+    the same way."""
+    import numpy as np
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    rng = W.rng_for(17)
+    shapes = [("cfg0 4096x4096", 4096, 4096)] + [(f"cfg1 {n_}", n, k) for n_, n, k in W.LAYER_LINEARS] + \
+             [("cfg2 lm_head", W.VOCAB, W.HIDDEN)]
+    out = {}
+    for name, n, k in shapes:
+        q, s_ = W.int4_weights_device(gen, n, k, device=dev)
+        wp, sp = qs.qs_pack_weights(q, s_)
+        del q, s_
+        wbytes = n * k // 2 + n * (k // 128) * 2
+        copies = max(2, -(-(512 << 20) // wbytes))
+        ws_list = [(wp.clone(), sp.clone()) for _ in range(copies)]
+        rec = {"N": n, "K": k, "weight_bytes": wbytes, "copies": copies}
+        runs = [("w4a16_M4", qs.QS_W4A16, 4), ("w4a4_M1", qs.QS_W4A4, 1)]
+        if name.startswith("cfg0"):
+            runs.append(("w4a4_M4", qs.QS_W4A4, 4))
+        for key, mode, m in runs:
+            x = torch.from_numpy(W.activations(rng, m, k)[0]).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            lw = qs.linear_workspace_bytes(mode, m, n, k)
+            wsp = torch.zeros(max(lw, 1), dtype=torch.uint8, device=dev)
+
+            def call(wpk, spk, lg=None):
+                if name.startswith("cfg2"):
+                    qs.qs_lmhead(mode, x, wpk, spk, n, logits=y, ws=wsp if lw else None)
+                elif mode == qs.QS_W4A16:
+                    qs.qs_linear_w4a16(x, wpk, spk, n, y=y)
+                else:
+                    qs.qs_linear_w4a4(x, wpk, spk, n, y=y, ws=wsp if lw else None)
+            for wpk, spk in ws_list[:2]:
+                call(wpk, spk)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for wpk, spk in ws_list:
+                    call(wpk, spk)
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                a, b = E(enable_timing=True), E(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / copies)
+            us = float(np.median(ts))
+            rec[key] = {"us": us, "GBps": wbytes / (us * 1e-6) / 1e9, "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            del g, x, y, wsp
+        if name.startswith("cfg2"):  # the LM-head with the fused Top-1 epilogue, same rotation
+            for key, mode, m in (("top1_w4a16_M4", qs.QS_W4A16, 4), ("top1_w4a4_M1", qs.QS_W4A4, 1)):
+                x = torch.from_numpy(W.activations(rng, m, k)[0]).to(dev)
+                wst = torch.zeros(qs.lmhead_top1_workspace_bytes(mode, m, n, k), dtype=torch.uint8, device=dev)
+                o = qs.qs_lmhead_top1(mode, x, ws_list[0][0], ws_list[0][1], n, want_logits=False, ws=wst)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for wpk, spk in ws_list:
+                        qs.qs_lmhead_top1(mode, x, wpk, spk, n, want_logits=False, top1=o["top1"],
+                                          top1_prob=o["top1_prob"], ws=wst)
+                g.replay()
+                torch.cuda.synchronize()
+                a, b = E(enable_timing=True), E(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / copies
+                rec[key] = {"us": us, "GBps": wbytes / (us * 1e-6) / 1e9}
+                del g, wst, o, x
+        out[name] = rec
+        del ws_list, wp, sp
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_per_config(budget_s: float):
+    """The oracle (as it stands) per config, on bounded samples, in the GPU lines' units: weight GB/s
+    of single linears (configs 0, 1), of the LM-head (config 2, one 8192-row block), positions/s of the
+    accept step (configs 0, 2, 4), and config 3's iteration time extrapolated from layer 0."""
+    import time as _t
+
+    import numpy as np
+
+    from oracle import qspec_oracle as O
+    from quantized_speculative_decoding_int4_amd import workloads as W
+
+    rng = W.rng_for(12)
+    res = {}
+    t_start = _t.perf_counter()
+
+    def wrate(fn, n, k, m):
+        q, s = W.int4_weights(rng, n, k)
+        x, _ = W.activations(rng, m, k)
+        t0 = _t.perf_counter()
+        fn(x, q, s)
+        dt = _t.perf_counter() - t0
+        return {"s": dt, "GBps": (n * k // 2 + n * (k // 128) * 2) / dt / 1e9}
+
+    w16 = lambda x, q, s: O.linear_w4a16(x, q, s)  # noqa: E731
+    w4 = lambda x, q, s: O.linear_w4a4(x, q, s)    # noqa: E731
+    wrate(w16, 4096, 4096, 4)  # untimed: the process's first large allocations
+    res["cfg0"] = {"w4a16_M4": wrate(w16, 4096, 4096, 4), "w4a4_M4": wrate(w4, 4096, 4096, 4)}
+    res["cfg1"] = {}
+    layer_s = {"w4a16_M4": 0.0, "w4a4_M1": 0.0}
+    for name, n, k in W.LAYER_LINEARS:
+        a_, b_ = wrate(w16, n, k, 4), wrate(w4, n, k, 1)
+        res["cfg1"][name] = {"w4a16_M4": a_, "w4a4_M1": b_}
+        layer_s["w4a16_M4"] += a_["s"]
+        layer_s["w4a4_M1"] += b_["s"]
+    head_rows = 8192  # one block of the LM-head; the rate is per weight byte
+    res["cfg2"] = {"lm_head_block_rows": head_rows, "w4a16_M4": wrate(w16, head_rows, W.HIDDEN, 4),
+                   "w4a4_M1": wrate(w4, head_rows, W.HIDDEN, 1)}
+    head_s = {k_: res["cfg2"][k_]["s"] * W.VOCAB / head_rows for k_ in ("w4a16_M4", "w4a4_M1")}
+
+    def accept_rate(B, G, V, reps=1):
+        tg = W.logits(rng, (B, G + 1, V), sigma=5.24)
+        dr = W.perturb(rng, tg[:, :G])
+        d = rng.integers(0, V, size=(B, G)).astype(np.int32)
+        ua, uf = W.uniforms(rng, (B, G)), W.uniforms(rng, (B,))
+        t0 = _t.perf_counter()
+        for _ in range(reps):
+            O.verify_greedy(tg, d)
+        tgr = (_t.perf_counter() - t0) / reps
+        t0 = _t.perf_counter()
+        for _ in range(reps):
+            O.verify_sample(tg, dr, d, ua, uf)
+        tsm = (_t.perf_counter() - t0) / reps
+        pos = B * (G + 1)
+        return {"greedy_positions_per_s": pos / tgr, "sample_positions_per_s": pos / tsm}
+
+    res["cfg0"]["accept_V32_gamma3"] = accept_rate(1, 3, 32, reps=200)
+    res["cfg2"]["accept_B1_gamma3"] = accept_rate(1, 3, W.VOCAB)
+    res["cfg4"] = {"accept_B16_gamma7": accept_rate(16, 7, W.VOCAB)}
+    # config 3: 32 x layer 0 + the head, extrapolated (labelled so): 3 draft passes (W4A4, M = 1) + one verify
+    # pass (W4A16, M = 4); accept costs are negligible next to them
+    it = 3 * (32 * layer_s["w4a4_M1"] + head_s["w4a4_M1"]) + 32 * layer_s["w4a16_M4"] + head_s["w4a16_M4"]
+    res["cfg3"] = {"iteration_s_extrapolated": it, "verify_pass_s_extrapolated": 32 * layer_s["w4a16_M4"] + head_s["w4a16_M4"]}
+    res["wall_s"] = _t.perf_counter() - t_start
+    return res
 
 
 def main():
@@ -317,8 +466,11 @@ def main():
         tgms = time_calls(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg))
         tsms = time_calls(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg))
         pos = B * (G + 1)
+        greedy_bytes = 4.0 * V * pos                                  # every logit read once
+        sample_bytes = 4.0 * V * B * (2 * G + 1) + 8.0 * V * B         # plus the two drawn-from rows again
         accept[f"B{B}_gamma{G}"] = {
             "positions": pos,
+            "greedy_bytes": greedy_bytes, "sample_bytes": sample_bytes,
             "greedy_us": tgms * 1e3, "greedy_positions_per_s": pos / (tgms * 1e-3),
             "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
             "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
@@ -330,6 +482,12 @@ def main():
             "sample_cold": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), reps=30,
                                      before=flush),
         }
+        a_ = accept[f"B{B}_gamma{G}"]
+        # achieved HBM (or MALL, when warm) rate of the median call against the 8 TB/s HBM peak
+        a_["roofline"] = {k: {"GBps": byt / (a_[k]["median_us"] * 1e-6) / 1e9,
+                              "frac": byt / (a_[k]["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                          for k, byt in (("greedy_warm", greedy_bytes), ("greedy_cold", greedy_bytes),
+                                         ("sample_warm", sample_bytes), ("sample_cold", sample_bytes))}
         del tg, dr, wsg
     del flush_buf
 
@@ -384,6 +542,10 @@ def main():
         lmtop[mname] = {"separate_us": sep_ms * 1e3, "fused_us": fused_ms * 1e3, "fused_no_logits_us": nolog_ms * 1e3}
         del wsl, wsg, wst1, lg
     accept["lmhead_top1"] = lmtop
+
+    # ---------------- configs 0-2, one linear at a time (MALL-rotated weight copies)
+    per_linear = linear_rates(qs, W, torch, E)
+    log("per-linear W4A16 M=4 GB/s: " + ", ".join(f"{k}: {v['w4a16_M4']['GBps']:.0f}" for k, v in per_linear.items()))
 
     # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
     # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
@@ -520,6 +682,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         cpu = cpu_baseline(args.cpu_budget_s)
+        cpu["per_config"] = cpu_per_config(args.cpu_budget_s)
+        log(f"oracle per config: {cpu['per_config']['wall_s']:.1f} s")
 
     result = {
         "metric": METRIC,
@@ -551,6 +715,7 @@ def main():
         "draft_verify_top1_agreement": agree,
         "accept_positions_per_s": accept,
         "batched_verify": batched,
+        "per_linear": per_linear,
         "speculative_model": spec,
         "roofline": roof_draft,
         "roofline_verify": roof_verify,
