@@ -320,17 +320,13 @@ def main():
     d = torch.zeros((1, GAMMA), dtype=torch.int32, device=dev)
     u_acc = torch.from_numpy(W.uniforms(rng, (1, GAMMA))).to(dev)
     u_fin = torch.from_numpy(W.uniforms(rng, (1,))).to(dev)
-    ws_draft = torch.empty(chain.workspace_bytes(qs.QS_W4A4, 1), dtype=torch.uint8, device=dev)
-    ws_verify = torch.empty(chain.workspace_bytes(qs.QS_W4A16, M_VERIFY), dtype=torch.uint8, device=dev)
-    ws_acc = torch.zeros(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
+    ws_draft = torch.empty(chain.top1_workspace_bytes(qs.QS_W4A4, 1), dtype=torch.uint8, device=dev)
+    ws_verify = torch.empty(chain.top1_workspace_bytes(qs.QS_W4A16, M_VERIFY), dtype=torch.uint8, device=dev)
     ws_acc2 = torch.zeros(qs.verify_workspace_bytes(1, GAMMA, V), dtype=torch.uint8, device=dev)
-    draft_out = [{
-        "tgt_top1": torch.empty((1, 1), dtype=torch.int32, device=dev), "top1_prob": None,
-        "n_accept": torch.empty((1,), dtype=torch.int32, device=dev), "out_tokens": d[:, i:i + 1],
-    } for i in range(GAMMA)]
+    d_steps = torch.zeros((GAMMA, 1), dtype=torch.int32, device=dev)  # draft step i's token, row i
+    t_verify = torch.empty((M_VERIFY,), dtype=torch.int32, device=dev)
+    p_verify = torch.empty((M_VERIFY,), dtype=torch.float32, device=dev)
     greedy_out = {
-        "tgt_top1": torch.empty((1, M_VERIFY), dtype=torch.int32, device=dev),
-        "top1_prob": torch.empty((1, M_VERIFY), dtype=torch.float32, device=dev),
         "n_accept": torch.empty((1,), dtype=torch.int32, device=dev),
         "out_tokens": torch.empty((1, M_VERIFY), dtype=torch.int32, device=dev),
     }
@@ -341,16 +337,21 @@ def main():
         "final_dist": None,
     }
 
+    # The greedy path never re-reads logits: each draft pass and the verify pass reduce their LM-head
+    # output to the Top-1 in the last stage's epilogue, and acceptance takes the Top-1 ids.  The logits
+    # are still written, for the sampling acceptance the step also runs.
     def draft_phase():
         for i in range(GAMMA):
-            qs.qs_chain_forward(qs.QS_W4A4, x_draft[i], chain, out=logits_q[0, i:i + 1], ws=ws_draft)
-            qs.qs_verify_greedy(logits_q[:, i:i + 1], None, out=draft_out[i], ws=ws_acc)
+            qs.qs_chain_forward_top1(qs.QS_W4A4, x_draft[i], chain, out=logits_q[0, i:i + 1], top1=d_steps[i],
+                                     want_prob=False, ws=ws_draft)
+        d.copy_(d_steps.view(1, GAMMA))
 
     def verify_phase():
-        qs.qs_chain_forward(qs.QS_W4A16, x_verify, chain, out=logits_p[0], ws=ws_verify)
+        qs.qs_chain_forward_top1(qs.QS_W4A16, x_verify, chain, out=logits_p[0], top1=t_verify, top1_prob=p_verify,
+                                 ws=ws_verify)
 
     def accept_phase():
-        qs.qs_verify_greedy(logits_p, d, out=greedy_out, ws=ws_acc)
+        qs.qs_accept_greedy(t_verify.view(1, M_VERIFY), d, out=greedy_out)
         qs.qs_verify_sample(logits_p, logits_q, d, u_acc, u_fin, out=sample_out, ws=ws_acc2)
 
     phases = [draft_phase, verify_phase, accept_phase]
@@ -413,7 +414,7 @@ def main():
             sys.exit(3)
     n_acc = int(greedy_out["n_accept"].item())
     assert bool(torch.isfinite(logits_p).all()) and bool(torch.isfinite(logits_q).all()), "non-finite logits"
-    agree = float((greedy_out["tgt_top1"][:, :GAMMA] == d).float().mean().item())
+    agree = float((t_verify.view(1, M_VERIFY)[:, :GAMMA] == d).float().mean().item())
 
     # ---------------- accept throughput at the batched-verify scale (B=16, gamma=7)
     def time_calls(fn, reps=20):
@@ -542,6 +543,52 @@ def main():
         lmtop[mname] = {"separate_us": sep_ms * 1e3, "fused_us": fused_ms * 1e3, "fused_no_logits_us": nolog_ms * 1e3}
         del wsl, wsg, wst1, lg
     accept["lmhead_top1"] = lmtop
+
+    # Verify pass + greedy acceptance, graph-replayed: the pass writing logits then the greedy verify
+    # kernel reading them, against the pass with the Top-1 fused into its LM-head stage then the prefix
+    # rule on the Top-1 ids (B = 1, gamma = 3: the persistent pass; B = 16, gamma = 7: batched kernels).
+    fused_top1 = {}
+    for (B, G) in ((1, GAMMA), (16, 7)):
+        mm = B * (G + 1)
+        xb = torch.from_numpy(W.activations(W.rng_for(22), mm, H)[0]).to(dev)
+        db = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
+        lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
+        wsc = torch.empty(chain.top1_workspace_bytes(qs.QS_W4A16, mm), dtype=torch.uint8, device=dev)
+        wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+        t1b = torch.empty((mm,), dtype=torch.int32, device=dev)
+        p1b = torch.empty((mm,), dtype=torch.float32, device=dev)
+        go = qs.qs_verify_greedy(lg.view(B, G + 1, V), db, ws=wsg)
+        ao = qs.qs_accept_greedy(t1b.view(B, G + 1), db)
+
+        def separate():
+            qs.qs_chain_forward(qs.QS_W4A16, xb, chain, out=lg, ws=wsc)
+            qs.qs_verify_greedy(lg.view(B, G + 1, V), db, out=go, ws=wsg)
+
+        def fused():
+            qs.qs_chain_forward_top1(qs.QS_W4A16, xb, chain, out=None, want_logits=False, top1=t1b, top1_prob=p1b,
+                                     ws=wsc)
+            qs.qs_accept_greedy(t1b.view(B, G + 1), db, out=ao)
+
+        graphs_ = {}
+        for name, fn in (("separate", separate), ("fused", fused)):
+            fn()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs_[name] = g
+        # interleaved rounds, median of the per-round means (the pass itself varies by ~1% between replays)
+        rounds = {"separate": [], "fused": []}
+        for _ in range(5):
+            for name in ("separate", "fused"):
+                rounds[name].append(time_calls(graphs_[name].replay, reps=8) * 1e3)
+        res = {k: float(np.median(v)) for k, v in rounds.items()}
+        assert bool((go["out_tokens"] == ao["out_tokens"]).all()), "fused and separate greedy paths disagree"
+        fused_top1[f"B{B}_gamma{G}"] = {"M": mm, "separate_us": res["separate"], "fused_us": res["fused"],
+                                        "saved_us": res["separate"] - res["fused"],
+                                        "logit_bytes_not_reread": 4 * mm * V}
+        log(f"verify + greedy, B={B} gamma={G}: pass then greedy kernel {res['separate']:.1f} us, fused Top-1 then "
+            f"accept {res['fused']:.1f} us")
+        del lg, wsc, wsg
 
     # ---------------- configs 0-2, one linear at a time (MALL-rotated weight copies)
     per_linear = linear_rates(qs, W, torch, E)
@@ -701,7 +748,8 @@ def main():
         "config": {
             "workload": ("Llama-3-8B-shaped INT4 (group-128, fp16 scales) 32-layer linear stack + 4096->128256 "
                          "LM-head; one speculative iteration at batch 1, gamma 3: 3 W4A4 draft passes (M=1, "
-                         "int8 MFMA), 1 W4A16 verify pass (M=4, fp16 MFMA), greedy + sampling accept"),
+                         "int8 MFMA), 1 W4A16 verify pass (M=4, fp16 MFMA), each pass's Top-1 fused into its "
+                         "LM-head stage, greedy accept on the Top-1 ids + sampling accept on the logits"),
             "verify_rows": M_VERIFY, "gamma": GAMMA, "batch": 1, "vocab": V,
             "weight_bytes_per_pass": pass_bytes, "graphs": not args.eager,
         },
@@ -714,6 +762,7 @@ def main():
         "iteration_accepted_tokens": n_acc + 1,
         "draft_verify_top1_agreement": agree,
         "accept_positions_per_s": accept,
+        "verify_greedy_fused_top1": fused_top1,
         "batched_verify": batched,
         "per_linear": per_linear,
         "speculative_model": spec,

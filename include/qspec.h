@@ -158,8 +158,9 @@ int qs_lmhead(int mode, const uint16_t* x, const uint8_t* w_packed,
  * greedy section) without a second pass over the logits:
  *   top1[m]      = argmax_v logits[m][v]   (lowest index among equal maxima)
  *   top1_prob[m] = 1 / sum_v exp(logits[m][v] - max)   (softmax, temperature 1)
- * Each 256-column output tile reduces its rows to (max, sum of exp, first
- * argmax); the last tile of a row block merges them in column order.
+ * Each wave of an output tile reduces its 64 columns of every row to (max,
+ * sum of exp, first argmax); a second, small launch merges a row's partials
+ * in column order.
  *   mode       QS_W4A16, QS_W4A4 or QS_W4A8 (arithmetic of that mode's linear)
  *   x          fp16 [M][K];  logits fp32 [M][V] (out, nullable)
  *   top1       int32 [M] (out);  top1_prob fp32 [M] (out, nullable)
@@ -217,6 +218,32 @@ size_t qs_chain_workspace_bytes(int mode, int M, const qs_linear_desc* chain, in
  */
 int qs_chain_forward(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n,
                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_chain_forward_top1 -- qs_chain_forward whose last stage (the LM-head) also
+ * reduces each row of its output to the target's Top-1 inside its epilogue
+ * ([P1] "結果": each mode's Top-1 token and its probability; [P3] greedy
+ * section: greedy acceptance needs only the target's argmax per position), so
+ * a greedy verify needs no second pass over the logits:
+ *   top1[m]      = argmax_v y[m][v]   (lowest index among equal maxima)
+ *   top1_prob[m] = 1 / sum_v exp(y[m][v] - max)   (softmax, temperature 1)
+ * over the fp32 values y that out receives (the same values as
+ * qs_chain_forward's out, whose arithmetic this call shares).
+ *   out        fp32 [M][chain[n-1].N] (out, nullable: the logits are then not
+ *              written)
+ *   top1       int32 [M] (out);  top1_prob fp32 [M] (out, nullable)
+ *   ws         >= qs_chain_top1_workspace_bytes(mode, M, chain, n) bytes of
+ *              scratch (no zero-fill needed)
+ * The persistent pass reduces each workgroup's columns to one partial per row
+ * and the last workgroup to finish merges them; on the per-linear path the
+ * LM-head runs as in qs_lmhead_top1 (partials per wave, then a merge launch).  After a persistent-pass wait
+ * time-out (see qs_set_barrier_timeout_us) top1 holds -1 and top1_prob NaN
+ * for every row whose merge did not run.  Errors as qs_chain_forward.
+ */
+size_t qs_chain_top1_workspace_bytes(int mode, int M, const qs_linear_desc* chain, int n);
+int qs_chain_forward_top1(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n,
+                          float* out, int32_t* top1, float* top1_prob,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Number of persistent pass-kernel launches qs_chain_forward makes for this
@@ -287,6 +314,23 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids,
                      int32_t* tgt_top1, float* top1_prob,
                      int32_t* n_accept, int32_t* out_tokens,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_accept_greedy -- the prefix rule of qs_verify_greedy ([P3] "greedy
+ * decodingでは一致するprefixを採用する"; [P1] "Speculative Decoding") applied to
+ * Top-1 ids already computed, e.g. by qs_chain_forward_top1 over the verify
+ * pass's B * (gamma + 1) rows:
+ *   n = number of leading i < gamma with draft_ids[b][i] == tgt_top1[b][i]
+ *   out_tokens[b] = draft_ids[b][0..n-1], tgt_top1[b][n], then -1 up to
+ *   gamma + 1 entries;  n_accept[b] = n
+ *   tgt_top1   int32 [B][gamma+1];  draft_ids int32 [B][gamma] (may be NULL
+ *              if gamma = 0);  n_accept int32 [B] (out);  out_tokens int32
+ *              [B][gamma+1] (out)
+ * A negative tgt_top1 entry (what a timed-out pass leaves) matches nothing.
+ * One thread per sequence, no workspace.  gamma > 63 -> QS_ERR_UNSUPPORTED.
+ */
+int qs_accept_greedy(const int32_t* tgt_top1, const int32_t* draft_ids, int B, int gamma,
+                     int32_t* n_accept, int32_t* out_tokens, void* stream);
 
 /*
  * qs_verify_greedy_noalloc -- qs_verify_greedy for callers that cannot

@@ -341,21 +341,34 @@ def verify_greedy(tgt_logits: np.ndarray, draft_ids: np.ndarray) -> dict:
     out_tokens [B, gamma+1] padded with -1).
     """
     b, gp1, v = tgt_logits.shape
-    gamma = gp1 - 1
-    d = np.asarray(draft_ids, dtype=np.int64).reshape(b, gamma)
     t, prob = top1(tgt_logits.reshape(b * gp1, v))
     t = t.reshape(b, gp1)
     prob = prob.reshape(b, gp1)
+    acc = greedy_accept(t, draft_ids)
+    return {"t": t, "top1_prob": prob, "n_accept": acc["n_accept"], "out_tokens": acc["out_tokens"]}
+
+
+def greedy_accept(t: np.ndarray, draft_ids: np.ndarray) -> dict:
+    """The prefix rule of greedy verification on the target's Top-1 ids t [B, gamma+1]
+    ([P3] "greedy decodingでは一致するprefixを採用する"): draft token i is accepted while it and
+    every draft token before it equal the target's Top-1 at their positions; the first mismatch
+    (or the position after the last draft token) contributes the target's own Top-1.  A negative
+    t (no Top-1) equals no draft token.  Returns dict(n_accept [B], out_tokens [B, gamma+1]
+    padded with -1)."""
+    t = np.asarray(t, dtype=np.int64)
+    b, gp1 = t.shape
+    gamma = gp1 - 1
+    d = np.asarray(draft_ids, dtype=np.int64).reshape(b, gamma)
     n_accept = np.zeros(b, dtype=np.int64)
     out = np.full((b, gp1), -1, dtype=np.int64)
     for bi in range(b):
         n = 0
-        while n < gamma and d[bi, n] == t[bi, n]:
+        while n < gamma and t[bi, n] >= 0 and d[bi, n] == t[bi, n]:
             n += 1
         out[bi, :n] = d[bi, :n]
         out[bi, n] = t[bi, n]
         n_accept[bi] = n
-    return {"t": t, "top1_prob": prob, "n_accept": n_accept, "out_tokens": out}
+    return {"n_accept": n_accept, "out_tokens": out}
 
 
 def acceptance_probability(p_x: float, q_x: float) -> float:

@@ -154,7 +154,7 @@ int qs_lmhead_top1(int mode, const uint16_t* x, const uint8_t* w_packed, const u
   if (!ws || ws_bytes < lmhead_top1_workspace(mode, M, V, K)) return QS_ERR_WORKSPACE;
   if (!aligned16(ws)) return QS_ERR_MISALIGNED;
   if (!device_info()->ok) return QS_ERR_DEVICE;
-  return launch_lmhead_top1(mode, x, w_packed, s_packed, logits, M, V, K, top1, top1_prob, ws,
+  return launch_lmhead_top1(mode, x, K, 0, w_packed, s_packed, logits, M, V, K, top1, top1_prob, ws,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -185,6 +185,15 @@ int qs_verify_greedy(const float* tgt_logits, const int32_t* draft_ids, int B, i
   if (!device_info()->ok) return QS_ERR_DEVICE;
   return launch_verify_greedy(tgt_logits, draft_ids, B, gamma, V, tgt_top1, top1_prob, n_accept, out_tokens,
                               ws, static_cast<hipStream_t>(stream));
+}
+
+int qs_accept_greedy(const int32_t* tgt_top1, const int32_t* draft_ids, int B, int gamma, int32_t* n_accept,
+                     int32_t* out_tokens, void* stream) {
+  if (!tgt_top1 || !n_accept || !out_tokens || (gamma > 0 && !draft_ids)) return QS_ERR_INVALID_ARG;
+  if (B < 1 || gamma < 0) return QS_ERR_INVALID_ARG;
+  if (gamma > kMaxGamma) return QS_ERR_UNSUPPORTED;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  return launch_accept_greedy(tgt_top1, draft_ids, B, gamma, n_accept, out_tokens, static_cast<hipStream_t>(stream));
 }
 
 int qs_verify_tree_greedy(const float* tgt_logits, const int32_t* tokens, const int32_t* parent, int B, int T,

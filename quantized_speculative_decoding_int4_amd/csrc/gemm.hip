@@ -39,7 +39,6 @@ constexpr int kGemmBlocks = kGemmWaves * kGemmNt;  // row blocks per workgroup (
 constexpr int kGemmMaxSplits = 16;
 constexpr int kGemmMinGroupsPerSplit = 4;
 constexpr int kGemmMaxCounters = 1024;           // split runs have fewer than 256 output tiles
-constexpr int kGemmStatCounters = 64;            // Top-1 epilogue: one per row block (M <= 256)
 
 // Partial slot of one (K split, output tile) workgroup, device-coherent, read back only by the
 // tile's last-arriving workgroup: the accumulators in register order ([wave][mt][nt][lane] float4 or,
@@ -53,18 +52,19 @@ constexpr int kSlotBytes = kSlotStats + kGemmMaxRows * 8;
 static_assert(kSlotBytes % 256 == 0, "slots stay 256-byte aligned");
 
 // 16-row tiles per workgroup: the smallest tile that covers M up to 32 rows, 32 rows beyond that.
-// (64-row tiles measured slower over the Llama-3-8B-shaped stack -- W4A16 M = 64 4.26 ms per pass
-// against 3.66, M = 128 5.41 against 4.98 -- and no longer fit the registers with per-group scaling
-// or fp64 accumulators.)  Rows past 32 are re-read weight tiles that hit the XCD's L2 (see the
-// XCD-aware order below).
-static int gemm_mt(int M, int N) {
-  (void)N;
+// Rows past 32 are re-read weight tiles that hit the XCD's L2 (see the XCD-aware order below).
+// 64-row W4A16 tiles (each expanded weight fragment feeding four MFMAs) measured slower over the
+// Llama-3-8B-shaped stack -- M = 128 5.18 against 4.71 ms per pass, M = 64 4.05 against 3.38 --
+// because their registers leave room for one group of weights in flight, not two.
+static int gemm_mt(int mode, int M) {
+  (void)mode;
   return M <= 16 ? 1 : 2;
 }
-// Waves per SIMD the register budget allows: W4A16 and 16-row integer tiles fit three (at most 168
-// registers), the 32-row integer tile's fp64 accumulators and the Top-1 epilogue need two.
-template <int MODE, int MT, bool STATS>
-constexpr int kGemmOcc = (!STATS && (MODE == 0 || MT == 1)) ? 3 : 2;
+// Waves per SIMD the register budget allows: 16-row tiles and W4A16 32-row tiles with a 2-group
+// ring fit three (at most 168 registers, the standardisation and the Top-1 epilogue included); a
+// deeper ring and the 32-row integer tile's fp64 accumulators need two.
+template <int MODE, bool NORM, int MT, int D, bool STATS>
+constexpr int kGemmOcc = ((MODE == 0 && D <= 2) || MT == 1) ? 3 : 2;
 
 struct GemmArgs {
   const uint16_t* x;   // W4A16: fp16 activations [M][ldx]
@@ -81,12 +81,9 @@ struct GemmArgs {
   float* y;            // fp32 output [M][N] ...
   uint16_t* y16;       // ... or fp16 output with row stride ldy (both NULL: not written)
   int ldy;
-  // Top-1 epilogue (LM-head): per-(row, column tile) softmax-statistics partials [M][tiles],
-  // arrival counter per row block (zero at launch, left zero), per-row Top-1 and its probability
+  // Top-1 epilogue (LM-head): per-(row, column tile, wave) softmax-statistics partials
+  // [M][tiles][4], merged by top1_merge_kernel
   unsigned char* stats;
-  unsigned* stats_cnt;
-  int32_t* top1;
-  float* top1_prob;
 };
 
 __device__ __forceinline__ void gemm_lds_barrier() {
@@ -152,67 +149,67 @@ __device__ __forceinline__ int fragment_code_sum(const uint4 w) {
   return (int)u - 32 * 8;
 }
 
-// Top-1 epilogue of one output tile (see STATS below); values as stored (out32: the integer modes'
-// row scale applied; the LM-head takes no standardisation).
-template <int MT, typename Acc>
-__device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const Acc (&acc)[MT][kGemmNt], int m0,
-                                                   int rb0, int bx, int by, int lane, int wave) {
-  constexpr int kRows = MT * 16;
-  __shared__ Msi wst[kGemmWaves][kRows];
-  __shared__ int last_top1;
+// Top-1 epilogue of one output tile (see STATS below) over the values as stored: value(mt, nt, j,
+// ml) is the output of accumulator element j of (mt, nt) at tile row ml.  Each wave reduces its 64
+// columns of every row to one (max, sum of exp, first argmax) partial and stores it with a plain
+// store: no barrier, no arrival, so the workgroup retires as soon as its stores are issued.  The
+// partials of a row, [row][column tile][wave] in column order, are merged by top1_merge_kernel.
+template <int MT, typename F>
+__device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, F&& value, int m0, int rb0, int by, int lane,
+                                                   int wave) {
+  const size_t parts = (size_t)gridDim.y * kGemmWaves;  // partials per row
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ml = mt * 16 + 4 * (lane >> 4) + j;
-      const int m = m0 + ml < a.M ? m0 + ml : a.M - 1;  // rows past M: computed, never stored
-      const float sx = a.sxf ? a.sxf[m] : 1.0f;
-      Msi t{-INFINITY, 0.0f, 0x7fffffff};
+      Msi t{-INFINITY, 0.0f, 0x7fffffff};  // rows past M: computed, never stored
 #pragma unroll
       for (int nt = 0; nt < kGemmNt; ++nt) {
         const int n = (rb0 + nt) * 16 + (lane & 15);
-        if (n < a.N) t = msi_merge(t, Msi{out32(acc[mt][nt][j], sx), 1.0f, n});
+        if (n < a.N) t = msi_merge(t, Msi{value(mt, nt, j, ml), 1.0f, n});
       }
       // the 16 lanes holding this row: pairs, quads, halves of 8, rows of 16
       t = msi_merge(t, msi_dpp<0xB1>(t));
       t = msi_merge(t, msi_dpp<0x4E>(t));
       t = msi_merge(t, msi_dpp<0x141>(t));
       t = msi_merge(t, msi_dpp<0x140>(t));
-      if ((lane & 15) == 0) wst[wave][ml] = t;
+      if ((lane & 15) == 0 && m0 + ml < a.M)
+        reinterpret_cast<float4_t*>(a.stats)[(size_t)(m0 + ml) * parts + (size_t)by * kGemmWaves + wave] =
+            float4_t{t.m, t.s, __int_as_float(t.i), 0.0f};
     }
   }
-  __syncthreads();
-  const int tiles = (int)gridDim.y;
-  if ((int)threadIdx.x < kRows && m0 + (int)threadIdx.x < a.M) {
-    const int r = (int)threadIdx.x;
-    const Msi t = msi_merge(msi_merge(wst[0][r], wst[1][r]), msi_merge(wst[2][r], wst[3][r]));  // column order
-    const float4_t v{t.m, t.s, __int_as_float(t.i), 0.0f};
-    slot_store4(a.stats, (int)(((size_t)(m0 + r) * tiles + by) * 16), v);
+}
+
+// Row m's Top-1 from its `parts` partials, one workgroup per row: thread t merges partials t, t +
+// 256, ... in order (eight loaded before any is merged, one round trip up to 2048 partials), then
+// a fixed-order merge over the lanes and the four waves.
+__global__ __launch_bounds__(256) void top1_merge_kernel(const float4_t* __restrict__ stats, int parts,
+                                                         int32_t* __restrict__ top1, float* __restrict__ top1_prob) {
+  __shared__ Msi wt[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = (int)blockIdx.x;
+  const float4_t* row = stats + (size_t)m * parts;
+  constexpr int kPer = 8;
+  Msi t{-INFINITY, 0.0f, 0x7fffffff};
+  for (int c0 = 0; c0 < parts; c0 += 256 * kPer) {
+    float4_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int c = c0 + 256 * k + (int)threadIdx.x;
+      v[k] = row[c < parts ? c : parts - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (c0 + 256 * k + (int)threadIdx.x < parts) t = msi_merge(t, Msi{v[k][0], v[k][1], __float_as_int(v[k][2])});
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are in memory
+  t = wave_msi(t);
+  if (lane == 0) wt[wave] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(a.stats_cnt + bx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old + 1u == (unsigned)tiles;
-    if (last) __hip_atomic_store(a.stats_cnt + bx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_top1 = last;
-  }
-  __syncthreads();
-  if (!last_top1) return;
-  // the row block's last tile: one wave per row, lane-strided over the tiles, then a fixed-order
-  // wave merge
-  for (int r = wave; r < kRows && m0 + r < a.M; r += kGemmWaves) {
-    Msi t{-INFINITY, 0.0f, 0x7fffffff};
-    for (int c = lane; c < tiles; c += 64) {
-      const float4_t v = slot_load4(a.stats, (int)(((size_t)(m0 + r) * tiles + c) * 16));
-      const float vm = v[0], vs = v[1], vi = v[2];
-      t = msi_merge(t, Msi{vm, vs, __float_as_int(vi)});
-    }
-    t = wave_msi(t);
-    if (lane == 0) {
-      a.top1[m0 + r] = t.i;
-      if (a.top1_prob) a.top1_prob[m0 + r] = 1.0f / t.s;
-    }
+    t = msi_merge(msi_merge(wt[0], wt[1]), msi_merge(wt[2], wt[3]));
+    top1[m] = t.i;
+    if (top1_prob) top1_prob[m] = 1.0f / t.s;
   }
 }
 
@@ -223,15 +220,13 @@ __device__ __forceinline__ void gemm_top1_epilogue(const GemmArgs& a, const Acc 
 // (a register ring: the weights do not depend on the activations, so they are fetched D groups
 // ahead of their use).
 //
-// STATS (the LM-head's Top-1 epilogue): besides (or instead of) storing the logits, each output
-// tile reduces every row's values to (max, sum of exp(v - max), first argmax) over its 256
-// columns and stores that partial; the last tile of a row block to finish merges the row's
-// partials in column order into its Top-1 and Top-1 probability 1 / sum exp(v - max).  So a greedy
-// step never reads the logits back.
+// STATS (the LM-head's Top-1 epilogue): besides (or instead of) storing the logits, each wave
+// reduces every row's values over its 64 columns to (max, sum of exp(v - max), first argmax) and
+// stores that partial; top1_merge_kernel merges a row's partials in column order into its Top-1
+// and Top-1 probability 1 / sum exp(v - max).  So a greedy step never reads the logits back.
 template <int MODE, bool NORM, int MT, int D, bool STATS>
-__global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, NORM, MT, D, STATS>)) void gemm_kernel(const GemmArgs a) {
   static_assert(MODE == 0 || !NORM, "standardisation is fused for W4A16 only");
-  static_assert(!(NORM && STATS), "the Top-1 epilogue serves the stand-alone LM-head");
   using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
   constexpr int kRows = MT * 16;
   constexpr int kRowB = MODE == 0 ? 256 : 128;  // activation bytes per row and group
@@ -269,7 +264,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
   // Activation staging: thread t copies pieces t + 256 j of the [rows][kRowB] chunk.  Rows past
   // M copy row M-1: result row i depends only on operand row i, and those rows are not stored.
   // (W4A16: piece t + 256 j is row t / 16 + 16 j, so the 16 lanes of a DPP row share a row.)
-  const unsigned char* asrc[kPieces];
+  // Sources as 32-bit byte offsets from the (uniform) activation base: at most 256 rows of 64 Ki
+  // fp16 columns, and they keep the register count low enough that nothing is spilled.
+  const unsigned char* const abase =
+      MODE == 0 ? reinterpret_cast<const unsigned char*>(a.x) : reinterpret_cast<const unsigned char*>(a.xq);
+  uint32_t asrc[kPieces];
   uint32_t adst[kPieces];
   bool aon[kPieces];
 #pragma unroll
@@ -279,8 +278,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
     const int pc = aon[j] ? p : 0;
     const int row = pc / (kRowB / 16), col = pc - row * (kRowB / 16);
     const int r = m0 + row < a.M ? m0 + row : a.M - 1;
-    asrc[j] = MODE == 0 ? reinterpret_cast<const unsigned char*>(a.x + (size_t)r * a.ldx) + col * 16
-                        : reinterpret_cast<const unsigned char*>(a.xq + (size_t)r * a.K) + col * 16;
+    asrc[j] = (uint32_t)(r * (MODE == 0 ? 2 * a.ldx : a.K) + col * 16);
     adst[j] = (uint32_t)(row * kPitch + col * 16);
   }
   // A native vector type: an array of HIP's uint4 struct is copied with memcpy and stays in
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
     const int gg = g < g1 ? g : g1 - 1;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j)
-      if (aon[j]) areg[j] = *reinterpret_cast<const int4_t*>(asrc[j] + (size_t)gg * kRowB);
+      if (aon[j]) areg[j] = *reinterpret_cast<const int4_t*>(abase + asrc[j] + (size_t)gg * kRowB);
   };
   // store the staged group into LDS buffer b; `real` = it is a group of this split (not a re-read
   // past the end)
@@ -304,25 +302,26 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
     if constexpr (NORM) {
       if (real) {
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j) {
+        for (int j = 0; j < kPieces; ++j) {  // fp16 pairs: products exact, sums in fp32
           const half8_t h = __builtin_bit_cast(half8_t, areg[j]);
+          const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = (float)h[e];
-            rsum[j] += f;
-            rsq[j] += f * f;
+          for (int e = 0; e < 4; ++e) {
+            const half2_t p = {h[2 * e], h[2 * e + 1]};
+            rsum[j] = __builtin_amdgcn_fdot2(p, one, rsum[j], false);
+            rsq[j] = __builtin_amdgcn_fdot2(p, p, rsq[j], false);
           }
         }
       }
     }
   };
 
-  // Weight row blocks past N read block 0 (never stored).
-  size_t wbase[kGemmNt];
+  // Weight row blocks past N read block 0 (never stored).  Tile indices fit 32 bits (N / 16 * K / 128).
+  uint32_t wbase[kGemmNt];
 #pragma unroll
   for (int nt = 0; nt < kGemmNt; ++nt) {
     const int rb = rb0 + nt < nrb ? rb0 + nt : 0;
-    wbase[nt] = (size_t)rb * G;
+    wbase[nt] = (uint32_t)(rb * G);
   }
   uint4 wr[D][kGemmNt];
   uint16_t sr[D][kGemmNt];
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
     const int gg = g < g1 ? g : g1 - 1;
 #pragma unroll
     for (int nt = 0; nt < kGemmNt; ++nt) {
-      const size_t t = wbase[nt] + gg;
+      const size_t t = wbase[nt] + (uint32_t)gg;
       wr[slot][nt] = a.w[t * 64 + lane];
       sr[slot][nt] = a.sc[t * 16 + (lane & 15)];
     }
@@ -364,39 +363,32 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
         a_load(gi + 1);  // next group's activations, stored after this group's math
         const unsigned char* ab = abuf[cur];
         if constexpr (MODE == 0) {
-          // each group's exact products summed in fp32 by the MFMAs, then scaled by the group's scale
-          float4_t dg[MT][kGemmNt];
+          // each group's exact products summed in fp32 by the MFMAs, then scaled by the group's scale.
+          // The group's A fragments (every row tile and k-step) are read once and held; the blocks
+          // are then taken one at a time, so only one block's group sums are live.
+          half8_t av[MT][kSteps];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < kGemmNt; ++nt) dg[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < kSteps; ++t) {
-            half8_t b[kGemmNt];
-#pragma unroll
-            for (int nt = 0; nt < kGemmNt; ++nt) {
-              const uint4 wv = wr[i][nt];
-              const uint32_t wt = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
-              b[nt] = unpack_f16x8(wt, magic);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const half8_t av = *reinterpret_cast<const half8_t*>(ab + lane_off + mt * 16 * kPitch + 16 * t);
-#pragma unroll
-              for (int nt = 0; nt < kGemmNt; ++nt)
-                dg[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], dg[mt][nt], 0, 0, 0);
-            }
-          }
+            for (int t = 0; t < kSteps; ++t)
+              av[mt][t] = *reinterpret_cast<const half8_t*>(ab + lane_off + mt * 16 * kPitch + 16 * t);
 #pragma unroll
           for (int nt = 0; nt < kGemmNt; ++nt) {
+            float4_t dg[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) dg[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            const uint4 wv = wr[i][nt];
+#pragma unroll
+            for (int t = 0; t < kSteps; ++t) {
+              const half8_t b = unpack_f16x8(t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w, magic);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) dg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt][t], b, dg[mt], 0, 0, 0);
+            }
             const float s = h2f(sr[i][nt]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt][nt] += s * dg[mt][nt];
-          }
-          if constexpr (NORM) {
-#pragma unroll
-            for (int nt = 0; nt < kGemmNt; ++nt)  // exact product; the weights' own sum, unrounded
-              csum[nt] += h2f(sr[i][nt]) * (float)fragment_code_sum(wr[i][nt]);
+            for (int mt = 0; mt < MT; ++mt) acc[mt][nt] += s * dg[mt];
+            if constexpr (NORM)  // exact product; the weights' own sum, unrounded
+              csum[nt] += s * (float)fragment_code_sum(wv);
           }
         } else {
           int4_t dg[MT][kGemmNt];
@@ -583,7 +575,18 @@ __global__ __launch_bounds__(kGemmWaves * 64, (kGemmOcc<MODE, MT, STATS>)) void 
       }
     }
   }
-  if constexpr (STATS) gemm_top1_epilogue<MT, Acc>(a, acc, m0, rb0, bx, by, lane, wave);
+  if constexpr (STATS) {
+    // the values as stored: standardised (NORM) or with the integer modes' row scale applied
+    auto value = [&](int mt, int nt, int j, int ml) __attribute__((always_inline)) {
+      if constexpr (NORM) {
+        return (acc[mt][nt][j] - row_mu[ml] * csum[nt]) * row_inv[ml];
+      } else {
+        const int m = m0 + ml < a.M ? m0 + ml : a.M - 1;
+        return out32(acc[mt][nt][j], MODE == 1 ? a.sxf[m] : 1.0f);
+      }
+    };
+    gemm_top1_epilogue<MT>(a, value, m0, rb0, by, lane, wave);
+  }
 }
 
 __global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ cnt, int n) {
@@ -594,69 +597,70 @@ __global__ __launch_bounds__(256) void gemm_clear_kernel(unsigned* __restrict__ 
 
 // K splits for an M x N x K linear: enough workgroups for a 256-CU part, at least
 // kGemmMinGroupsPerSplit groups per split.
-static int gemm_tiles(int M, int N) {
-  const int rows = gemm_mt(M, N) * 16;
+static int gemm_tiles(int mode, int M, int N) {
+  const int rows = gemm_mt(mode, M) * 16;
   return (((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks) * ((M + rows - 1) / rows);
 }
 
-int gemm_splits(int M, int N, int K) {
-  const int tiles = gemm_tiles(M, N);
+int gemm_splits(int mode, int M, int N, int K) {
+  const int tiles = gemm_tiles(mode, M, N);
   const int G = K / kGroup;
   int s = 1;
   while (s < kGemmMaxSplits && tiles * s < 256 && G / (2 * s) >= kGemmMinGroupsPerSplit) s *= 2;
   return s;
 }
 
-size_t gemm_counter_bytes() { return align_up((size_t)(kGemmMaxCounters + kGemmStatCounters) * 4, 256); }
+size_t gemm_counter_bytes() { return align_up((size_t)kGemmMaxCounters * 4, 256); }
 
 size_t gemm_top1_bytes(int M, int N) {
   const size_t ntiles = (size_t)((N + 15) / 16 + kGemmBlocks - 1) / kGemmBlocks;
-  return align_up((size_t)M * ntiles * 16, 256);
+  return align_up((size_t)M * ntiles * kGemmWaves * 16, 256);
 }
 
-size_t gemm_workspace(int M, int N, int K) {
-  const int s = gemm_splits(M, N, K);
+size_t gemm_workspace(int mode, int M, int N, int K) {
+  const int s = gemm_splits(mode, M, N, K);
   if (s <= 1) return 0;
-  return (size_t)s * gemm_tiles(M, N) * kSlotBytes;
+  return (size_t)s * gemm_tiles(mode, M, N) * kSlotBytes;
 }
 
 int launch_gemm_clear(unsigned* cnt, hipStream_t st) {
-  hipLaunchKernelGGL(gemm_clear_kernel, dim3(1), dim3(256), 0, st, cnt, kGemmMaxCounters + kGemmStatCounters);
+  hipLaunchKernelGGL(gemm_clear_kernel, dim3(1), dim3(256), 0, st, cnt, kGemmMaxCounters);
   return launch_status();
 }
 
 template <int MODE, bool NORM, int MT, int D>
 static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (!NORM) {
-    if (a.stats) {
-      hipLaunchKernelGGL((gemm_kernel<MODE, false, MT, D, true>), grid, dim3(kGemmWaves * 64), 0, st, a);
-      return;
-    }
+  if (a.stats) {
+    hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D, true>), grid, dim3(kGemmWaves * 64), 0, st, a);
+    return;
   }
   hipLaunchKernelGGL((gemm_kernel<MODE, NORM, MT, D, false>), grid, dim3(kGemmWaves * 64), 0, st, a);
 }
 
 // Weight ring depth per row tile: 16-row tiles a 3-group (W4A16, whose per-group sums take registers)
-// or 4-group ring, 32-row tiles a 2-group ring.
+// or 4-group ring, 32-row tiles a QS_GEMM_MT2_RING-group ring.
+#ifndef QS_GEMM_MT2_RING
+#define QS_GEMM_MT2_RING 2
+#endif
 template <int MODE, bool NORM>
 static void gemm_launch_mt(const GemmArgs& a, int mt, dim3 grid, hipStream_t st) {
   if (mt == 1)
     gemm_launch_one<MODE, NORM, 1, MODE == 0 ? 3 : 4>(a, grid, st);
   else
-    gemm_launch_one<MODE, NORM, 2, 2>(a, grid, st);
+    gemm_launch_one<MODE, NORM, 2, QS_GEMM_MT2_RING>(a, grid, st);
 }
 
 int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* xq, const float* sxf,
                 const uint8_t* wp, const uint16_t* sp, int M, int N, int K, float* y, uint16_t* y16, int ldy,
                 unsigned* cnt, void* ws, size_t ws_bytes, hipStream_t st, const GemmTop1* t1) {
-  if (t1 && (norm || !cnt || !t1->stats || !t1->top1)) return QS_ERR_INVALID_ARG;
+  if (t1 && (!t1->stats || !t1->top1)) return QS_ERR_INVALID_ARG;
   if (mode != QS_W4A16 && norm) return QS_ERR_INVALID_ARG;
   // split K only when the caller's scratch holds the partial slots and the (zeroed) counters;
   // results then differ from the unsplit order by fp32 rounding only
-  const size_t need = gemm_workspace(M, N, K);
-  const int splits = need > 0 && cnt != nullptr && ws != nullptr && ws_bytes >= need ? gemm_splits(M, N, K) : 1;
+  const size_t need = gemm_workspace(mode, M, N, K);
+  const int splits = need > 0 && cnt != nullptr && ws != nullptr && ws_bytes >= need ? gemm_splits(mode, M, N, K) : 1;
   const int G = K / kGroup;
-  const int mt = gemm_mt(M, N);
+  const int mt = gemm_mt(mode, M);
   GemmArgs a{};
   a.x = x;
   a.ldx = ldx;
@@ -674,12 +678,7 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
   a.y = y;
   a.y16 = y16;
   a.ldy = ldy;
-  if (t1) {
-    a.stats = t1->stats;
-    a.stats_cnt = cnt + kGemmMaxCounters;
-    a.top1 = t1->top1;
-    a.top1_prob = t1->top1_prob;
-  }
+  if (t1) a.stats = t1->stats;
   const int nrb = (N + 15) / 16;
   const dim3 grid((M + mt * 16 - 1) / (mt * 16), (nrb + kGemmBlocks - 1) / kGemmBlocks, a.splits);
   if (a.splits > 1 && (int)(grid.x * grid.y) > kGemmMaxCounters) return QS_ERR_UNSUPPORTED;
@@ -690,6 +689,13 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
       gemm_launch_mt<0, false>(a, mt, grid, st);
   } else {
     gemm_launch_mt<1, false>(a, mt, grid, st);
+  }
+  if (t1) {
+    const int rc = launch_status();
+    if (rc != QS_OK) return rc;
+    hipLaunchKernelGGL(top1_merge_kernel, dim3((unsigned)M), dim3(256), 0, st,
+                       reinterpret_cast<const float4_t*>(t1->stats), (int)grid.y * kGemmWaves, t1->top1,
+                       t1->top1_prob);
   }
   return launch_status();
 }

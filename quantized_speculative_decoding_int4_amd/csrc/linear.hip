@@ -520,7 +520,7 @@ static size_t counter_bytes(int mode, int M) { return use_gemm(mode, M, nullptr)
 
 size_t linear_workspace(int mode, int M, int N, int K, bool norm_in) {
   const size_t stage = staging_bytes(mode, M, K, norm_in);
-  return counter_bytes(mode, M) + stage + (use_gemm(mode, M, nullptr) ? gemm_workspace(M, N, K) : 0);
+  return counter_bytes(mode, M) + stage + (use_gemm(mode, M, nullptr) ? gemm_workspace(mode, M, N, K) : 0);
 }
 
 int linear_clear_counters(int mode, int M, void* ws, hipStream_t st) {
@@ -619,27 +619,29 @@ static size_t top1_stage_bytes(int mode, int M, int K) {
 }
 
 size_t lmhead_top1_workspace(int mode, int M, int V, int K) {
-  return gemm_counter_bytes() + top1_stage_bytes(mode, M, K) + gemm_workspace(M, V, K) +
+  return gemm_counter_bytes() + top1_stage_bytes(mode, M, K) + gemm_workspace(mode, M, V, K) +
          gemm_top1_bytes(M, V);
 }
 
-int launch_lmhead_top1(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* logits, int M,
-                       int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st) {
+int launch_lmhead_top1(int mode, const uint16_t* x, int ldx, int norm, const uint8_t* wp, const uint16_t* sp,
+                       float* logits, int M, int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st) {
   unsigned char* base = static_cast<unsigned char*>(ws);
   unsigned* cnt = reinterpret_cast<unsigned*>(base);
   unsigned char* stg = base + gemm_counter_bytes();
   unsigned char* slots = stg + top1_stage_bytes(mode, M, K);
-  const size_t slot_bytes = gemm_workspace(M, V, K);
+  const size_t slot_bytes = gemm_workspace(mode, M, V, K);
   GemmTop1 t1{slots + slot_bytes, top1, top1_prob};
   if (mode == QS_W4A16)
-    return launch_gemm(QS_W4A16, false, x, K, nullptr, nullptr, wp, sp, M, V, K, logits, nullptr, V, cnt, slots,
-                       slot_bytes, st, &t1);
+    return launch_gemm(QS_W4A16, norm != 0, x, ldx, nullptr, nullptr, wp, sp, M, V, K, logits, nullptr, V, cnt,
+                       slots, slot_bytes, st, &t1);
   int8_t* xq_op = reinterpret_cast<int8_t*>(stg);
   float* sxf = reinterpret_cast<float*>(stg + align_up((size_t)M * K, 256));
   if (mode == QS_W4A4)
-    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(kAqThreads), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+    hipLaunchKernelGGL(act_quant_kernel<7>, dim3(M), dim3(kAqThreads), 0, st, x, K, ldx, norm, xq_op, sxf, nullptr,
+                       nullptr);
   else
-    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(kAqThreads), 0, st, x, K, K, 0, xq_op, sxf, nullptr, nullptr);
+    hipLaunchKernelGGL(act_quant_kernel<127>, dim3(M), dim3(kAqThreads), 0, st, x, K, ldx, norm, xq_op, sxf, nullptr,
+                       nullptr);
   const int rc = launch_status();
   if (rc != QS_OK) return rc;
   return launch_gemm(mode, false, nullptr, 0, xq_op, sxf, wp, sp, M, V, K, logits, nullptr, V, cnt, slots,
@@ -685,7 +687,7 @@ int launch_linear_io(int mode, const LinearIO& io, const uint8_t* wp, const uint
   unsigned* cnt = pre > 0 && ws != nullptr && ws_bytes >= pre ? static_cast<unsigned*>(ws) : nullptr;
   if (cnt && !io.counters_zero) {
     // counters of a workspace not known to be clear; only needed if the GEMM splits K
-    if (gemm && gemm_workspace(M, N, K) > 0 && ws_bytes >= pre + need + gemm_workspace(M, N, K)) {
+    if (gemm && gemm_workspace(mode, M, N, K) > 0 && ws_bytes >= pre + need + gemm_workspace(mode, M, N, K)) {
       const int rc = launch_gemm_clear(cnt, st);
       if (rc != QS_OK) return rc;
     }

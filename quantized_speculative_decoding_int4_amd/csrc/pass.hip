@@ -60,6 +60,7 @@
 #include "qs_act.h"
 #include "qs_device.h"
 #include "qs_internal.h"
+#include "qs_msi.h"
 
 #include <atomic>
 #include <type_traits>
@@ -120,8 +121,16 @@ struct PassArgs {
   const uint16_t* x;  // input of the launch's first stage, fp16, row stride ldx0 (complete at launch)
   int ldx0;
   int norm0;          // standardise the first stage's input rows
-  float* out;         // fp32 output of the launch's last stage when last_is_final
+  float* out;         // fp32 output of the launch's last stage when last_is_final (nullable)
   int last_is_final;
+  // Top-1 epilogue of the final stage (the LM-head), when top1 is not NULL: per row, the lowest
+  // index of the largest output and 1 / sum exp(y - max).  Each workgroup reduces its columns to
+  // a (max, sum of exp, argmax) partial per row in t1_stats [M][grid] (16 bytes each); the last
+  // workgroup to arrive at t1_cnt (zero at pass start) merges them.
+  int32_t* top1;
+  float* top1_prob;   // nullable
+  unsigned char* t1_stats;
+  unsigned* t1_cnt;
   unsigned* flags;    // W4A16: per-workgroup arrival epochs (kFlagStride apart), zero at pass start
   unsigned epoch0;    // W4A16: epochs of this launch's boundaries are epoch0 + 1, epoch0 + 2, ...
   unsigned* error;    // set to 1 if a wait passed its deadline
@@ -257,6 +266,86 @@ __device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned v, con
   return true;
 }
 
+// Top-1 epilogue of the final stage, run by every control wave of every workgroup (also one
+// without columns in the stage, so that all workgroups arrive).  No workgroup barrier: the
+// streaming waves may already have ended.  The wave's 16-lane rows are merged by DPP; the last
+// control wave of the workgroup to arrive (an LDS counter) merges the waves' partials in wave
+// order and publishes the workgroup's partial per row; the last workgroup to arrive merges the
+// partials of all workgroups, lanes strided over them, then a fixed-order lane merge.
+struct Top1Out {
+  int32_t* top1;
+  float* top1_prob;
+  unsigned char* stats;
+  unsigned* cnt;
+};
+__device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], float4_t (*t1_wave)[4],
+                                              unsigned* t1_arrive, int cw, int lane, int bid, int grid, int M) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Msi t = t1v[j];
+    t = msi_merge(t, msi_dpp<0xB1>(t));
+    t = msi_merge(t, msi_dpp<0x4E>(t));
+    t = msi_merge(t, msi_dpp<0x141>(t));
+    t = msi_merge(t, msi_dpp<0x140>(t));
+    if (lane == 0) t1_wave[cw][j] = float4_t{t.m, t.s, __int_as_float(t.i), 0.0f};
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's partials are in LDS
+  unsigned old = 0u;
+  if (lane == 0) old = __hip_atomic_fetch_add(t1_arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = (unsigned)__builtin_amdgcn_readfirstlane((int)old);
+  asm volatile("" ::: "memory");
+  if (old != (unsigned)(kCW - 1)) return;
+  // the workgroup's last control wave: lane m merges row m over the waves, in wave order
+  const __amdgpu_buffer_rsrc_t rs = sc1_rsrc(o.stats, (uint32_t)(M * grid * 16));
+  if (lane < M) {
+    Msi t{-INFINITY, 0.0f, 0x7fffffff};
+    for (int w = 0; w < kCW; ++w) {
+      const float4_t v = t1_wave[w][lane];
+      t = msi_merge(t, Msi{v[0], v[1], __float_as_int(v[2])});
+    }
+    const float4_t pv{t.m, t.s, __int_as_float(t.i), 0.0f};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4_t, pv), rs, (lane * grid + bid) * 16, 0, kSc1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partials are in memory
+  unsigned prev = 0u;
+  if (lane == 0) prev = __hip_atomic_fetch_add(o.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = (unsigned)__builtin_amdgcn_readfirstlane((int)prev);
+  asm volatile("" ::: "memory");
+  if (prev + 1u != (unsigned)grid) return;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) t1v[m] = Msi{-INFINITY, 0.0f, 0x7fffffff};
+  // the last workgroup: every row over all workgroups (lane c takes workgroups c, c + 64, ...).  The
+  // partials of all rows are loaded before any is merged, so they cost one round trip (buffer loads
+  // past the extent return zeros and are not merged).
+  constexpr int kPer = 4;  // workgroups per lane and round
+  for (int c0 = 0; c0 < grid; c0 += 64 * kPer) {
+    float4_t v[4][kPer];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int c = c0 + 64 * k + lane;
+        v[m][k] = m < M ? __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (m * grid + c) * 16, 0, kSc1))
+                        : float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (c0 + 64 * k + lane < grid) t1v[m] = msi_merge(t1v[m], Msi{v[m][k][0], v[m][k][1], __float_as_int(v[m][k][2])});
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m < M) {
+      const Msi t = wave_msi(t1v[m]);
+      if (lane == 0) {
+        o.top1[m] = t.i;
+        if (o.top1_prob) o.top1_prob[m] = 1.0f / t.s;
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // Partials of the streaming waves: fp32 (W4A16) or fp64 (the integer modes: exact sums).
@@ -270,6 +359,8 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   __shared__ __align__(16) uint32_t zero_pad[16];
   __shared__ __align__(16) uint32_t ones_pad[16];  // fp16 1.0 pairs: the W4A16 row-sum operand
   __shared__ int fail_sh;
+  __shared__ float4_t t1_wave[kCW][4];             // Top-1 epilogue: per control wave and row
+  __shared__ unsigned t1_arrive;                   // control waves done with their Top-1 partials
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -423,7 +514,10 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // ======================= control waves =======================
   const int ct = (int)threadIdx.x - 64 * kSW;  // 0 .. kCT-1
   const int cw = wave - kSW;
-  if (ct == 0) fail_sh = 0;
+  if (ct == 0) {
+    fail_sh = 0;
+    t1_arrive = 0u;
+  }
   if (ct < 16) {
     zero_pad[ct] = 0u;
     ones_pad[ct] = 0x3C003C00u;
@@ -617,6 +711,11 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     const PassStage ps = stage_at(s);
     const int sets = stage_sets(ps, bid, grid);
     const bool final_out = a.last_is_final && s + 1 == a.n_stages;
+    const bool want_t1 = final_out && a.top1 != nullptr;
+    // Top-1 partials of this lane's rows j (lanes 0-15 hold rows 0..M-1, column lane & 15)
+    Msi t1v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t1v[j] = Msi{-INFINITY, 0.0f, 0x7fffffff};
     if (sets > 0) {
       // sum, in a fixed order, the S partials of each (set, row block) and store the outputs
       const int S = 1 << ps.s_log2, R = kSW >> ps.s_log2;
@@ -651,7 +750,8 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
                 h = f64_to_f16_rn(o64);
               }
               if (final_out) {
-                a.out[(size_t)m * N + n] = outv;
+                if (a.out) a.out[(size_t)m * N + n] = outv;
+                if (want_t1) t1v[j] = msi_merge(t1v[j], Msi{outv, 1.0f, n});
               } else {  // device-coherent store, read by other workgroups in the next stage
                 if (h == kEmpty) h = 0x7E00u;
                 __hip_atomic_store(ps.y16 + (size_t)m * N + n, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -661,6 +761,8 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         }
       }
     }
+    if (want_t1) top1_epilogue(Top1Out{a.top1, a.top1_prob, a.t1_stats, a.t1_cnt}, t1v, t1_wave, &t1_arrive, cw, lane,
+                               bid, grid, M);
     if constexpr (MODE == 0) {
       if (s + 1 < a.n_stages) {  // grid barrier: all outputs of stage s are in memory
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's output stores have completed
@@ -677,11 +779,18 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   }
 }
 
-// Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores) and the
-// final output with NaN, and zeroes the control words (a reserved word and the error word, then
-// n_flags arrival flags kFlagStride apart).
+// Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores), the
+// final output with NaN and the Top-1 outputs with -1 and NaN, and zeroes the control words (the
+// Top-1 arrival counter and the error word, then n_flags arrival flags kFlagStride apart).
 __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags,
-                                                         float* out, uint32_t n_out) {
+                                                         float* out, uint32_t n_out, int32_t* top1, float* top1_prob,
+                                                         int n_top1) {
+  if (blockIdx.x == 0 && top1) {
+    for (int i = threadIdx.x; i < n_top1; i += 256) {
+      top1[i] = -1;
+      if (top1_prob) top1_prob[i] = __builtin_nanf("");
+    }
+  }
   if (blockIdx.x == 0) {
     if (threadIdx.x < 2) __hip_atomic_store(ctrl + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = threadIdx.x; i < n_flags; i += 256)
@@ -691,8 +800,10 @@ __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n
   const int4_t e = int4_t{-1, -1, -1, -1};
   for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += gridDim.x * 256u)
     __builtin_amdgcn_raw_buffer_store_b128(e, r, (int)(i * 16u), 0, kSc1);
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n_out; i += gridDim.x * 256u)
-    out[i] = __builtin_nanf("");
+  if (out) {
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n_out; i += gridDim.x * 256u)
+      out[i] = __builtin_nanf("");
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -741,12 +852,14 @@ static int pick_pass_split(int N, int K, int grid) {
 
 int pass_launch_count(int n) { return (n + kMaxPassStages - 1) / kMaxPassStages; }
 
+size_t pass_top1_bytes(int M) { return align_up((size_t)M * kMaxPassWorkgroups * 16, 256); }
+
 static std::atomic<int> g_barrier_timeout_us{200000};
 int pass_barrier_timeout_us() { return g_barrier_timeout_us.load(); }
 void set_pass_barrier_timeout_us(int us) { g_barrier_timeout_us.store(us); }
 
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                unsigned* ctrl, uint16_t* stage_out, hipStream_t st) {
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1) {
   const DeviceInfo* di = device_info();
   const int grid = di->num_cus;
   auto fn0 = pass_kernel<0>;
@@ -774,13 +887,13 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   const size_t sb = pass_stage_bytes(M, c, n);
   if (sb > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
   const uint32_t n16 = mode != QS_W4A16 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
-  const size_t n_out = (size_t)M * c[n - 1].N;
+  const size_t n_out = out ? (size_t)M * c[n - 1].N : 0;
   if (n_out > 0xFFFFFFFFu) return QS_ERR_UNSUPPORTED;
   const size_t work = (size_t)n16 + n_out / 4;
   const unsigned rblocks = (unsigned)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
   hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st,
                      reinterpret_cast<uint4*>(stage_out), n16, ctrl, mode == QS_W4A16 ? grid : 0, out,
-                     (uint32_t)n_out);
+                     (uint32_t)n_out, t1 ? t1->top1 : nullptr, t1 ? t1->top1_prob : nullptr, M);
   int rc = launch_status();
   if (rc != QS_OK) return rc;
 
@@ -804,6 +917,12 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     }
     a.out = out;
     a.last_is_final = s0 + cnt == n;
+    if (t1 && a.last_is_final) {
+      a.top1 = t1->top1;
+      a.top1_prob = t1->top1_prob;
+      a.t1_stats = t1->stats;
+      a.t1_cnt = ctrl;  // the control region's first word
+    }
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
     a.epoch0 = (unsigned)s0;

@@ -28,10 +28,12 @@ int launch_linear(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t
                   float* y, int M, int N, int K, int8_t* xq_out, uint16_t* sx_out,
                   int32_t* acc_out, void* ws, size_t ws_bytes, hipStream_t st);
 
-// LM-head with the fused Top-1 epilogue (batched kernel at any M): logits nullable.
+// LM-head with the fused Top-1 epilogue (batched kernel at any M): x fp16 [M][ldx], its rows
+// standardised first when norm (the chain's last stage); logits nullable.  The workspace starts
+// with the batched kernel's arrival counters (zero before the call, left zero).
 size_t lmhead_top1_workspace(int mode, int M, int V, int K);
-int launch_lmhead_top1(int mode, const uint16_t* x, const uint8_t* wp, const uint16_t* sp, float* logits, int M,
-                       int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st);
+int launch_lmhead_top1(int mode, const uint16_t* x, int ldx, int norm, const uint8_t* wp, const uint16_t* sp,
+                       float* logits, int M, int V, int K, int32_t* top1, float* top1_prob, void* ws, hipStream_t st);
 
 // Input/output placement of one linear inside a chain: x with row stride ldx, optionally
 // standardised per row; output either fp32 y [M][N] or fp16(y) into y16 with row stride ldy.
@@ -57,10 +59,10 @@ int linear_clear_counters(int mode, int M, void* ws, hipStream_t st);
 // fp32 y [M][N] or fp16 y16 (row stride ldy).  K is split over workgroups when cnt (zeroed arrival
 // counters, left zero) and ws (partial slots of gemm_workspace bytes) are given.
 size_t gemm_counter_bytes();
-size_t gemm_workspace(int M, int N, int K);
+size_t gemm_workspace(int mode, int M, int N, int K);
 int launch_gemm_clear(unsigned* cnt, hipStream_t st);
 // Top-1 epilogue of the batched kernel (LM-head): stats holds gemm_top1_bytes of partials, top1 [M],
-// top1_prob [M] (nullable); the counters behind cnt must be zero and are left zero.
+// top1_prob [M] (nullable), written by a merge launch that follows the linear's.
 struct GemmTop1 {
   unsigned char* stats;
   int32_t* top1;
@@ -75,8 +77,8 @@ int launch_gemm(int mode, bool norm, const uint16_t* x, int ldx, const int8_t* x
 // linears of a chain per launch.
 constexpr int kMaxPassStages = 72;
 constexpr int kMaxPassWorkgroups = 1024;
-// Control region of a persistent pass in the workspace: a reserved word and the error word, then
-// one 128-byte arrival flag per workgroup.
+// Control region of a persistent pass in the workspace: the Top-1 arrival counter and the error
+// word, then one 128-byte arrival flag per workgroup.
 constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
 int pass_max_rows(int mode);   // most rows a persistent pass takes in this mode
@@ -85,13 +87,24 @@ int pass_launch_count(int n);  // launches of a persistent pass over n linears
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n);
 int pass_barrier_timeout_us();  // wall-clock limit of one wait for a stage's input (process-wide)
 void set_pass_barrier_timeout_us(int us);
+// Top-1 of the final stage (the LM-head): top1 [M], top1_prob [M] (nullable), and stats, the
+// partials of pass_top1_bytes(M) bytes.
+struct PassTop1 {
+  int32_t* top1;
+  float* top1_prob;
+  unsigned char* stats;
+};
+size_t pass_top1_bytes(int M);
+// out nullable when t1 is given
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                unsigned* ctrl, uint16_t* stage_out, hipStream_t st);
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1 = nullptr);
 
 size_t verify_workspace(int B, int gamma, int V);
 size_t verify_counter_bytes();  // the arrival counters at the start of a verify workspace
 int launch_verify_greedy(const float* tgt, const int32_t* d, int B, int gamma, int V,
                          int32_t* t, float* p1, int32_t* n_acc, int32_t* out, void* ws,
+                         hipStream_t st);
+int launch_accept_greedy(const int32_t* t, const int32_t* d, int B, int gamma, int32_t* n_acc, int32_t* out,
                          hipStream_t st);
 int launch_verify_tree_greedy(const float* tgt, const int32_t* tok, const int32_t* par, int B, int T, int V,
                               int32_t* t, int32_t* n_acc, int32_t* out, int32_t* nodes, void* ws, hipStream_t st);

@@ -41,7 +41,10 @@ constexpr int kVThreads = 256;
 // once, not once per round of workgroups.  Draw workgroups take 2048 (8 per thread): their fp64
 // exponentials are slow, and a sequence's draw runs two of them back to back (its chunk sums, then
 // the search inside the chosen chunk), so shorter chunks shorten that path.
-constexpr int kStatPerThread = 32;
+#ifndef QS_VERIFY_STAT_PER_THREAD
+#define QS_VERIFY_STAT_PER_THREAD 32
+#endif
+constexpr int kStatPerThread = QS_VERIFY_STAT_PER_THREAD;
 constexpr int kStatChunk = kVThreads * kStatPerThread;
 constexpr int kPerThread = 8;
 constexpr int kChunk = kVThreads * kPerThread;
@@ -826,6 +829,33 @@ static int sample_block(const float* tgt, const float* drf, const int32_t* d, co
     hipLaunchKernelGGL(sample_final_kernel<false>, dim3((unsigned)fb), dim3(kVThreads), 0, st, tgt, drf,
                        gamma, V, C, w.info, w.csum, u_fin, out, fdist);
   }
+  return launch_status();
+}
+
+// Greedy acceptance from Top-1 ids already computed (the LM-head epilogue of a verify pass): one
+// thread per sequence applies the prefix rule of greedy_kernel.  A negative Top-1 (what a timed-out
+// pass leaves) matches no draft token.
+__global__ __launch_bounds__(256) void accept_greedy_kernel(const int32_t* __restrict__ t,
+                                                            const int32_t* __restrict__ draft, int B, int gamma,
+                                                            int32_t* __restrict__ n_acc, int32_t* __restrict__ out) {
+  const int b = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (b >= B) return;
+  const int rows = gamma + 1;
+  const int32_t* tb = t + (size_t)b * rows;
+  const int32_t* db = draft + (size_t)b * gamma;  // not read when gamma = 0
+  int na = 0;
+  while (na < gamma && tb[na] >= 0 && db[na] == tb[na]) ++na;
+  int32_t* o = out + (size_t)b * rows;
+  for (int i = 0; i < na; ++i) o[i] = db[i];
+  o[na] = tb[na];
+  for (int i = na + 1; i < rows; ++i) o[i] = -1;
+  n_acc[b] = na;
+}
+
+int launch_accept_greedy(const int32_t* t, const int32_t* d, int B, int gamma, int32_t* n_acc, int32_t* out,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(accept_greedy_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, t, d, B, gamma,
+                     n_acc, out);
   return launch_status();
 }
 

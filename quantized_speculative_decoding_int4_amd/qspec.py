@@ -49,6 +49,9 @@ _SIGS = {
     "qs_verify_workspace_bytes": ([_i, _i, _i], _sz),
     "qs_chain_workspace_bytes": ([_i, _i, _p, _i], _sz),
     "qs_chain_forward": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p], _i),
+    "qs_chain_top1_workspace_bytes": ([_i, _i, _p, _i], _sz),
+    "qs_chain_forward_top1": ([_i, _p, _i, _p, _i, _p, _p, _p, _p, _sz, _p], _i),
+    "qs_accept_greedy": ([_p, _p, _i, _i, _p, _p, _p], _i),
     "qs_chain_pass_launches": ([_i, _i, _p, _i], _i),
     "qs_set_barrier_timeout_us": ([_i], _i),
     "qs_chain_pass_status": ([_i, _i, _p, _i, _p, _sz, _p, _p], _i),
@@ -365,6 +368,10 @@ class Chain:
     def workspace_bytes(self, mode: int, m: int) -> int:
         return _lib.qs_chain_workspace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
 
+    def top1_workspace_bytes(self, mode: int, m: int) -> int:
+        """Workspace of qs_chain_forward_top1."""
+        return _lib.qs_chain_top1_workspace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
+
     def pass_launches(self, mode: int, m: int) -> int:
         """Persistent pass-kernel launches of qs_chain_forward (0: one launch per linear)."""
         rc = _lib.qs_chain_pass_launches(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
@@ -400,4 +407,48 @@ def qs_chain_forward(mode: int, x, chain: Chain, out=None, ws=None):
         mode, _ptr(x, torch.float16, (m, k), "x"), m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n,
         _ptr(out, torch.float32, (m, chain.out_features), "out"), _ptr(ws, torch.uint8, None, "ws"),
         ws.numel(), _stream()))
+    return out
+
+
+def qs_chain_forward_top1(mode: int, x, chain: Chain, out=None, want_logits=True, top1=None, top1_prob=None,
+                          want_prob=True, ws=None):
+    """x fp16 [M, chain.in_features] -> (out fp32 [M, chain.out_features] or None, top1 int32 [M],
+    top1_prob fp32 [M] or None): the chain with the LM-head's Top-1 fused into its last stage."""
+    m, k = x.shape
+    if k != chain.in_features:
+        raise ValueError("x width does not match the first linear")
+    dev = x.device
+    if out is None and want_logits:
+        out = torch.empty((m, chain.out_features), dtype=torch.float32, device=dev)
+    if top1 is None:
+        top1 = torch.empty((m,), dtype=torch.int32, device=dev)
+    if top1_prob is None and want_prob:
+        top1_prob = torch.empty((m,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(chain.top1_workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
+    _check("qs_chain_forward_top1", _lib.qs_chain_forward_top1(
+        mode, _ptr(x, torch.float16, (m, k), "x"), m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n,
+        _ptr(out, torch.float32, (m, chain.out_features), "out", nullable=True),
+        _ptr(top1, torch.int32, (m,), "top1"),
+        _ptr(top1_prob, torch.float32, (m,), "top1_prob", nullable=True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()))
+    return out, top1, top1_prob
+
+
+def qs_accept_greedy(tgt_top1, draft_ids, out=None):
+    """tgt_top1 int32 [B, gamma+1], draft_ids int32 [B, gamma] -> dict(n_accept, out_tokens)."""
+    b, gp1 = tgt_top1.shape
+    gamma = gp1 - 1
+    dev = tgt_top1.device
+    if out is None:
+        out = {
+            "n_accept": torch.empty((b,), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((b, gp1), dtype=torch.int32, device=dev),
+        }
+    _check("qs_accept_greedy", _lib.qs_accept_greedy(
+        _ptr(tgt_top1, torch.int32, (b, gp1), "tgt_top1"),
+        _ptr(draft_ids, torch.int32, (b, gamma), "draft_ids", nullable=gamma == 0),
+        b, gamma,
+        _ptr(out["n_accept"], torch.int32, (b,), "n_accept"),
+        _ptr(out["out_tokens"], torch.int32, (b, gp1), "out_tokens"), _stream()))
     return out

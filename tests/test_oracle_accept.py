@@ -91,6 +91,20 @@ def test_greedy_brute_force_v3():
                 assert r["out_tokens"][0].tolist() == expect
 
 
+def test_greedy_accept_from_top1_ids_brute_force():
+    """The prefix rule on Top-1 ids (the fused path), over all ids in {-1, 0, 1} for gamma <= 3: the
+    common prefix of draft and target ids, where a missing target id (-1) matches nothing, not even
+    a -1 draft id."""
+    ids = (-1, 0, 1)
+    for gamma in range(0, 4):
+        for t_ids in itertools.product(ids, repeat=gamma + 1):
+            for d_ids in itertools.product(ids, repeat=gamma):
+                r = O.greedy_accept(np.array([t_ids]), np.array([d_ids], dtype=np.int64).reshape(1, gamma))
+                n = next((i for i in range(gamma) if t_ids[i] < 0 or d_ids[i] != t_ids[i]), gamma)
+                assert r["n_accept"][0] == n
+                assert r["out_tokens"][0].tolist() == list(d_ids[:n]) + [t_ids[n]] + [-1] * (gamma - n)
+
+
 def test_greedy_out_of_range_draft_ids_mismatch():
     lg = _onehot_logits([2, 0, 1], 4)[None]
     r = O.verify_greedy(lg, np.array([[-1, 0]]))

@@ -148,6 +148,71 @@ def test_barrier_timeout_is_reported_and_cleared(qs, mode, m):
         assert_exact(y, ref, "chain after a time-out")
 
 
+# ---------------------------------------------------------------- the LM-head's Top-1 fused into the last stage
+
+def _check_fused_top1(out, top1, prob, what):
+    """top1 / top1_prob of a fused call against the oracle's Top-1 of the logits the same call wrote:
+    the index exactly, the probability within the accept bar."""
+    t_ref, p_ref = O.top1(out)
+    assert np.array_equal(top1, t_ref), f"{what}: Top-1"
+    assert np.abs(prob.astype(np.float64) - p_ref).max() <= PROB_ABS, f"{what}: Top-1 probability"
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (0, 1), (1, 1), (2, 1), (0, 12), (1, 8), (0, 70), (1, 70), (2, 33),
+                                    (0, 256)])
+def test_chain_top1_fused(qs, mode, m):
+    """qs_chain_forward_top1 on a two-layer stack with a 33000-wide head whose second half repeats the
+    first (rows v and v + 16500 are the same weights, so every logit appears twice and the Top-1 must
+    be the lower copy: ties across workgroups and output tiles).  The logits it writes equal
+    qs_chain_forward's bit for bit (both run the same kernels with the same splits: the persistent
+    pass, or the batched kernel for the head), its Top-1 is the oracle's Top-1 of those logits, and
+    a call that skips the logits returns the same Top-1."""
+    print(f"fused top1 mode={mode} m={m}", flush=True)
+    rng = W.rng_for(860 + m + 7 * mode)
+    h, inter, half = 512, 1024, 16500
+    shapes = [(h + 256, h), (h, h), (2 * inter, h), (h, inter)] * 2
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    hq, hs = W.int4_weights(rng, half, h)
+    layers.append((np.concatenate([hq, hq]), np.concatenate([hs, hs])))
+    x, _ = W.activations(rng, m, h)
+    chain = _pack_chain(qs, layers)
+    xd = dev(x)
+    out, t1, p1 = qs.qs_chain_forward_top1(mode, xd, chain)
+    out, t1, p1 = host(out), host(t1), host(p1)
+    plain = host(qs.qs_chain_forward(mode, xd, chain))
+    assert np.array_equal(out, plain), "fused call's logits"
+    _check_fused_top1(out, t1, p1, f"mode={mode} m={m}")
+    assert (t1 < half).all(), "ties must resolve to the lowest index"
+    _, t2, p2 = qs.qs_chain_forward_top1(mode, xd, chain, want_logits=False, want_prob=False)
+    assert p2 is None and np.array_equal(host(t2), t1)
+    if mode != 0:  # and the oracle's own chain, for the exact modes
+        t_or, _ = O.top1(O.chain_forward(MODE_NAMES[mode], x, layers).astype(np.float32))
+        assert np.array_equal(t1, t_or)
+
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1)])
+def test_chain_top1_after_a_timeout(qs, mode, m):
+    """A persistent pass whose waits time out leaves Top-1 -1 and probability NaN (the last
+    workgroup's merge never runs), and the next call on the same workspace is correct."""
+    rng = W.rng_for(955)
+    shapes = [(384, 256), (256, 384), (2048, 256)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 256)
+    chain = _pack_chain(qs, layers)
+    ws = torch.empty(chain.top1_workspace_bytes(mode, m), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    qs.qs_set_barrier_timeout_us(0)
+    try:
+        out, t1, p1 = qs.qs_chain_forward_top1(mode, xd, chain, ws=ws)
+        assert qs.qs_chain_pass_status(mode, m, chain, ws)
+        assert (host(t1) == -1).all() and torch.isnan(p1).all() and torch.isnan(out).all()
+    finally:
+        qs.qs_set_barrier_timeout_us(200000)
+    out, t1, p1 = qs.qs_chain_forward_top1(mode, xd, chain, ws=ws)
+    assert not qs.qs_chain_pass_status(mode, m, chain, ws)
+    _check_fused_top1(host(out), host(t1), host(p1), "after a time-out")
+
+
 # ---------------------------------------------------------------- full-size stack, the bench's launch configurations
 
 _STACK = {}
@@ -206,6 +271,11 @@ def test_full_stack_against_the_oracle(qs, mode, m):
     near = (srt[:, -1] - srt[:, -2] <= tol) & (ref[np.arange(m), t_gpu] >= srt[:, -1] - tol)
     print(f"  Top-1 agreement over the sampled columns: {int(agree.sum())}/{m}", flush=True)
     assert (agree | near).all(), "Top-1 differs where the oracle's top-2 gap exceeds the bound"
+    # the fused Top-1 of the same pass over the full vocabulary: same logits, their exact Top-1
+    out, t1, p1 = qs.qs_chain_forward_top1(mode, dev(x), chain)
+    out = host(out)
+    assert np.array_equal(out, logits), "fused call's logits"
+    _check_fused_top1(out, host(t1), host(p1), f"full stack mode={mode} m={m}")
 
 
 @pytest.mark.parametrize("m", [4, 128])
@@ -288,6 +358,20 @@ def test_speculative_iteration(qs, draft_mode, B):
     dd = dev(d)
     gr = qs.qs_verify_greedy(dev(tgt), dd)
     sm = qs.qs_verify_sample(dev(tgt), dev(drf), dd, dev(ua), dev(uf))
+    # the greedy path without logits: draft tokens and the verify pass's Top-1 fused into the LM-head,
+    # then the prefix rule on the Top-1 ids
+    for i in range(gamma):
+        _, tq, _ = qs.qs_chain_forward_top1(draft_mode, dev(np.ascontiguousarray(xv[:, i])), chain,
+                                            want_logits=False, want_prob=False)
+        assert np.array_equal(host(tq), d[:, i]), f"fused draft token {i}"
+    lp, tp, pp = qs.qs_chain_forward_top1(0, dev(xv.reshape(-1, h)), chain)
+    _check_fused_top1(host(lp), host(tp), host(pp), "fused verify Top-1")
+    fa = qs.qs_accept_greedy(tp.view(B, gamma + 1), dd)
+    ofa = O.greedy_accept(host(tp).reshape(B, gamma + 1), d)
+    assert np.array_equal(host(fa["n_accept"]), ofa["n_accept"])
+    assert np.array_equal(host(fa["out_tokens"]), ofa["out_tokens"])
+    if np.array_equal(host(lp).reshape(B, gamma + 1, V), tgt):
+        assert np.array_equal(host(fa["out_tokens"]), host(gr["out_tokens"]))
 
     # ---- oracle, step for step
     for i in range(gamma):

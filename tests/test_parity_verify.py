@@ -357,3 +357,41 @@ def test_tree_greedy_batch_beyond_one_launch_block_and_reuse(qs):
     _check_tree(qs, tg, tokens, parent, ws=ws)
     tg2, tokens2, parent2 = _tree_case(rng, 7, 5, 1000)
     _check_tree(qs, tg2, tokens2, parent2, ws=ws)
+
+
+# ---------------------------------------------------------------- greedy acceptance from Top-1 ids
+
+@pytest.mark.parametrize("b,gamma", [(1, 0), (1, 3), (16, 7), (300, 1), (20000, 5), (7, 63)])
+def test_accept_greedy_from_top1(qs, b, gamma):
+    """qs_accept_greedy against the oracle's prefix rule on random Top-1 ids, with drafts that
+    match a random-length prefix, ids out of any vocabulary and negative (missing) Top-1 ids."""
+    rng = W.rng_for(1100 + b + gamma)
+    t = rng.integers(0, 50, size=(b, gamma + 1)).astype(np.int32)
+    d = rng.integers(0, 50, size=(b, gamma)).astype(np.int32)
+    if gamma:
+        cut = rng.integers(0, gamma + 1, size=b)
+        for i in range(b):
+            d[i, :cut[i]] = t[i, :cut[i]]
+        d[rng.random((b, gamma)) < 0.02] = -5
+        miss = rng.random((b, gamma + 1)) < 0.02
+        t[miss] = -1
+        d[miss[:, :gamma] & (rng.random((b, gamma)) < 0.5)] = -1  # a -1 draft must not match a -1 Top-1
+    out = qs.qs_accept_greedy(dev(t), dev(d) if gamma else None)
+    ref = O.greedy_accept(t, d)
+    assert np.array_equal(host(out["n_accept"]), ref["n_accept"])
+    assert np.array_equal(host(out["out_tokens"]), ref["out_tokens"])
+
+
+def test_accept_greedy_matches_verify_greedy(qs):
+    """On the Top-1 ids qs_verify_greedy computes from logits, qs_accept_greedy commits the same
+    tokens as qs_verify_greedy itself."""
+    rng = W.rng_for(1150)
+    b, gamma, v = 33, 4, 5003
+    tg = rng.standard_normal((b, gamma + 1, v)).astype(np.float32)
+    d = np.argmax(tg[:, :gamma], axis=2).astype(np.int32)
+    flip = rng.random((b, gamma)) < 0.3
+    d[flip] = (d[flip] + 1) % v
+    g = qs.qs_verify_greedy(dev(tg), dev(d))
+    a = qs.qs_accept_greedy(g["tgt_top1"], dev(d))
+    assert np.array_equal(host(a["n_accept"]), host(g["n_accept"]))
+    assert np.array_equal(host(a["out_tokens"]), host(g["out_tokens"]))
