@@ -21,7 +21,7 @@ draft passes take most of a step) and of the W4A16 verify pass kernel, each
 timed with HIP events around graph replays of one pass, and the CPU oracle
 baseline.  Per-call distributions (mean, median, p10, p90) are given for 100
 replays of the verify phase and for the accept kernels, warm (logits just read)
-and cold (L2 and MALL flushed by a 512 MiB write before each call).
+and cold (L2 and MALL flushed by a 1 GiB read before each call).
 """
 
 from __future__ import annotations
@@ -429,7 +429,7 @@ def main():
         return a.elapsed_time(b) / reps
 
     # Per-call HIP events: mean, median, p10 and p90 in us over `reps` calls.  `before` (untimed, on the
-    # same stream) runs ahead of each call, e.g. a 512 MiB write that evicts the inputs from L2 and MALL.
+    # same stream) runs ahead of each call, e.g. a 1 GiB read that evicts the inputs from L2 and MALL.
     def time_dist(fn, reps=100, before=None):
         fn()
         torch.cuda.synchronize()
@@ -448,8 +448,10 @@ def main():
     verify_dist = time_dist(runners[1], reps=100)
     log(f"verify phase over 100 replays: median {verify_dist['median_us']:.1f} us, "
         f"p10 {verify_dist['p10_us']:.1f}, p90 {verify_dist['p90_us']:.1f}")
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    flush = lambda: flush_buf.fill_(1)  # noqa: E731
+    # "cold": a 1 GiB read before each call evicts the inputs from L2 and the 256 MiB MALL with clean
+    # lines (a write would leave dirty lines whose write-back then competes with the call's reads)
+    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.int64)
+    flush = lambda: flush_buf.sum()  # noqa: E731
     # A spin kernel that touches no memory keeps the GPU busy while the host marshals the next call, so
     # a warm call's events bracket its kernels rather than the host's launch latency.
     spin = lambda: torch.cuda._sleep(200_000)  # noqa: E731
@@ -476,7 +478,7 @@ def main():
             "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
             "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
             # per-call distributions: warm (logits just read, as in the pipeline) and cold (L2 and
-            # MALL flushed by a 512 MiB write before each call)
+            # MALL flushed by a 1 GiB read before each call)
             "greedy_warm": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), before=spin),
             "greedy_cold": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), reps=30, before=flush),
             "sample_warm": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), before=spin),

@@ -120,7 +120,7 @@ int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n) 
   if (!chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!device_info()->ok) return QS_ERR_DEVICE;
-  return pass_eligible(mode, M, chain, n) ? pass_launch_count(n) : 0;
+  return pass_eligible(mode, M, chain, n) ? pass_launch_count(mode, M, chain, n) : 0;
 }
 
 int qs_set_barrier_timeout_us(int us) {

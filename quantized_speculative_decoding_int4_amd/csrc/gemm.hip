@@ -606,7 +606,14 @@ int gemm_splits(int mode, int M, int N, int K) {
   const int tiles = gemm_tiles(mode, M, N);
   const int G = K / kGroup;
   int s = 1;
-  while (s < kGemmMaxSplits && tiles * s < 256 && G / (2 * s) >= kGemmMinGroupsPerSplit) s *= 2;
+  // The integer modes' fp64 partial slots are twice as large and their last arrival sums them in
+  // fp64, so they split less: over the Llama-3-8B-shaped stack (W4A4 pass ms, M = 4 / 24 / 64 / 128)
+  // at most 128 workgroups and 8 groups per split gave 2.97 / 3.90 / 4.29 / 5.38 against
+  // 3.36 / 4.75 / 5.28 / 5.19 with the W4A16 rule, and at M = 128 16 groups per split 4.92.
+  const bool wide = mode != QS_W4A16 && M > 64;
+  const int target = mode == QS_W4A16 || wide ? 256 : 128;
+  const int min_groups = mode == QS_W4A16 ? kGemmMinGroupsPerSplit : wide ? 16 : 8;
+  while (s < kGemmMaxSplits && tiles * s < target && G / (2 * s) >= min_groups) s *= 2;
   return s;
 }
 
@@ -638,7 +645,8 @@ static void gemm_launch_one(const GemmArgs& a, dim3 grid, hipStream_t st) {
 }
 
 // Weight ring depth per row tile: 16-row tiles a 3-group (W4A16, whose per-group sums take registers)
-// or 4-group ring, 32-row tiles a QS_GEMM_MT2_RING-group ring.
+// or 4-group ring, 32-row tiles a QS_GEMM_MT2_RING-group ring.  Deeper 32-row rings (at two waves
+// per SIMD) measured no faster: W4A16 M = 128 4.74 / 4.85 / 4.82 ms with 2 / 3 / 4 groups.
 #ifndef QS_GEMM_MT2_RING
 #define QS_GEMM_MT2_RING 2
 #endif

@@ -1,5 +1,5 @@
-// Persistent pass kernel: one launch runs up to kMaxStages linears of a chain
-// (the W4A4 draft pass at M = batch rows or the W4A16 verify pass at M = 4 rows,
+// Persistent pass kernel: one launch runs up to kMaxPassStages linears of a chain
+// (the W4A4 draft pass at M = 1 row or the W4A16 verify pass at up to 14 rows,
 // [P3] "draft modelとtarget modelの処理フロー"; modes from [P1] "QSpec の W4A4
 // モードと W4A16 モード"; W4A8 from [P2] "3.中核となる技術的要素").  The integer modes W4A4
 // and W4A8 share one kernel body and differ only in the activation code range (7 or 127).
@@ -26,7 +26,9 @@
 //    one workgroup in 2-byte stores, so a piece read while it is being written
 //    shows the pattern in the halves not yet written.  This saves the producer's
 //    wait for its store acknowledgements and the two hops of a grid barrier.
-//  * W4A16 (four rows, up to 112 KiB of input): a grid barrier, then one fetch.
+//  * W4A16 (up to 14 rows, up to 112 KiB of staged input): a grid barrier, then one fetch.
+//    Where M rows of a linear's K do not fit in LDS, the linear runs as several table entries,
+//    each over a K chunk that does; they sum into the same outputs with no barrier in between.
 //    A premature fetch of that much data costs a second full round trip, which
 //    measured slower than the barrier.  Workgroup b stores an epoch into its own
 //    flag once its outputs are acknowledged, and every workgroup watches all the
@@ -63,6 +65,7 @@
 #include "qs_msi.h"
 
 #include <atomic>
+#include <vector>
 #include <type_traits>
 
 namespace qs {
@@ -103,19 +106,31 @@ constexpr size_t kPassLdsStageInt = 81920;
 // CU, so the launch spreads one workgroup per CU.
 constexpr size_t kPassLdsMin = 81920;
 constexpr int kPassSlots = 4;              // row-block sets a workgroup may own per stage
+constexpr int kCtrlSlots = (kPassSlots * kPW + kCW - 1) / kCW;  // (set, row block) pairs per control wave
 constexpr int kPiecesMax4 = 8;             // W4A4: 16-byte input pieces a control thread holds per stage
 constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
 constexpr int kSc1 = 16;                   // cache-policy bit SC1: device-coherent access
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw 32-bit buffer resource, no swizzle
 
+// One entry of a launch's stage table: a linear, or one K chunk of a linear whose M staged input
+// rows do not fit in LDS at once (W4A16 at K = 14336 above four rows).  A chunked linear's entries sum into the
+// same outputs: every chunk but the last hands its partial sums on in the control waves' registers,
+// the last one writes the outputs; a grid barrier follows only a linear's last chunk.
 struct PassStage {
   const uint4* w;      // packed tiles
   const uint16_t* sc;  // packed scales
   uint16_t* y16;       // fp16 output [M][N], filled with kEmpty before the launch (not the last stage)
-  int N, K;
+  int N, K;            // K: columns of this entry's chunk
   int s_log2;          // S = 1 << s_log2 streaming waves split K of one row block
   int nsets;           // row-block sets: ceil(nrb / R), R = kSW / S
+  int gfull;           // 128-wide groups of the whole linear (tiles per row block)
+  int chunk;           // bits 0-15: the chunk's first group; bit 16: first chunk; bit 17: last chunk;
+                       // bits 24-31: entries back to the producer's last chunk (0: the launch input)
 };
+__device__ __forceinline__ int chunk_g0(const PassStage& p) { return p.chunk & 0xFFFF; }
+__device__ __forceinline__ bool chunk_first(const PassStage& p) { return ((p.chunk >> 16) & 1) != 0; }
+__device__ __forceinline__ bool chunk_last(const PassStage& p) { return ((p.chunk >> 17) & 1) != 0; }
+__device__ __forceinline__ int chunk_back(const PassStage& p) { return (p.chunk >> 24) & 0xFF; }
 
 struct PassArgs {
   const uint16_t* x;  // input of the launch's first stage, fp16, row stride ldx0 (complete at launch)
@@ -139,6 +154,7 @@ struct PassArgs {
   int n_stages;
   PassStage st[kMaxPassStages];
 };
+static_assert(sizeof(PassArgs) <= 4096, "the stage table travels in the 4 KiB kernel-argument segment");
 
 // Stage i of the running launch, read straight from the kernel-argument segment with scalar loads
 // (the argument is the kernel's first and only one, at offset 0).  Indexing the by-value argument
@@ -156,6 +172,8 @@ __device__ __forceinline__ PassStage stage_at(int i) {
   p.K = k->st[u].K;
   p.s_log2 = k->st[u].s_log2;
   p.nsets = k->st[u].nsets;
+  p.gfull = k->st[u].gfull;
+  p.chunk = k->st[u].chunk;
   return p;
 }
 
@@ -191,8 +209,8 @@ __device__ __forceinline__ StageView stage_view(const PassStage& ps, int wave, i
   v.gcnt = v.G - g0 < v.per ? v.G - g0 : v.per;
   v.nrb = (ps.N + 15) >> 4;
   v.my_sets = stage_sets(ps, bid, grid);
-  v.tile0 = (size_t)(bid * v.R + v.r) * v.G + g0;
-  v.set_stride = (size_t)grid * v.R * v.G;
+  v.tile0 = (size_t)(bid * v.R + v.r) * ps.gfull + chunk_g0(ps) + g0;  // tiles of a row block: gfull apart
+  v.set_stride = (size_t)grid * v.R * ps.gfull;
   return v;
 }
 
@@ -278,8 +296,9 @@ struct Top1Out {
   unsigned char* stats;
   unsigned* cnt;
 };
-__device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], float4_t (*t1_wave)[4],
+__device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], float4_t (*t1_wave)[16],
                                               unsigned* t1_arrive, int cw, int lane, int bid, int grid, int M) {
+  // lane l holds rows 4 (l >> 4) + j of its column; the 16 lanes of a DPP row share those rows
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     Msi t = t1v[j];
@@ -287,7 +306,7 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
     t = msi_merge(t, msi_dpp<0x4E>(t));
     t = msi_merge(t, msi_dpp<0x141>(t));
     t = msi_merge(t, msi_dpp<0x140>(t));
-    if (lane == 0) t1_wave[cw][j] = float4_t{t.m, t.s, __int_as_float(t.i), 0.0f};
+    if ((lane & 15) == 0) t1_wave[cw][4 * (lane >> 4) + j] = float4_t{t.m, t.s, __int_as_float(t.i), 0.0f};
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's partials are in LDS
   unsigned old = 0u;
@@ -312,35 +331,39 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
   prev = (unsigned)__builtin_amdgcn_readfirstlane((int)prev);
   asm volatile("" ::: "memory");
   if (prev + 1u != (unsigned)grid) return;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) t1v[m] = Msi{-INFINITY, 0.0f, 0x7fffffff};
-  // the last workgroup: every row over all workgroups (lane c takes workgroups c, c + 64, ...).  The
-  // partials of all rows are loaded before any is merged, so they cost one round trip (buffer loads
-  // past the extent return zeros and are not merged).
+  // the last workgroup: every row over all workgroups (lane c takes workgroups c, c + 64, ...), four
+  // rows at a time.  A round's partials are all loaded before any is merged, so they cost one round
+  // trip (buffer loads past the extent return zeros and are not merged).
   constexpr int kPer = 4;  // workgroups per lane and round
-  for (int c0 = 0; c0 < grid; c0 += 64 * kPer) {
-    float4_t v[4][kPer];
+  for (int m0 = 0; m0 < M; m0 += 4) {
+    Msi t4[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int r = 0; r < 4; ++r) t4[r] = Msi{-INFINITY, 0.0f, 0x7fffffff};
+    for (int c0 = 0; c0 < grid; c0 += 64 * kPer) {
+      float4_t v[4][kPer];
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int c = c0 + 64 * k + lane;
-        v[m][k] = m < M ? __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (m * grid + c) * 16, 0, kSc1))
-                        : float4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int k = 0; k < kPer; ++k) {
+          const int c = c0 + 64 * k + lane;
+          v[r][k] = m0 + r < M ? __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  rs, ((m0 + r) * grid + c) * 16, 0, kSc1))
+                               : float4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        if (c0 + 64 * k + lane < grid) t1v[m] = msi_merge(t1v[m], Msi{v[m][k][0], v[m][k][1], __float_as_int(v[m][k][2])});
-  }
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m < M) {
-      const Msi t = wave_msi(t1v[m]);
-      if (lane == 0) {
-        o.top1[m] = t.i;
-        if (o.top1_prob) o.top1_prob[m] = 1.0f / t.s;
+        for (int k = 0; k < kPer; ++k)
+          if (c0 + 64 * k + lane < grid) t4[r] = msi_merge(t4[r], Msi{v[r][k][0], v[r][k][1], __float_as_int(v[r][k][2])});
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (m0 + r < M) {
+        const Msi t = wave_msi(t4[r]);
+        if (lane == 0) {
+          o.top1[m0 + r] = t.i;
+          if (o.top1_prob) o.top1_prob[m0 + r] = 1.0f / t.s;
+        }
       }
     }
   }
@@ -352,14 +375,15 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   __shared__ Acc red[kPassSlots][kSW][64];         // per-set partials of one stage
-  __shared__ float row_a[8], row_b[8], row_c[8];   // W4A16: per-row mean, 1/std; integer modes: scale
+  __shared__ float row_a[16], row_b[16], row_c[16];  // W4A16: per-row mean, 1/std; integer modes: scale
+  __shared__ float row_su[16], row_sq[16];          // W4A16 chunked linear: row sums of earlier chunks
   __shared__ double row_mu64[8], row_inv64[8];     // integer modes: per-row mean, 1/std (fp64)
   __shared__ double stat_sum[2][2 * kCW];          // integer staging: fp64 sum, sum of squares per unit
   __shared__ float stat_mm[2][2 * kCW];            // integer staging: max, min per unit
   __shared__ __align__(16) uint32_t zero_pad[16];
   __shared__ __align__(16) uint32_t ones_pad[16];  // fp16 1.0 pairs: the W4A16 row-sum operand
   __shared__ int fail_sh;
-  __shared__ float4_t t1_wave[kCW][4];             // Top-1 epilogue: per control wave and row
+  __shared__ float4_t t1_wave[kCW][16];            // Top-1 epilogue: per control wave and row
   __shared__ unsigned t1_arrive;                   // control waves done with their Top-1 partials
 
   const int lane = threadIdx.x & 63;
@@ -438,7 +462,9 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       while (true) {
         lds_barrier();  // A
         if (cs + 1 >= a.n_stages) { cs = a.n_stages; return; }
-        if constexpr (MODE == 0) static_for<0, kGridBarriers>([&](auto) { lds_barrier(); });  // B C
+        if constexpr (MODE == 0) {  // B C, after a linear's last chunk (the control waves' condition)
+          if (chunk_last(stage_at(cs))) static_for<0, kGridBarriers>([&](auto) { lds_barrier(); });
+        }
         static_for<0, kStagingBarriers<MODE>>([&](auto) { lds_barrier(); });
         if (__builtin_amdgcn_readfirstlane(fail_sh)) { cs = a.n_stages; return; }
         ++cs;
@@ -540,15 +566,33 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     return true;
   };
 
-  // W4A16 (input complete: after the grid barrier, or from the previous launch): raw fp16 rows
-  // straight into LDS, [M][K] row-major, by direct DMA, 64 pieces (1 KiB) per wave instruction.
-  // The row statistics for the epilogue are taken after barrier G, while the contraction runs,
-  // by one control wave per row (needed at barrier A).
+  // Input of entry s: the launch input, or the output of the producer's last chunk.
+  auto input_of = [&](const PassStage& ps, int s, const uint16_t** x, int* ldx, int* norm) {
+    const int back = chunk_back(ps);
+    if (back == 0) {
+      *x = a.x;
+      *ldx = a.ldx0;
+      *norm = a.norm0;
+    } else {
+      const PassStage pr = stage_at(s - back);
+      *x = pr.y16;
+      *ldx = pr.N;
+      *norm = 1;
+    }
+  };
+
+  // W4A16 (input complete: after the grid barrier, or from the previous launch): raw fp16 rows of
+  // this entry's K chunk straight into LDS, [M][K] row-major, by direct DMA, 64 pieces (1 KiB) per
+  // wave instruction.  The row statistics for the epilogue are taken after barrier G, while the
+  // contraction runs, by one control wave per row (needed at barrier A); a chunked linear sums
+  // them over its chunks and forms the row parameters at its last chunk.
   auto stage_in16 = [&](int s, bool has) __attribute__((always_inline)) {
-    const int K = stage_at(s).K;
-    const uint16_t* x = s == 0 ? a.x : stage_at(s - 1).y16;
-    const int ldx = s == 0 ? a.ldx0 : stage_at(s - 1).N;
-    const int norm = s == 0 ? a.norm0 : 1;
+    const PassStage ps = stage_at(s);
+    const int K = ps.K;
+    const uint16_t* xin;
+    int ldx, norm;
+    input_of(ps, s, &xin, &ldx, &norm);
+    const uint16_t* x = xin + chunk_g0(ps) * kGroup;  // the chunk's first column
     const int nb = K / 8;  // pieces per row
     if (has) {
       // the wave's chunks q = cw, cw + kCW, ... of M * cpr: (row, 64-piece column block), no division
@@ -564,10 +608,10 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     lds_barrier();  // G
-    if (has && cw < M) {
+    for (int m = cw; has && m < M; m += kCW) {
       float mu = 0.f, inv = 1.f;
       if (norm) {
-        const uint4* r = reinterpret_cast<const uint4*>(dyn_lds) + (size_t)cw * nb;
+        const uint4* r = reinterpret_cast<const uint4*>(dyn_lds) + (size_t)m * nb;
         float su = 0.f, sq = 0.f, mx = 0.f, mn = 0.f;
         for (int i0 = 0; i0 < nb; i0 += 256) {  // four LDS reads in flight per lane
           uint4 v[4];
@@ -581,11 +625,22 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         }
         su = wave_sum_dpp(su);
         sq = wave_sum_dpp(sq);
-        norm_params(su, sq, K, mu, inv);
+        if (!chunk_first(ps)) {  // the linear's earlier chunks (this wave's own row, in LDS)
+          su += row_su[m];
+          sq += row_sq[m];
+        }
+        if (!chunk_last(ps)) {
+          if (lane == 0) {
+            row_su[m] = su;
+            row_sq[m] = sq;
+          }
+          continue;
+        }
+        norm_params(su, sq, ps.gfull * kGroup, mu, inv);
       }
       if (lane == 0) {
-        row_a[cw] = mu;
-        row_b[cw] = inv;
+        row_a[m] = mu;
+        row_b[m] = inv;
       }
     }
   };
@@ -599,10 +654,11 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // count are read (next row, or zeros past the buffer resource's extent) and not used.
   auto stage_in4 = [&](auto pc, int s, bool has) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    const int K = stage_at(s).K;
-    const uint16_t* x = s == 0 ? a.x : stage_at(s - 1).y16;
-    const int ldx = s == 0 ? a.ldx0 : stage_at(s - 1).N;
-    const int norm = s == 0 ? a.norm0 : 1;
+    const PassStage ps = stage_at(s);
+    const int K = ps.K;  // integer modes take whole linears (no chunks)
+    const uint16_t* x;
+    int ldx, norm;
+    input_of(ps, s, &x, &ldx, &norm);
     const int nb = K / 8;  // pieces per row
     // A whole wave serves one row (gsz >= 128), so `active` is wave-uniform.
     const bool active = has && my_row < M;
@@ -704,6 +760,10 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
   };
 
+  constexpr int kCarry = MODE == 0 ? kCtrlSlots : 1;
+  Acc carry[kCarry];  // W4A16 chunked linears: this wave's partial sums of the earlier chunks
+#pragma unroll
+  for (int pi = 0; pi < kCarry; ++pi) carry[pi] = Acc{0, 0, 0, 0};
   for (int s = 0; s < a.n_stages; ++s) {
     prologue(s);
     if (__builtin_amdgcn_readfirstlane(fail_sh)) return;
@@ -712,20 +772,33 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     const int sets = stage_sets(ps, bid, grid);
     const bool final_out = a.last_is_final && s + 1 == a.n_stages;
     const bool want_t1 = final_out && a.top1 != nullptr;
-    // Top-1 partials of this lane's rows j (lanes 0-15 hold rows 0..M-1, column lane & 15)
+    // Top-1 partials of this lane's rows 4 (lane >> 4) + j, column lane & 15
     Msi t1v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) t1v[j] = Msi{-INFINITY, 0.0f, 0x7fffffff};
     if (sets > 0) {
-      // sum, in a fixed order, the S partials of each (set, row block) and store the outputs
+      // sum, in a fixed order, the S partials of each (set, row block) and store the outputs; a
+      // chunked linear's earlier chunks are added from `carry` (same (set, row block) per slot pi
+      // in every chunk, since its chunks share one split) and only its last chunk stores
       const int S = 1 << ps.s_log2, R = kSW >> ps.s_log2;
       const int nrb = (ps.N + 15) >> 4, N = ps.N;
-      const int norm = s == 0 ? a.norm0 : 1;
-      for (int p = cw; p < sets * R; p += kCW) {
+      const int norm = chunk_back(ps) == 0 ? a.norm0 : 1;
+      const bool first = chunk_first(ps), last = chunk_last(ps);
+#pragma unroll
+      for (int pi = 0; pi < kCtrlSlots; ++pi) {
+        const int p = cw + pi * kCW;
+        if (p >= sets * R) break;
         const int si = p / R, r2 = p - si * R;
         const int rb = (bid + si * grid) * R + r2;
         Acc v = red[si][r2 * S][lane];
         for (int s2 = 1; s2 < S; ++s2) v += red[si][r2 * S + s2][lane];
+        if constexpr (MODE == 0) {
+          if (!first) v += carry[pi % kCarry];
+          if (!last) {
+            carry[pi % kCarry] = v;
+            continue;
+          }
+        }
         float rowsum = 0.f;  // W4A16: sum_k w[n,k] from the all-ones operand row M
         if constexpr (MODE == 0) {
           const int q = M & 3;
@@ -764,7 +837,9 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     if (want_t1) top1_epilogue(Top1Out{a.top1, a.top1_prob, a.t1_stats, a.t1_cnt}, t1v, t1_wave, &t1_arrive, cw, lane,
                                bid, grid, M);
     if constexpr (MODE == 0) {
-      if (s + 1 < a.n_stages) {  // grid barrier: all outputs of stage s are in memory
+      // grid barrier after a linear's last chunk: all outputs of the linear are in memory (the
+      // streaming waves take the same condition)
+      if (s + 1 < a.n_stages && chunk_last(ps)) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's output stores have completed
         lds_barrier();  // B
         const unsigned epoch = a.epoch0 + (unsigned)(s + 1);
@@ -810,6 +885,18 @@ __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n
 
 static int pick_pass_split(int N, int K, int grid);
 
+// K chunks of a linear at M rows: W4A16 stages M fp16 rows of each chunk in LDS, so K is split
+// into equal chunks of whole groups that fit; the integer modes take whole linears.  -1: no fit.
+static int pass_chunks(int mode, int M, int K) {
+  if (mode != QS_W4A16) return (size_t)M * K <= kPassLdsStageInt ? 1 : -1;
+  const int gmax = (int)(kPassLdsStage / ((size_t)M * kGroup * 2));  // groups per chunk
+  if (gmax < 1) return -1;
+  const int G = K / kGroup;
+  return (G + gmax - 1) / gmax;
+}
+// Groups in each chunk of a linear split into nch chunks (the last may be shorter).
+static int chunk_groups(int K, int nch) { return (K / kGroup + nch - 1) / nch; }
+
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   // W4A4 above one row: every workgroup would quantize all rows itself and the fp16 exchange grows
   // with M; measured on MI355X, one launch per linear is as fast from M = 2 on.
@@ -818,15 +905,19 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   if (grid < 1 || grid > kMaxPassWorkgroups) return false;
   const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);  // control threads per input row
   for (int i = 0; i < n; ++i) {
-    if ((size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1) > (mode == QS_W4A16 ? kPassLdsStage : kPassLdsStageInt))
-      return false;
+    const int nch = pass_chunks(mode, M, c[i].K);
+    if (nch < 1 || nch > kMaxPassStages) return false;
     if (mode != QS_W4A16 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
-    if (pick_pass_split(c[i].N, c[i].K, grid) < 0) return false;
+    if (pick_pass_split(c[i].N, chunk_groups(c[i].K, nch) * kGroup, grid) < 0) return false;
   }
   return true;
 }
 
-int pass_max_rows(int mode) { return mode == QS_W4A16 ? 4 : (mode == QS_W4A4 || mode == QS_W4A8) ? 1 : 0; }
+// W4A16 takes up to 14 rows (row M of the 16-row MFMA operand is the all-ones row of the
+// standardisation's weight sums).  Measured over the Llama-3-8B-shaped stack: 5, 6, 8, 12 rows
+// 1.41, 1.40, 1.43, 1.90 ms per pass against 2.1-2.3 ms with one launch per linear; at 15 rows every
+// 4096-wide linear needs two K chunks and the pass took 2.25 ms against 2.12 ms.
+int pass_max_rows(int mode) { return mode == QS_W4A16 ? 14 : (mode == QS_W4A4 || mode == QS_W4A8) ? 1 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   size_t b = 0;
@@ -850,7 +941,30 @@ static int pick_pass_split(int N, int K, int grid) {
   return best;
 }
 
-int pass_launch_count(int n) { return (n + kMaxPassStages - 1) / kMaxPassStages; }
+// Launch boundaries (first linear of each launch, then n): linears are packed in order into
+// launches of at most kMaxPassStages entries, balanced in entries, never splitting a linear's chunks.
+static std::vector<int> pass_launch_plan(int mode, int M, const qs_linear_desc* c, int n) {
+  std::vector<int> nch(n);
+  int total = 0;
+  for (int i = 0; i < n; ++i) total += nch[i] = pass_chunks(mode, M, c[i].K);
+  const int launches = (total + kMaxPassStages - 1) / kMaxPassStages;
+  const int target = (total + launches - 1) / launches;
+  std::vector<int> first{0};
+  int in_launch = 0;
+  for (int i = 0; i < n; ++i) {
+    if (in_launch > 0 && in_launch + nch[i] > target) {
+      first.push_back(i);
+      in_launch = 0;
+    }
+    in_launch += nch[i];
+  }
+  first.push_back(n);
+  return first;
+}
+
+int pass_launch_count(int mode, int M, const qs_linear_desc* c, int n) {
+  return (int)pass_launch_plan(mode, M, c, n).size() - 1;
+}
 
 size_t pass_top1_bytes(int M) { return align_up((size_t)M * kMaxPassWorkgroups * 16, 256); }
 
@@ -879,7 +993,8 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   }
   size_t lds = kPassLdsMin;
   for (int i = 0; i < n; ++i) {
-    const size_t b = (size_t)M * c[i].K * (mode == QS_W4A16 ? 2 : 1);
+    const int nch = pass_chunks(mode, M, c[i].K);
+    const size_t b = (size_t)M * chunk_groups(c[i].K, nch) * kGroup * (mode == QS_W4A16 ? 2 : 1);
     lds = b > lds ? b : lds;
   }
 
@@ -897,26 +1012,26 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   int rc = launch_status();
   if (rc != QS_OK) return rc;
 
-  // Output of stage i at the running offset: stages are laid out in chain order.
+  // Output of linear i at the running offset: outputs are laid out in chain order.
   unsigned char* const base = reinterpret_cast<unsigned char*>(stage_out);
-  size_t off = 0;           // offset of the next stage's output
-  uint16_t* prev = nullptr;  // output of the stage before the launch's first
-  const int launches = pass_launch_count(n);
-  const int per_launch = (n + launches - 1) / launches;
-  for (int s0 = 0; s0 < n; s0 += per_launch) {
-    const int cnt = n - s0 < per_launch ? n - s0 : per_launch;
+  size_t off = 0;            // offset of the next linear's output
+  uint16_t* prev = nullptr;  // output of the linear before the launch's first
+  const std::vector<int> plan = pass_launch_plan(mode, M, c, n);
+  int entry0 = 0;  // pass-wide index of the launch's first entry (epochs count entries)
+  for (size_t l = 0; l + 1 < plan.size(); ++l) {
+    const int i0 = plan[l], i1 = plan[l + 1];
     PassArgs a{};
-    if (s0 == 0) {
+    if (i0 == 0) {
       a.x = x;
       a.ldx0 = c[0].K;
       a.norm0 = 0;
     } else {
       a.x = prev;  // written by the previous launch
-      a.ldx0 = c[s0 - 1].N;
+      a.ldx0 = c[i0 - 1].N;
       a.norm0 = 1;
     }
     a.out = out;
-    a.last_is_final = s0 + cnt == n;
+    a.last_is_final = i1 == n;
     if (t1 && a.last_is_final) {
       a.top1 = t1->top1;
       a.top1_prob = t1->top1_prob;
@@ -925,27 +1040,38 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     }
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
-    a.epoch0 = (unsigned)s0;
+    a.epoch0 = (unsigned)entry0;
     a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
-    a.n_stages = cnt;
-    for (int i = 0; i < cnt; ++i) {
-      const qs_linear_desc& d = c[s0 + i];
-      PassStage& p = a.st[i];
-      p.w = reinterpret_cast<const uint4*>(d.w_packed);
-      p.sc = d.s_packed;
-      p.y16 = nullptr;
-      if (s0 + i + 1 < n) {
-        p.y16 = reinterpret_cast<uint16_t*>(base + off);
+    int e = 0;
+    for (int i = i0; i < i1; ++i) {
+      const qs_linear_desc& d = c[i];
+      uint16_t* y16 = nullptr;
+      if (i + 1 < n) {
+        y16 = reinterpret_cast<uint16_t*>(base + off);
         off += align_up((size_t)M * d.N * 2, 256);
-        prev = p.y16;
       }
-      p.N = d.N;
-      p.K = d.K;
-      p.s_log2 = pick_pass_split(d.N, d.K, grid);
-      const int R = kPW >> p.s_log2;
-      p.nsets = ((d.N + 15) / 16 + R - 1) / R;
+      const int G = d.K / kGroup, nch = pass_chunks(mode, M, d.K), gc = chunk_groups(d.K, nch);
+      const int sl = pick_pass_split(d.N, gc * kGroup, grid);  // one split for all chunks
+      const int R = kPW >> sl;
+      for (int j = 0; j < nch; ++j, ++e) {
+        PassStage& p = a.st[e];
+        const int g0 = j * gc;
+        p.w = reinterpret_cast<const uint4*>(d.w_packed);
+        p.sc = d.s_packed;
+        p.y16 = y16;
+        p.N = d.N;
+        p.K = (G - g0 < gc ? G - g0 : gc) * kGroup;
+        p.s_log2 = sl;
+        p.nsets = ((d.N + 15) / 16 + R - 1) / R;
+        p.gfull = G;
+        const int back = i == i0 ? 0 : j + 1;  // the previous linear's last chunk
+        p.chunk = g0 | (j == 0 ? 1 << 16 : 0) | (j + 1 == nch ? 1 << 17 : 0) | (back << 24);
+      }
+      if (y16) prev = y16;
     }
+    a.n_stages = e;
+    entry0 += e;
     if (mode == QS_W4A16)
       hipLaunchKernelGGL(pass_kernel<0>, dim3(grid), dim3(kPThreads), lds, st, a);
     else if (mode == QS_W4A4)

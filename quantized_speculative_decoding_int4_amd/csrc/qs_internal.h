@@ -82,7 +82,7 @@ constexpr int kMaxPassWorkgroups = 1024;
 constexpr size_t kPassCtrlBytes = 128 + (size_t)kMaxPassWorkgroups * 128;
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n);
 int pass_max_rows(int mode);   // most rows a persistent pass takes in this mode
-int pass_launch_count(int n);  // launches of a persistent pass over n linears
+int pass_launch_count(int mode, int M, const qs_linear_desc* c, int n);  // launches of a persistent pass
 // fp16 outputs of all stages but the last, each 256-byte aligned, in chain order
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n);
 int pass_barrier_timeout_us();  // wall-clock limit of one wait for a stage's input (process-wide)

@@ -103,15 +103,15 @@ def test_chain_with_vocabulary_wide_head(qs, mode, m):
 @pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     """75 linears.  At M <= 4 (W4A16) / M = 1 (integer modes) the persistent pass splits them over
-    two launches (at most 72 per launch), so the hand-over at the seam is covered; the other row
-    counts run linear by linear."""
+    two launches (at most 72 per launch), so the hand-over at the seam is covered; so does W4A16 up
+    to 14 rows; the other row counts run linear by linear."""
     print(f"long chain mode={mode} m={m}", flush=True)
     rng = W.rng_for(900 + 10 * m + mode)
     shapes = [(384, 256), (256, 384)] * 37 + [(1000, 256)]
     layers = [W.int4_weights(rng, n, k) for n, k in shapes]
     x, _ = W.activations(rng, m, 256)
     chain = _pack_chain(qs, layers)
-    persistent = (m <= 4) if mode == 0 else (m <= 1)
+    persistent = (m <= 14) if mode == 0 else (m <= 1)
     assert chain.pass_launches(mode, m) == (2 if persistent else 0)
     y = host(qs.qs_chain_forward(mode, dev(x), chain))
     _check(y, O.chain_forward(MODE_NAMES[mode], x, layers), mode, "long75", f"long chain mode={mode} m={m}")
@@ -213,6 +213,62 @@ def test_chain_top1_after_a_timeout(qs, mode, m):
     _check_fused_top1(host(out), host(t1), host(p1), "after a time-out")
 
 
+# ---------------------------------------------------------------- W4A16 persistent pass above four rows (K chunks)
+
+@pytest.mark.parametrize("m", [5, 8, 12, 14])
+def test_chain_w4a16_chunked_k(qs, m):
+    """W4A16 persistent pass at 5-14 rows on a chain whose wide linears do not fit M staged rows in
+    LDS at once, so their K is split into chunks that sum into the same outputs (two chunks here
+    from 8 rows on; at 5 rows everything fits).  Every stage is compared with the oracle given
+    the GPU's own input (a chain cut after it), held to the single-linear bar; the full chain too;
+    and the fused Top-1 of the head against the oracle's Top-1 of the GPU logits."""
+    print(f"chunked W4A16 m={m}", flush=True)
+    rng = W.rng_for(990 + m)
+    shapes = [(8192, 512), (512, 8192), (4096, 512), (3000, 4096)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 512)
+    chain = _pack_chain(qs, layers)
+    assert chain.pass_launches(0, m) == 1
+    xd = dev(x)
+    packed = [(wp, sp, n, k) for (wp, sp), (n, k) in zip(chain.tensors, shapes)]
+    for i in range(len(layers)):
+        got = host(qs.qs_chain_forward(0, xd, qs.Chain(packed[:i + 1])))
+        prev = x if i == 0 else host(qs.qs_chain_forward(0, xd, qs.Chain(packed[:i]))).astype(np.float16)
+        q, s_ = layers[i]
+        v = np.ascontiguousarray(prev[:, :q.shape[1]])
+        z = v.astype(np.float64) if i == 0 else O.standardize_rows_exact(v)
+        assert_linear_close(got, z @ O.dequantize_weights(q, s_).T, f"chunked stage {i} m={m}")
+    y = host(qs.qs_chain_forward(0, xd, chain))
+    assert_linear_close(y, O.chain_forward("w4a16", x, layers), f"chunked chain m={m}")
+    out, t1, p1 = qs.qs_chain_forward_top1(0, xd, chain)
+    assert np.array_equal(host(out), y)
+    _check_fused_top1(y, host(t1), host(p1), f"chunked chain m={m}")
+
+
+def test_chain_w4a16_chunked_timeout(qs):
+    """The time-out path of a chunked pass (the first grid barrier follows the first linear's last
+    chunk): every workgroup exits, the word is reported, output and Top-1 are NaN / -1, and the next
+    call is correct."""
+    rng = W.rng_for(996)
+    shapes = [(8192, 512), (512, 8192), (1000, 512)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    m = 8
+    x, _ = W.activations(rng, m, 512)
+    chain = _pack_chain(qs, layers)
+    ws = torch.empty(chain.top1_workspace_bytes(0, m), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    qs.qs_set_barrier_timeout_us(0)
+    try:
+        out, t1, p1 = qs.qs_chain_forward_top1(0, xd, chain, ws=ws)
+        assert qs.qs_chain_pass_status(0, m, chain, ws)
+        assert torch.isnan(out).all() and (host(t1) == -1).all() and torch.isnan(p1).all()
+    finally:
+        qs.qs_set_barrier_timeout_us(200000)
+    out, t1, p1 = qs.qs_chain_forward_top1(0, xd, chain, ws=ws)
+    assert not qs.qs_chain_pass_status(0, m, chain, ws)
+    assert_linear_close(host(out), O.chain_forward("w4a16", x, layers), "chunked chain after a time-out")
+
+
 # ---------------------------------------------------------------- full-size stack, the bench's launch configurations
 
 _STACK = {}
@@ -242,11 +298,11 @@ def _sampled_head(st):
     return st["host"][:-1] + [(hq[st["cols"]], hs[st["cols"]])]
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 128), (1, 128), (2, 64)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 8), (0, 128), (1, 128), (2, 64)])
 def test_full_stack_against_the_oracle(qs, mode, m):
     """The whole stack in the bench's launch configurations: the persistent pass (W4A16 verify at
-    M = 4, W4A4 / W4A8 draft at M = 1) and one launch of the batched kernel per linear (M = 64, 128,
-    config 4's batched verify).  The oracle runs the whole stack itself from the same inputs, its
+    M = 4 and at M = 8, where the down projection runs in two K chunks; W4A4 / W4A8 draft at M = 1)
+    and one launch of the batched kernel per linear (M = 64, 128, config 4's batched verify).  The oracle runs the whole stack itself from the same inputs, its
     head restricted to 3000 sampled vocabulary rows (which gives exactly those logit columns).
     Integer modes: bit-exact.  W4A16: the chain bound of the full stack.  Top-1 over the sampled
     columns: the same in every row, except (W4A16) where the oracle's two best sampled logits are
@@ -254,8 +310,9 @@ def test_full_stack_against_the_oracle(qs, mode, m):
     print(f"full stack mode={mode} m={m}", flush=True)
     st = _stack(qs)
     chain = st["chain"]
-    persistent_rows = {0: 4, 1: 1, 2: 1}[mode]
-    assert chain.pass_launches(mode, m) == (0 if m > persistent_rows else 2)
+    persistent_rows = {0: 14, 1: 1, 2: 1}[mode]
+    # W4A16 above 4 rows splits the down projection's K into chunks: more entries, three launches
+    assert chain.pass_launches(mode, m) == (0 if m > persistent_rows else 2 if m <= 4 else 3)
     x = W.activations(W.rng_for(31), m, W.HIDDEN)[0]
     logits = host(qs.qs_chain_forward(mode, dev(x), chain))
     assert np.isfinite(logits).all()
