@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--core-only", action="store_true",
+                    help="time the iteration and the pass rooflines only (for counter runs under a profiler: no "
+                         "accept, per-linear, batched or timing-model sections)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device to device twice (a plain copy kernel of known "
                          "size, to scale memory-traffic counters under a profiler)")
@@ -448,262 +451,271 @@ def main():
     verify_dist = time_dist(runners[1], reps=100)
     log(f"verify phase over 100 replays: median {verify_dist['median_us']:.1f} us, "
         f"p10 {verify_dist['p10_us']:.1f}, p90 {verify_dist['p90_us']:.1f}")
-    # "cold": a 1 GiB read before each call evicts the inputs from L2 and the 256 MiB MALL with clean
-    # lines (a write would leave dirty lines whose write-back then competes with the call's reads)
-    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.int64)
-    flush = lambda: flush_buf.sum()  # noqa: E731
-    # A spin kernel that touches no memory keeps the GPU busy while the host marshals the next call, so
-    # a warm call's events bracket its kernels rather than the host's launch latency.
-    spin = lambda: torch.cuda._sleep(200_000)  # noqa: E731
-
-    accept = {}
-    for (B, G) in ((1, GAMMA), (16, 7)):
-        tg = torch.from_numpy(W.logits(rng, (B, G + 1, V), sigma=5.24)).to(dev)
-        dr = torch.from_numpy(W.perturb(rng, tg[:, :G].cpu().numpy())).to(dev)
-        dd = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
-        ua = torch.from_numpy(W.uniforms(rng, (B, G))).to(dev)
-        uf = torch.from_numpy(W.uniforms(rng, (B,))).to(dev)
-        wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
-        go = qs.qs_verify_greedy(tg, dd, ws=wsg)
-        so = qs.qs_verify_sample(tg, dr, dd, ua, uf, ws=wsg)
-        tgms = time_calls(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg))
-        tsms = time_calls(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg))
-        pos = B * (G + 1)
-        greedy_bytes = 4.0 * V * pos                                  # every logit read once
-        sample_bytes = 4.0 * V * B * (2 * G + 1) + 8.0 * V * B         # plus the two drawn-from rows again
-        accept[f"B{B}_gamma{G}"] = {
-            "positions": pos,
-            "greedy_bytes": greedy_bytes, "sample_bytes": sample_bytes,
-            "greedy_us": tgms * 1e3, "greedy_positions_per_s": pos / (tgms * 1e-3),
-            "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
-            "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
-            # per-call distributions: warm (logits just read, as in the pipeline) and cold (L2 and
-            # MALL flushed by a 1 GiB read before each call)
-            "greedy_warm": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), before=spin),
-            "greedy_cold": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), reps=30, before=flush),
-            "sample_warm": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), before=spin),
-            "sample_cold": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), reps=30,
-                                     before=flush),
+    def optional_sections():
+        """Accept throughput, per-linear rates, batched sweep and the timing model (skipped by --core-only)."""
+        # "cold": a 1 GiB read before each call evicts the inputs from L2 and the 256 MiB MALL with clean
+        # lines (a write would leave dirty lines whose write-back then competes with the call's reads)
+        flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.int64)
+        flush = lambda: flush_buf.sum()  # noqa: E731
+        # A spin kernel that touches no memory keeps the GPU busy while the host marshals the next call, so
+        # a warm call's events bracket its kernels rather than the host's launch latency.
+        spin = lambda: torch.cuda._sleep(200_000)  # noqa: E731
+    
+        accept = {}
+        for (B, G) in ((1, GAMMA), (16, 7)):
+            tg = torch.from_numpy(W.logits(rng, (B, G + 1, V), sigma=5.24)).to(dev)
+            dr = torch.from_numpy(W.perturb(rng, tg[:, :G].cpu().numpy())).to(dev)
+            dd = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
+            ua = torch.from_numpy(W.uniforms(rng, (B, G))).to(dev)
+            uf = torch.from_numpy(W.uniforms(rng, (B,))).to(dev)
+            wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+            go = qs.qs_verify_greedy(tg, dd, ws=wsg)
+            so = qs.qs_verify_sample(tg, dr, dd, ua, uf, ws=wsg)
+            tgms = time_calls(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg))
+            tsms = time_calls(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg))
+            pos = B * (G + 1)
+            greedy_bytes = 4.0 * V * pos                                  # every logit read once
+            sample_bytes = 4.0 * V * B * (2 * G + 1) + 8.0 * V * B         # plus the two drawn-from rows again
+            accept[f"B{B}_gamma{G}"] = {
+                "positions": pos,
+                "greedy_bytes": greedy_bytes, "sample_bytes": sample_bytes,
+                "greedy_us": tgms * 1e3, "greedy_positions_per_s": pos / (tgms * 1e-3),
+                "sample_us": tsms * 1e3, "sample_positions_per_s": pos / (tsms * 1e-3),
+                "greedy_GBps": 4.0 * V * pos / (tgms * 1e-3) / 1e9,
+                # per-call distributions: warm (logits just read, as in the pipeline) and cold (L2 and
+                # MALL flushed by a 1 GiB read before each call)
+                "greedy_warm": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), before=spin),
+                "greedy_cold": time_dist(lambda: qs.qs_verify_greedy(tg, dd, out=go, ws=wsg), reps=30, before=flush),
+                "sample_warm": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), before=spin),
+                "sample_cold": time_dist(lambda: qs.qs_verify_sample(tg, dr, dd, ua, uf, out=so, ws=wsg), reps=30,
+                                         before=flush),
+            }
+            a_ = accept[f"B{B}_gamma{G}"]
+            # achieved HBM (or MALL, when warm) rate of the median call against the 8 TB/s HBM peak
+            a_["roofline"] = {k: {"GBps": byt / (a_[k]["median_us"] * 1e-6) / 1e9,
+                                  "frac": byt / (a_[k]["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                              for k, byt in (("greedy_warm", greedy_bytes), ("greedy_cold", greedy_bytes),
+                                             ("sample_warm", sample_bytes), ("sample_cold", sample_bytes))}
+            del tg, dr, wsg
+        del flush_buf
+    
+        # tree-shaped greedy verify: 16 sequences x 8-node random trees (parent uniform over earlier
+        # nodes; a node's token is its parent's Top-1 with probability 0.96), V = 128256
+        Bt, Tt = 16, 8
+        tgt_tree = torch.from_numpy(W.logits(rng, (Bt, Tt, V), sigma=5.24)).to(dev)
+        par_np = np.zeros((Bt, Tt), np.int32)
+        par_np[:, 0] = -1
+        for i in range(1, Tt):
+            par_np[:, i] = rng.integers(0, i, size=Bt)
+        tok_np = rng.integers(0, V, size=(Bt, Tt)).astype(np.int32)
+        tree_tok, tree_par = torch.from_numpy(tok_np).to(dev), torch.from_numpy(par_np).to(dev)
+        wst = torch.zeros(qs.verify_workspace_bytes(Bt, Tt - 1, V), dtype=torch.uint8, device=dev)
+        r0 = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
+        t1 = r0["tgt_top1"].cpu().numpy()
+        agree_t = rng.random((Bt, Tt)) < 0.96
+        for i in range(1, Tt):
+            tok_np[:, i] = np.where(agree_t[:, i], t1[np.arange(Bt), par_np[:, i]], tok_np[:, i])
+        tree_tok.copy_(torch.from_numpy(tok_np))
+        tr = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
+        ttms = time_calls(lambda: qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, out=tr, ws=wst))
+        accept[f"tree_B{Bt}_T{Tt}"] = {
+            "positions": Bt * Tt, "greedy_us": ttms * 1e3, "greedy_positions_per_s": Bt * Tt / (ttms * 1e-3),
+            "mean_accepted": float(tr["n_accept"].float().mean().item()),
         }
-        a_ = accept[f"B{B}_gamma{G}"]
-        # achieved HBM (or MALL, when warm) rate of the median call against the 8 TB/s HBM peak
-        a_["roofline"] = {k: {"GBps": byt / (a_[k]["median_us"] * 1e-6) / 1e9,
-                              "frac": byt / (a_[k]["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
-                          for k, byt in (("greedy_warm", greedy_bytes), ("greedy_cold", greedy_bytes),
-                                         ("sample_warm", sample_bytes), ("sample_cold", sample_bytes))}
-        del tg, dr, wsg
-    del flush_buf
-
-    # tree-shaped greedy verify: 16 sequences x 8-node random trees (parent uniform over earlier
-    # nodes; a node's token is its parent's Top-1 with probability 0.96), V = 128256
-    Bt, Tt = 16, 8
-    tgt_tree = torch.from_numpy(W.logits(rng, (Bt, Tt, V), sigma=5.24)).to(dev)
-    par_np = np.zeros((Bt, Tt), np.int32)
-    par_np[:, 0] = -1
-    for i in range(1, Tt):
-        par_np[:, i] = rng.integers(0, i, size=Bt)
-    tok_np = rng.integers(0, V, size=(Bt, Tt)).astype(np.int32)
-    tree_tok, tree_par = torch.from_numpy(tok_np).to(dev), torch.from_numpy(par_np).to(dev)
-    wst = torch.zeros(qs.verify_workspace_bytes(Bt, Tt - 1, V), dtype=torch.uint8, device=dev)
-    r0 = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
-    t1 = r0["tgt_top1"].cpu().numpy()
-    agree_t = rng.random((Bt, Tt)) < 0.96
-    for i in range(1, Tt):
-        tok_np[:, i] = np.where(agree_t[:, i], t1[np.arange(Bt), par_np[:, i]], tok_np[:, i])
-    tree_tok.copy_(torch.from_numpy(tok_np))
-    tr = qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, ws=wst)
-    ttms = time_calls(lambda: qs.qs_verify_tree_greedy(tgt_tree, tree_tok, tree_par, out=tr, ws=wst))
-    accept[f"tree_B{Bt}_T{Tt}"] = {
-        "positions": Bt * Tt, "greedy_us": ttms * 1e3, "greedy_positions_per_s": Bt * Tt / (ttms * 1e-3),
-        "mean_accepted": float(tr["n_accept"].float().mean().item()),
-    }
-    del tgt_tree, wst
-
-    # LM-head with the fused Top-1 epilogue against LM-head + a separate Top-1 launch (the head of
-    # the stack above; W4A4 at M = 1 as in a draft step, W4A16 at M = 4 as in the verify)
-    head_wp, head_sp, head_n, head_k = layers[-1]
-    lmtop = {}
-    for mode, mname, mm in ((qs.QS_W4A4, "w4a4_M1", 1), (qs.QS_W4A16, "w4a16_M4", 4)):
-        xh = x_verify[:mm].contiguous()
-        lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
-        wsl = torch.empty(max(1, qs.linear_workspace_bytes(mode, mm, V, head_k)), dtype=torch.uint8, device=dev)
-        wsg = torch.zeros(qs.verify_workspace_bytes(mm, 0, V), dtype=torch.uint8, device=dev)
-        go = qs.qs_verify_greedy(lg.view(mm, 1, V), None, ws=wsg, want_prob=True)
-        wst1 = torch.zeros(qs.lmhead_top1_workspace_bytes(mode, mm, V, head_k), dtype=torch.uint8, device=dev)
-        fo = qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, ws=wst1)
-
-        def separate():
-            qs.qs_lmhead(mode, xh, head_wp, head_sp, V, logits=lg, ws=wsl)
-            qs.qs_verify_greedy(lg.view(mm, 1, V), None, out=go, ws=wsg)
-
-        sep_ms = time_calls(separate)
-        fused_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, top1=fo["top1"],
-                                                        top1_prob=fo["top1_prob"], ws=wst1))
-        nolog_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, want_logits=False,
-                                                        top1=fo["top1"], top1_prob=fo["top1_prob"], ws=wst1))
-        assert bool((fo["top1"] == go["tgt_top1"].view(-1)).all()), "fused Top-1 differs from the verify kernel's"
-        lmtop[mname] = {"separate_us": sep_ms * 1e3, "fused_us": fused_ms * 1e3, "fused_no_logits_us": nolog_ms * 1e3}
-        del wsl, wsg, wst1, lg
-    accept["lmhead_top1"] = lmtop
-
-    # Verify pass + greedy acceptance, graph-replayed: the pass writing logits then the greedy verify
-    # kernel reading them, against the pass with the Top-1 fused into its LM-head stage then the prefix
-    # rule on the Top-1 ids (B = 1, gamma = 3: the persistent pass; B = 16, gamma = 7: batched kernels).
-    fused_top1 = {}
-    for (B, G) in ((1, GAMMA), (16, 7)):
-        mm = B * (G + 1)
-        xb = torch.from_numpy(W.activations(W.rng_for(22), mm, H)[0]).to(dev)
-        db = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
-        lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
-        wsc = torch.empty(chain.top1_workspace_bytes(qs.QS_W4A16, mm), dtype=torch.uint8, device=dev)
-        wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
-        t1b = torch.empty((mm,), dtype=torch.int32, device=dev)
-        p1b = torch.empty((mm,), dtype=torch.float32, device=dev)
-        go = qs.qs_verify_greedy(lg.view(B, G + 1, V), db, ws=wsg)
-        ao = qs.qs_accept_greedy(t1b.view(B, G + 1), db)
-
-        def separate():
-            qs.qs_chain_forward(qs.QS_W4A16, xb, chain, out=lg, ws=wsc)
-            qs.qs_verify_greedy(lg.view(B, G + 1, V), db, out=go, ws=wsg)
-
-        def fused():
-            qs.qs_chain_forward_top1(qs.QS_W4A16, xb, chain, out=None, want_logits=False, top1=t1b, top1_prob=p1b,
-                                     ws=wsc)
-            qs.qs_accept_greedy(t1b.view(B, G + 1), db, out=ao)
-
-        graphs_ = {}
-        for name, fn in (("separate", separate), ("fused", fused)):
-            fn()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        del tgt_tree, wst
+    
+        # LM-head with the fused Top-1 epilogue against LM-head + a separate Top-1 launch (the head of
+        # the stack above; W4A4 at M = 1 as in a draft step, W4A16 at M = 4 as in the verify)
+        head_wp, head_sp, head_n, head_k = layers[-1]
+        lmtop = {}
+        for mode, mname, mm in ((qs.QS_W4A4, "w4a4_M1", 1), (qs.QS_W4A16, "w4a16_M4", 4)):
+            xh = x_verify[:mm].contiguous()
+            lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
+            wsl = torch.empty(max(1, qs.linear_workspace_bytes(mode, mm, V, head_k)), dtype=torch.uint8, device=dev)
+            wsg = torch.zeros(qs.verify_workspace_bytes(mm, 0, V), dtype=torch.uint8, device=dev)
+            go = qs.qs_verify_greedy(lg.view(mm, 1, V), None, ws=wsg, want_prob=True)
+            wst1 = torch.zeros(qs.lmhead_top1_workspace_bytes(mode, mm, V, head_k), dtype=torch.uint8, device=dev)
+            fo = qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, ws=wst1)
+    
+            def separate():
+                qs.qs_lmhead(mode, xh, head_wp, head_sp, V, logits=lg, ws=wsl)
+                qs.qs_verify_greedy(lg.view(mm, 1, V), None, out=go, ws=wsg)
+    
+            sep_ms = time_calls(separate)
+            fused_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, logits=lg, top1=fo["top1"],
+                                                            top1_prob=fo["top1_prob"], ws=wst1))
+            nolog_ms = time_calls(lambda: qs.qs_lmhead_top1(mode, xh, head_wp, head_sp, V, want_logits=False,
+                                                            top1=fo["top1"], top1_prob=fo["top1_prob"], ws=wst1))
+            assert bool((fo["top1"] == go["tgt_top1"].view(-1)).all()), "fused Top-1 differs from the verify kernel's"
+            lmtop[mname] = {"separate_us": sep_ms * 1e3, "fused_us": fused_ms * 1e3, "fused_no_logits_us": nolog_ms * 1e3}
+            del wsl, wsg, wst1, lg
+        accept["lmhead_top1"] = lmtop
+    
+        # Verify pass + greedy acceptance, graph-replayed: the pass writing logits then the greedy verify
+        # kernel reading them, against the pass with the Top-1 fused into its LM-head stage then the prefix
+        # rule on the Top-1 ids (B = 1, gamma = 3: the persistent pass; B = 16, gamma = 7: batched kernels).
+        fused_top1 = {}
+        for (B, G) in ((1, GAMMA), (16, 7)):
+            mm = B * (G + 1)
+            xb = torch.from_numpy(W.activations(W.rng_for(22), mm, H)[0]).to(dev)
+            db = torch.from_numpy(rng.integers(0, V, size=(B, G)).astype(np.int32)).to(dev)
+            lg = torch.empty((mm, V), dtype=torch.float32, device=dev)
+            wsc = torch.empty(chain.top1_workspace_bytes(qs.QS_W4A16, mm), dtype=torch.uint8, device=dev)
+            wsg = torch.zeros(qs.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+            t1b = torch.empty((mm,), dtype=torch.int32, device=dev)
+            p1b = torch.empty((mm,), dtype=torch.float32, device=dev)
+            go = qs.qs_verify_greedy(lg.view(B, G + 1, V), db, ws=wsg)
+            ao = qs.qs_accept_greedy(t1b.view(B, G + 1), db)
+    
+            def separate():
+                qs.qs_chain_forward(qs.QS_W4A16, xb, chain, out=lg, ws=wsc)
+                qs.qs_verify_greedy(lg.view(B, G + 1, V), db, out=go, ws=wsg)
+    
+            def fused():
+                qs.qs_chain_forward_top1(qs.QS_W4A16, xb, chain, out=None, want_logits=False, top1=t1b, top1_prob=p1b,
+                                         ws=wsc)
+                qs.qs_accept_greedy(t1b.view(B, G + 1), db, out=ao)
+    
+            graphs_ = {}
+            for name, fn in (("separate", separate), ("fused", fused)):
                 fn()
-            graphs_[name] = g
-        # interleaved rounds, median of the per-round means (the pass itself varies by ~1% between replays)
-        rounds = {"separate": [], "fused": []}
-        for _ in range(5):
-            for name in ("separate", "fused"):
-                rounds[name].append(time_calls(graphs_[name].replay, reps=8) * 1e3)
-        res = {k: float(np.median(v)) for k, v in rounds.items()}
-        assert bool((go["out_tokens"] == ao["out_tokens"]).all()), "fused and separate greedy paths disagree"
-        fused_top1[f"B{B}_gamma{G}"] = {"M": mm, "separate_us": res["separate"], "fused_us": res["fused"],
-                                        "saved_us": res["separate"] - res["fused"],
-                                        "logit_bytes_not_reread": 4 * mm * V}
-        log(f"verify + greedy, B={B} gamma={G}: pass then greedy kernel {res['separate']:.1f} us, fused Top-1 then "
-            f"accept {res['fused']:.1f} us")
-        del lg, wsc, wsg
-
-    # ---------------- configs 0-2, one linear at a time (MALL-rotated weight copies)
-    per_linear = linear_rates(qs, W, torch, E)
-    log("per-linear W4A16 M=4 GB/s: " + ", ".join(f"{k}: {v['w4a16_M4']['GBps']:.0f}" for k, v in per_linear.items()))
-
-    # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
-    # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
-    # INT4 weights with 8-bit activations on the int8 MFMA); each point is one
-    # graph-replayed pass, timed with HIP events.  MFMA utilisation = 2 M (weights) flop / time
-    # against the dense peak of the mode's MFMA (fp16 2.5166 PFLOP/s, int8 5.0332 POP/s).
-    n_weights = sum(n * k for (_, n, k) in shapes)
-    peaks = {qs.QS_W4A16: 2.5166e15, qs.QS_W4A4: 5.0332e15, qs.QS_W4A8: 5.0332e15}
-    batched = {"points": []}
-    rng_b = W.rng_for(21)
-    for (B, G) in ((1, 3), (1, 5), (1, 7), (4, 3), (4, 5), (4, 7), (16, 3), (16, 5), (16, 7)):
-        m = B * (G + 1)
-        xb = torch.from_numpy(W.activations(rng_b, m, W.HIDDEN)[0]).to(dev)
-        ob = torch.empty((m, V), dtype=torch.float32, device=dev)
-        for mode, mname in ((qs.QS_W4A16, "w4a16"), (qs.QS_W4A4, "w4a4"), (qs.QS_W4A8, "w4a8")):
-            wsb = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
-            qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                graphs_[name] = g
+            # interleaved rounds, median of the per-round means (the pass itself varies by ~1% between replays)
+            rounds = {"separate": [], "fused": []}
+            for _ in range(5):
+                for name in ("separate", "fused"):
+                    rounds[name].append(time_calls(graphs_[name].replay, reps=8) * 1e3)
+            res = {k: float(np.median(v)) for k, v in rounds.items()}
+            assert bool((go["out_tokens"] == ao["out_tokens"]).all()), "fused and separate greedy paths disagree"
+            fused_top1[f"B{B}_gamma{G}"] = {"M": mm, "separate_us": res["separate"], "fused_us": res["fused"],
+                                            "saved_us": res["separate"] - res["fused"],
+                                            "logit_bytes_not_reread": 4 * mm * V}
+            log(f"verify + greedy, B={B} gamma={G}: pass then greedy kernel {res['separate']:.1f} us, fused Top-1 then "
+                f"accept {res['fused']:.1f} us")
+            del lg, wsc, wsg
+    
+        # ---------------- configs 0-2, one linear at a time (MALL-rotated weight copies)
+        per_linear = linear_rates(qs, W, torch, E)
+        log("per-linear W4A16 M=4 GB/s: " + ", ".join(f"{k}: {v['w4a16_M4']['GBps']:.0f}" for k, v in per_linear.items()))
+    
+        # ---------------- batched verify: B sequences x (gamma + 1) rows through the same stack
+        # Sweep gamma in {3, 5, 7} x B in {1, 4, 16} (M = B (gamma + 1)) in all three modes (W4A8: the same
+        # INT4 weights with 8-bit activations on the int8 MFMA); each point is one
+        # graph-replayed pass, timed with HIP events.  MFMA utilisation = 2 M (weights) flop / time
+        # against the dense peak of the mode's MFMA (fp16 2.5166 PFLOP/s, int8 5.0332 POP/s).
+        n_weights = sum(n * k for (_, n, k) in shapes)
+        peaks = {qs.QS_W4A16: 2.5166e15, qs.QS_W4A4: 5.0332e15, qs.QS_W4A8: 5.0332e15}
+        batched = {"points": []}
+        rng_b = W.rng_for(21)
+        for (B, G) in ((1, 3), (1, 5), (1, 7), (4, 3), (4, 5), (4, 7), (16, 3), (16, 5), (16, 7)):
+            m = B * (G + 1)
+            xb = torch.from_numpy(W.activations(rng_b, m, W.HIDDEN)[0]).to(dev)
+            ob = torch.empty((m, V), dtype=torch.float32, device=dev)
+            for mode, mname in ((qs.QS_W4A16, "w4a16"), (qs.QS_W4A4, "w4a4"), (qs.QS_W4A8, "w4a8")):
+                wsb = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
                 qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
-            g.replay()
-            torch.cuda.synchronize()
-            ea, eb = E(enable_timing=True), E(enable_timing=True)
-            ea.record()
-            for _ in range(3):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    qs.qs_chain_forward(mode, xb, chain, out=ob, ws=wsb)
                 g.replay()
-            eb.record()
-            torch.cuda.synchronize()
-            ms = ea.elapsed_time(eb) / 3
-            ops = 2.0 * m * n_weights
-            batched["points"].append({
-                "B": B, "gamma": G, "M": m, "mode": mname, "pass_ms": ms,
-                "weight_GBps": pass_bytes / (ms * 1e-3) / 1e9,
-                "tflops": ops / (ms * 1e-3) / 1e12,
-                "mfma_util": ops / (ms * 1e-3) / peaks[mode],
-                "persistent_launches": chain.pass_launches(mode, m),
-            })
-            del g, wsb
-        assert bool(torch.isfinite(ob).all()), "non-finite batched logits"
-        del xb, ob
-    for pt in batched["points"]:
-        if pt["M"] == 128:
-            batched[f"M128_{pt['mode']}"] = {k: pt[k] for k in ("pass_ms", "weight_GBps", "tflops", "mfma_util")}
-    log("batched verify M=128: W4A16 %.3f ms (%.1f%% of fp16 MFMA), W4A4 %.3f ms (%.1f%% of int8 MFMA)" % (
-        batched["M128_w4a16"]["pass_ms"], 100 * batched["M128_w4a16"]["mfma_util"],
-        batched["M128_w4a4"]["pass_ms"], 100 * batched["M128_w4a4"]["mfma_util"]))
-
-    # ---------------- speculative timing model and draft-length choice (host-side planner)
-    # t_target: one plain decoding step = W4A16 pass at M = 1 (graph-replayed); t_draft: one draft
-    # pass + draft Top-1 of the iteration above; t_verify: its verify pass; t_overhead: its accept
-    # phase.  alpha = 0.96 (the pages' W4A4/W4A16 Top-1 agreement, rounded).
-    from quantized_speculative_decoding_int4_amd import planner as PL
-    ALPHA = 0.96
-    x1 = x_verify[:1].contiguous()
-    o1 = torch.empty((1, V), dtype=torch.float32, device=dev)
-    ws1 = torch.empty(chain.workspace_bytes(qs.QS_W4A16, 1), dtype=torch.uint8, device=dev)
-    qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
-    g1 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g1):
+                torch.cuda.synchronize()
+                ea, eb = E(enable_timing=True), E(enable_timing=True)
+                ea.record()
+                for _ in range(3):
+                    g.replay()
+                eb.record()
+                torch.cuda.synchronize()
+                ms = ea.elapsed_time(eb) / 3
+                ops = 2.0 * m * n_weights
+                batched["points"].append({
+                    "B": B, "gamma": G, "M": m, "mode": mname, "pass_ms": ms,
+                    "weight_GBps": pass_bytes / (ms * 1e-3) / 1e9,
+                    "tflops": ops / (ms * 1e-3) / 1e12,
+                    "mfma_util": ops / (ms * 1e-3) / peaks[mode],
+                    "persistent_launches": chain.pass_launches(mode, m),
+                })
+                del g, wsb
+            assert bool(torch.isfinite(ob).all()), "non-finite batched logits"
+            del xb, ob
+        for pt in batched["points"]:
+            if pt["M"] == 128:
+                batched[f"M128_{pt['mode']}"] = {k: pt[k] for k in ("pass_ms", "weight_GBps", "tflops", "mfma_util")}
+        log("batched verify M=128: W4A16 %.3f ms (%.1f%% of fp16 MFMA), W4A4 %.3f ms (%.1f%% of int8 MFMA)" % (
+            batched["M128_w4a16"]["pass_ms"], 100 * batched["M128_w4a16"]["mfma_util"],
+            batched["M128_w4a4"]["pass_ms"], 100 * batched["M128_w4a4"]["mfma_util"]))
+    
+        # ---------------- speculative timing model and draft-length choice (host-side planner)
+        # t_target: one plain decoding step = W4A16 pass at M = 1 (graph-replayed); t_draft: one draft
+        # pass + draft Top-1 of the iteration above; t_verify: its verify pass; t_overhead: its accept
+        # phase.  alpha = 0.96 (the pages' W4A4/W4A16 Top-1 agreement, rounded).
+        from quantized_speculative_decoding_int4_amd import planner as PL
+        ALPHA = 0.96
+        x1 = x_verify[:1].contiguous()
+        o1 = torch.empty((1, V), dtype=torch.float32, device=dev)
+        ws1 = torch.empty(chain.workspace_bytes(qs.QS_W4A16, 1), dtype=torch.uint8, device=dev)
         qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
-    target_ms = time_calls(g1.replay, reps=10)
-    del g1, ws1
-    # the same one-row pass in W4A8 (8-bit activation codes on the same int8 MFMA), as a draft
-    ws8 = torch.empty(chain.workspace_bytes(qs.QS_W4A8, 1), dtype=torch.uint8, device=dev)
-    qs.qs_chain_forward(qs.QS_W4A8, x1, chain, out=o1, ws=ws8)
-    g8 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g8):
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            qs.qs_chain_forward(qs.QS_W4A16, x1, chain, out=o1, ws=ws1)
+        target_ms = time_calls(g1.replay, reps=10)
+        del g1, ws1
+        # the same one-row pass in W4A8 (8-bit activation codes on the same int8 MFMA), as a draft
+        ws8 = torch.empty(chain.workspace_bytes(qs.QS_W4A8, 1), dtype=torch.uint8, device=dev)
         qs.qs_chain_forward(qs.QS_W4A8, x1, chain, out=o1, ws=ws8)
-    w4a8_draft_ms = time_calls(g8.replay, reps=10)
-    del g8, ws8
-    t_draft1 = draft_ms / GAMMA
-    spec = {
-        "alpha": ALPHA, "gamma": GAMMA,
-        "expected_tokens": PL.expected_tokens(ALPHA, GAMMA),
-        "t_target_ms": target_ms, "t_draft_ms": t_draft1, "t_verify_ms": verify_ms, "t_overhead_ms": accept_ms,
-        "modelled_speedup": PL.modelled_speedup(ALPHA, GAMMA, target_ms, t_draft1, verify_ms, accept_ms),
-        "itl_ms": PL.inter_token_latency(ALPHA, GAMMA, ms_step),
-        "target_itl_ms": target_ms,
-        "w4a8_draft_pass_ms": w4a8_draft_ms,
-        "w4a8_draft_persistent_launches": chain.pass_launches(qs.QS_W4A8, 1),
-    }
-    # per batch: draft step = W4A4 pass at M = B (B = 1: the draft pass above), verify = W4A16 pass at
-    # M = B (gamma + 1), both from the sweep; accept / Top-1 costs (tens of us) left out
-    pts = {(p_["mode"], p_["M"]): p_["pass_ms"] for p_ in batched["points"]}
-    choice = {}
-    for B in (1, 4, 16):
-        td = t_draft1 if B == 1 else pts.get(("w4a4", B))
-        tv = {G: pts[("w4a16", B * (G + 1))] for G in (3, 5, 7) if ("w4a16", B * (G + 1)) in pts}
-        if td is None or not tv:
-            continue
-        c = PL.choose_gamma(ALPHA, B, td, tv)
-        choice[f"B{B}"] = {"best_gamma": c["best_gamma"], "t_draft_ms": td,
-                           "tokens_per_s": {str(G): 1e3 * r["tokens_per_time"] for G, r in c["table"].items()}}
-    spec["gamma_choice"] = choice
-    log("speculative model: E[T] %.3f, t_target %.3f ms, speed-up %.3f, ITL %.3f ms (target alone %.3f); "
-        "best gamma by batch %s" % (spec["expected_tokens"], target_ms, spec["modelled_speedup"], spec["itl_ms"],
-                                    target_ms, {k: v["best_gamma"] for k, v in choice.items()}))
+        g8 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g8):
+            qs.qs_chain_forward(qs.QS_W4A8, x1, chain, out=o1, ws=ws8)
+        w4a8_draft_ms = time_calls(g8.replay, reps=10)
+        del g8, ws8
+        t_draft1 = draft_ms / GAMMA
+        spec = {
+            "alpha": ALPHA, "gamma": GAMMA,
+            "expected_tokens": PL.expected_tokens(ALPHA, GAMMA),
+            "t_target_ms": target_ms, "t_draft_ms": t_draft1, "t_verify_ms": verify_ms, "t_overhead_ms": accept_ms,
+            "modelled_speedup": PL.modelled_speedup(ALPHA, GAMMA, target_ms, t_draft1, verify_ms, accept_ms),
+            "itl_ms": PL.inter_token_latency(ALPHA, GAMMA, ms_step),
+            "target_itl_ms": target_ms,
+            "w4a8_draft_pass_ms": w4a8_draft_ms,
+            "w4a8_draft_persistent_launches": chain.pass_launches(qs.QS_W4A8, 1),
+        }
+        # per batch: draft step = W4A4 pass at M = B (B = 1: the draft pass above), verify = W4A16 pass at
+        # M = B (gamma + 1), both from the sweep; accept / Top-1 costs (tens of us) left out
+        pts = {(p_["mode"], p_["M"]): p_["pass_ms"] for p_ in batched["points"]}
+        choice = {}
+        for B in (1, 4, 16):
+            td = t_draft1 if B == 1 else pts.get(("w4a4", B))
+            tv = {G: pts[("w4a16", B * (G + 1))] for G in (3, 5, 7) if ("w4a16", B * (G + 1)) in pts}
+            if td is None or not tv:
+                continue
+            c = PL.choose_gamma(ALPHA, B, td, tv)
+            choice[f"B{B}"] = {"best_gamma": c["best_gamma"], "t_draft_ms": td,
+                               "tokens_per_s": {str(G): 1e3 * r["tokens_per_time"] for G, r in c["table"].items()}}
+        spec["gamma_choice"] = choice
+        log("speculative model: E[T] %.3f, t_target %.3f ms, speed-up %.3f, ITL %.3f ms (target alone %.3f); "
+            "best gamma by batch %s" % (spec["expected_tokens"], target_ms, spec["modelled_speedup"], spec["itl_ms"],
+                                        target_ms, {k: v["best_gamma"] for k, v in choice.items()}))
+        return accept, fused_top1, per_linear, batched, spec
+
+    if args.core_only:
+        accept, fused_top1, per_linear, batched, spec = None, None, None, None, None
+    else:
+        accept, fused_top1, per_linear, batched, spec = optional_sections()
 
     # ---------------- rooflines of the pass kernels (HIP events on the launch stream)
     # Algorithmic bytes of one pass: packed weights (0.515625 B per weight) plus, per linear,
     # x = 2*M*K and y = 4*M*N bytes.  A pass runs as `launches` persistent launches, each
-    # preceded by a one-workgroup control reset; bytes and time are averaged per launch.
+    # preceded by a one-workgroup control reset; bytes and time are averaged per launch.  The pass
+    # is the one of the iteration: the LM-head's Top-1 fused into the last stage.
     stream = torch.cuda.current_stream()
 
-    def pass_roofline(mode, m, x, out, ws, name, traffic_key, reps=10):
+    def pass_roofline(mode, m, x, out, top1, ws, name, traffic_key, reps=10):
         launches = chain.pass_launches(mode, m)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            qs.qs_chain_forward(mode, x, chain, out=out, ws=ws)
+            qs.qs_chain_forward_top1(mode, x, chain, out=out, top1=top1, want_prob=False, ws=ws)
         g.replay()
         torch.cuda.synchronize()
         evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
@@ -722,9 +734,9 @@ def main():
                 "bytes_per_launch": alg / per, "avg_launch_us": pass_ms * 1e3 / per,
                 "launches_per_pass": launches, "passes_timed": reps}
 
-    roof_draft = pass_roofline(qs.QS_W4A4, 1, x_draft[0], logits_q[0, 0:1], ws_draft,
+    roof_draft = pass_roofline(qs.QS_W4A4, 1, x_draft[0], logits_q[0, 0:1], d_steps[0], ws_draft,
                                "pass_kernel<W4A4> (draft pass, M=1, int8 MFMA)", "w4a4")
-    roof_verify = pass_roofline(qs.QS_W4A16, M_VERIFY, x_verify, logits_p[0], ws_verify,
+    roof_verify = pass_roofline(qs.QS_W4A16, M_VERIFY, x_verify, logits_p[0], t_verify, ws_verify,
                                 "pass_kernel<W4A16> (verify pass, M=4, fp16 MFMA)", "w4a16")
 
     cpu = None
