@@ -1,5 +1,5 @@
 // Persistent pass kernel: one launch runs up to kMaxPassStages linears of a chain
-// (the W4A4 draft pass at M = 1 row or the W4A16 verify pass at up to 14 rows,
+// (the W4A4 draft pass at up to 4 rows or the W4A16 verify pass at up to 14 rows,
 // [P3] "draft modelとtarget modelの処理フロー"; modes from [P1] "QSpec の W4A4
 // モードと W4A16 モード"; W4A8 from [P2] "3.中核となる技術的要素").  The integer modes W4A4
 // and W4A8 share one kernel body and differ only in the activation code range (7 or 127).
@@ -18,7 +18,7 @@
 // device-coherent loads (both go past the per-XCD L2 to memory), so no L2
 // write-back or invalidate is needed (an agent-scope release/acquire costs about
 // 3.5 us per boundary on MI355X).  Two ways to know the input is complete:
-//  * W4A4 and W4A8 (one row, 8-28 KiB of input): the data carries the signal.  The output
+//  * W4A4 and W4A8 (up to 4 rows, 8-112 KiB of input): the data carries the signal.  The output
 //    buffers start filled with the pattern 0xFFFF (a NaN the epilogue never
 //    emits: it rewrites that one pattern as the canonical NaN 0x7E00).  A
 //    consumer fetches its input as soon as its own stage is done and reads again
@@ -107,7 +107,7 @@ constexpr size_t kPassLdsStageInt = 81920;
 constexpr size_t kPassLdsMin = 81920;
 constexpr int kPassSlots = 4;              // row-block sets a workgroup may own per stage
 constexpr int kCtrlSlots = (kPassSlots * kPW + kCW - 1) / kCW;  // (set, row block) pairs per control wave
-constexpr int kPiecesMax4 = 8;             // W4A4: 16-byte input pieces a control thread holds per stage
+constexpr int kPiecesMax4 = 16;            // W4A4: 16-byte input pieces of a control thread per stage (two rounds above 8)
 constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
 constexpr int kSc1 = 16;                   // cache-policy bit SC1: device-coherent access
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw 32-bit buffer resource, no swizzle
@@ -369,7 +369,10 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
   }
 }
 
-template <int MODE>
+// WIDE (integer modes, more than one row): rows of up to kPiecesMax4 pieces per control thread,
+// staged in two rounds above 8; a separate instance, since the second round's code costs the one-row
+// kernel registers it does not have to spare.
+template <int MODE, bool WIDE>
 __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // Partials of the streaming waves: fp32 (W4A16) or fp64 (the integer modes: exact sums).
   using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
@@ -652,8 +655,14 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // branch.  The loads are unconditional: a load under a condition is merged with the old value by
   // a select, and the compiler then keeps two copies of all pieces live.  Pieces past this thread's
   // count are read (next row, or zeros past the buffer resource's extent) and not used.
-  auto stage_in4 = [&](auto pc, int s, bool has) __attribute__((always_inline)) {
+  // Rows wider than P pieces per thread (the 14336-wide down projection at 4 rows) are taken in H
+  // rounds of P pieces: each round is loaded (and, within a pass, polled until complete) and added to
+  // the statistics; after the row parameters every round but the last, whose pieces are still in
+  // registers, is loaded again (complete by then) to be quantised.  Holding 16 pieces per thread in
+  // registers instead spilled.
+  auto stage_in4 = [&](auto pc, auto hc, int s, bool has) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
+    constexpr int H = decltype(hc)::value;
     const PassStage ps = stage_at(s);
     const int K = ps.K;  // integer modes take whole linears (no chunks)
     const uint16_t* x;
@@ -668,32 +677,35 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     const uint32_t voff = (uint32_t)(((my_row < M ? my_row : 0) * ldx + 8 * row_tid) * 2);
     const uint32_t pstride = (uint32_t)gsz * 16u;
     uint4 v[P];
-    if (active) {
-#pragma unroll
-      for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)j * pstride);
-      if (s > 0) {
-        auto pending = [&]() {
-          uint32_t m = 0;
-#pragma unroll
-          for (int j = 0; j < P; ++j)
-            if (j < np && has_empty(v[j])) m |= 1u << j;
-          return m;
-        };
-        const long long t0 = wall_clock64();
-        while (a.deadline <= 0 || __any(pending() != 0u)) {
-          if (wait_failed(t0)) break;
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-          for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)j * pstride);  // data, once there, stays
-        }
-      }
-    }
     double su = 0.0, sq = 0.0;
     float mx = -INFINITY, mn = INFINITY;
-    if (active) {
+#pragma unroll 1
+    for (int h = 0; h < H; ++h) {
+      const int nh = np - h * P;  // this round's pieces (may be <= 0)
+      if (active) {
 #pragma unroll
-      for (int j = 0; j < P; ++j)
-        if (j < np) stats_block8_64(v[j], su, sq, mx, mn);
+        for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)(h * P + j) * pstride);
+        if (s > 0) {
+          auto pending = [&]() {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < P; ++j)
+              if (j < nh && has_empty(v[j])) m |= 1u << j;
+            return m;
+          };
+          const long long t0 = wall_clock64();
+          while (a.deadline <= 0 || __any(pending() != 0u)) {
+            if (wait_failed(t0)) break;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < P; ++j)
+              v[j] = load_sc1(rs, voff, (uint32_t)(h * P + j) * pstride);  // data, once there, stays
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+          if (j < nh) stats_block8_64(v[j], su, sq, mx, mn);
+      }
     }
     su = wave_sum_dpp64(su);
     sq = wave_sum_dpp64(sq);
@@ -730,14 +742,22 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K + 8 * row_tid;
       const double mu = row_mu64[my_row], inv = row_inv64[my_row];
       const float sc = row_c[my_row];
+#pragma unroll 1
+      for (int h = H - 1; h >= 0; --h) {  // the last round first: its pieces are still in registers
+        const int nh = np - h * P;
+        if (h < H - 1) {
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        if (j < np) {
-          uint4 w = v[j];
-          if (norm) w = norm_block8_64(w, mu, inv);
-          uint2 op, lg;
-          quant_block8<kPassQmax<MODE>>(w, sc, op, lg);
-          *reinterpret_cast<uint2*>(xq + j * (pstride / 2)) = op;
+          for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)(h * P + j) * pstride);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (j < nh) {
+            uint4 w = v[j];
+            if (norm) w = norm_block8_64(w, mu, inv);
+            uint2 op, lg;
+            quant_block8<kPassQmax<MODE>>(w, sc, op, lg);
+            *reinterpret_cast<uint2*>(xq + (h * P + j) * (pstride / 2)) = op;
+          }
         }
       }
     }
@@ -750,13 +770,16 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       stage_in16(s, has);
     } else {
       const int npmax = (stage_at(s).K / 8 + gsz - 1) / gsz;  // <= kPiecesMax4 (host check)
-      static_assert(kPiecesMax4 == 8, "piece buckets below end at kPiecesMax4");
+      static_assert(kPiecesMax4 == 16, "piece buckets below end at kPiecesMax4");
+      using one = std::integral_constant<int, 1>;
       if (npmax <= 2)
-        stage_in4(std::integral_constant<int, 2>{}, s, has);
+        stage_in4(std::integral_constant<int, 2>{}, one{}, s, has);
       else if (npmax <= 4)
-        stage_in4(std::integral_constant<int, 4>{}, s, has);
-      else
-        stage_in4(std::integral_constant<int, 8>{}, s, has);
+        stage_in4(std::integral_constant<int, 4>{}, one{}, s, has);
+      else if (!WIDE || npmax <= 8)  // one row: at most 8 (host check)
+        stage_in4(std::integral_constant<int, 8>{}, one{}, s, has);
+      else if constexpr (WIDE)
+        stage_in4(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{}, s, has);
     }
   };
 
@@ -898,8 +921,6 @@ static int pass_chunks(int mode, int M, int K) {
 static int chunk_groups(int K, int nch) { return (K / kGroup + nch - 1) / nch; }
 
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
-  // W4A4 above one row: every workgroup would quantize all rows itself and the fp16 exchange grows
-  // with M; measured on MI355X, one launch per linear is as fast from M = 2 on.
   if (M > pass_max_rows(mode)) return false;
   const int grid = device_info()->num_cus;
   if (grid < 1 || grid > kMaxPassWorkgroups) return false;
@@ -907,7 +928,7 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   for (int i = 0; i < n; ++i) {
     const int nch = pass_chunks(mode, M, c[i].K);
     if (nch < 1 || nch > kMaxPassStages) return false;
-    if (mode != QS_W4A16 && c[i].K / 8 > kPiecesMax4 * gsz) return false;
+    if (mode != QS_W4A16 && c[i].K / 8 > (M > 1 ? kPiecesMax4 : 8) * gsz) return false;
     if (pick_pass_split(c[i].N, chunk_groups(c[i].K, nch) * kGroup, grid) < 0) return false;
   }
   return true;
@@ -917,7 +938,11 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
 // standardisation's weight sums).  Measured over the Llama-3-8B-shaped stack: 5, 6, 8, 12 rows
 // 1.41, 1.40, 1.43, 1.90 ms per pass against 2.1-2.3 ms with one launch per linear; at 15 rows every
 // 4096-wide linear needs two K chunks and the pass took 2.25 ms against 2.12 ms.
-int pass_max_rows(int mode) { return mode == QS_W4A16 ? 14 : (mode == QS_W4A4 || mode == QS_W4A8) ? 1 : 0; }
+//
+// The integer modes take up to 4 rows (every workgroup standardises and quantises all rows itself,
+// so the staging grows with M): W4A4 pass 1.42 / 1.81 / 2.34 / 2.41 ms at 1 / 2 / 3 / 4 rows against
+// 2.97 ms with one launch per linear at 4 rows.
+int pass_max_rows(int mode) { return mode == QS_W4A16 ? 14 : (mode == QS_W4A4 || mode == QS_W4A8) ? 4 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   size_t b = 0;
@@ -976,20 +1001,21 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
                 unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1) {
   const DeviceInfo* di = device_info();
   const int grid = di->num_cus;
-  auto fn0 = pass_kernel<0>;
-  auto fn1 = pass_kernel<1>;
-  auto fn2 = pass_kernel<2>;
-  const void* fn = mode == QS_W4A16 ? reinterpret_cast<const void*>(fn0)
-                   : mode == QS_W4A4 ? reinterpret_cast<const void*>(fn1)
-                                     : reinterpret_cast<const void*>(fn2);
-  static int lds_set[3] = {0, 0, 0};
-  if (!lds_set[mode]) {
+  const bool wide = mode != QS_W4A16 && M > 1;
+  const int variant = mode + (wide ? 2 : 0);  // 0 W4A16, 1 W4A4, 2 W4A8, 3 W4A4 wide, 4 W4A8 wide
+  const void* fns[5] = {reinterpret_cast<const void*>(pass_kernel<0, false>),
+                        reinterpret_cast<const void*>(pass_kernel<1, false>),
+                        reinterpret_cast<const void*>(pass_kernel<2, false>),
+                        reinterpret_cast<const void*>(pass_kernel<1, true>),
+                        reinterpret_cast<const void*>(pass_kernel<2, true>)};
+  static int lds_set[5] = {0, 0, 0, 0, 0};
+  if (!lds_set[variant]) {
     const int limit = (int)(mode == QS_W4A16 ? kPassLdsStage : kPassLdsStageInt);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, limit) != hipSuccess) {
+    if (hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, limit) != hipSuccess) {
       (void)hipGetLastError();  // report it here, not at the caller's next HIP call
       return QS_ERR_HIP;
     }
-    lds_set[mode] = 1;
+    lds_set[variant] = 1;
   }
   size_t lds = kPassLdsMin;
   for (int i = 0; i < n; ++i) {
@@ -1072,12 +1098,13 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     }
     a.n_stages = e;
     entry0 += e;
-    if (mode == QS_W4A16)
-      hipLaunchKernelGGL(pass_kernel<0>, dim3(grid), dim3(kPThreads), lds, st, a);
-    else if (mode == QS_W4A4)
-      hipLaunchKernelGGL(pass_kernel<1>, dim3(grid), dim3(kPThreads), lds, st, a);
-    else
-      hipLaunchKernelGGL(pass_kernel<2>, dim3(grid), dim3(kPThreads), lds, st, a);
+    switch (variant) {
+      case 0: hipLaunchKernelGGL((pass_kernel<0, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 1: hipLaunchKernelGGL((pass_kernel<1, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 2: hipLaunchKernelGGL((pass_kernel<2, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 3: hipLaunchKernelGGL((pass_kernel<1, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      default: hipLaunchKernelGGL((pass_kernel<2, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+    }
     rc = launch_status();
     if (rc != QS_OK) return rc;
   }

@@ -103,21 +103,21 @@ def test_chain_with_vocabulary_wide_head(qs, mode, m):
 @pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
     """75 linears.  At M <= 4 (W4A16) / M = 1 (integer modes) the persistent pass splits them over
-    two launches (at most 72 per launch), so the hand-over at the seam is covered; so does W4A16 up
-    to 14 rows; the other row counts run linear by linear."""
+    two launches (at most 72 per launch), so the hand-over at the seam is covered; so do W4A16 up
+    to 14 rows and the integer modes up to 4; the other row counts run linear by linear."""
     print(f"long chain mode={mode} m={m}", flush=True)
     rng = W.rng_for(900 + 10 * m + mode)
     shapes = [(384, 256), (256, 384)] * 37 + [(1000, 256)]
     layers = [W.int4_weights(rng, n, k) for n, k in shapes]
     x, _ = W.activations(rng, m, 256)
     chain = _pack_chain(qs, layers)
-    persistent = (m <= 14) if mode == 0 else (m <= 1)
+    persistent = (m <= 14) if mode == 0 else (m <= 4)
     assert chain.pass_launches(mode, m) == (2 if persistent else 0)
     y = host(qs.qs_chain_forward(mode, dev(x), chain))
     _check(y, O.chain_forward(MODE_NAMES[mode], x, layers), mode, "long75", f"long chain mode={mode} m={m}")
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (1, 4), (2, 3)])
 def test_barrier_timeout_is_reported_and_cleared(qs, mode, m):
     """A zero time-out makes the first wait of a persistent pass fail at once (W4A16: the grid
     barrier; the integer modes: the poll for the next stage's input): every workgroup exits (no
@@ -213,6 +213,31 @@ def test_chain_top1_after_a_timeout(qs, mode, m):
     _check_fused_top1(host(out), host(t1), host(p1), "after a time-out")
 
 
+# ---------------------------------------------------------------- integer-mode persistent pass above one row
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_chain_int_rows_2_to_4(qs, mode, m):
+    """The integer-mode persistent pass at 2-4 rows (its own kernel instance), on a chain with a
+    14336-wide input: at 3 and 4 rows a control thread's share of such a row exceeds 8 pieces and is
+    staged in two rounds.  Bit-exact against the oracle, like every integer chain; and its fused
+    Top-1."""
+    print(f"int rows mode={mode} m={m}", flush=True)
+    rng = W.rng_for(1010 + 10 * m + mode)
+    shapes = [(14336, 512), (512, 14336), (4096, 512), (2000, 4096)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 512)
+    chain = _pack_chain(qs, layers)
+    assert chain.pass_launches(mode, m) == 1
+    xd = dev(x)
+    y = host(qs.qs_chain_forward(mode, xd, chain))
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
+    assert_exact(y, ref, f"int rows mode={mode} m={m}")
+    out, t1, p1 = qs.qs_chain_forward_top1(mode, xd, chain)
+    assert np.array_equal(host(out), y)
+    _check_fused_top1(y, host(t1), host(p1), f"int rows mode={mode} m={m}")
+
+
 # ---------------------------------------------------------------- W4A16 persistent pass above four rows (K chunks)
 
 @pytest.mark.parametrize("m", [5, 8, 12, 14])
@@ -298,7 +323,7 @@ def _sampled_head(st):
     return st["host"][:-1] + [(hq[st["cols"]], hs[st["cols"]])]
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 8), (0, 128), (1, 128), (2, 64)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 8), (1, 4), (0, 128), (1, 128), (2, 64)])
 def test_full_stack_against_the_oracle(qs, mode, m):
     """The whole stack in the bench's launch configurations: the persistent pass (W4A16 verify at
     M = 4 and at M = 8, where the down projection runs in two K chunks; W4A4 / W4A8 draft at M = 1)
@@ -310,7 +335,7 @@ def test_full_stack_against_the_oracle(qs, mode, m):
     print(f"full stack mode={mode} m={m}", flush=True)
     st = _stack(qs)
     chain = st["chain"]
-    persistent_rows = {0: 14, 1: 1, 2: 1}[mode]
+    persistent_rows = {0: 14, 1: 4, 2: 4}[mode]
     # W4A16 above 4 rows splits the down projection's K into chunks: more entries, three launches
     assert chain.pass_launches(mode, m) == (0 if m > persistent_rows else 2 if m <= 4 else 3)
     x = W.activations(W.rng_for(31), m, W.HIDDEN)[0]
