@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--core-only", action="store_true",
                     help="time the iteration and the pass rooflines only (for counter runs under a profiler: no "
                          "accept, per-linear, batched or timing-model sections)")
+    ap.add_argument("--pass-trace", action="store_true",
+                    help="instead of the bench: time every stage boundary of the persistent passes from in-kernel "
+                         "timestamps (qs_chain_forward_trace) and print the breakdown as one JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device to device twice (a plain copy kernel of known "
                          "size, to scale memory-traffic counters under a profiler)")
@@ -126,6 +129,80 @@ def cpu_baseline(budget_s: float):
                    f"down and an 8192-row LM-head block) in {t_used:.1f} s; float64 NumPy, "
                    f"BLAS threads {threads}, affinity cores {cores}"),
     }
+
+
+def pass_trace_report(qs, W, torch, chain, shapes):
+    """Boundary breakdown of the persistent passes of the Llama-shaped stack from the timestamps of
+    qs_chain_forward_trace: per workgroup and entry, t0 input staged, t1 stage done (partials parked),
+    t2 outputs stored, t3 hand-over done.  Per boundary (entry e -> e + 1), medians over workgroups of
+    epilogue = t2 - t1, hand-over = t3 - t2, staging = t0(e + 1) - t3 and the whole gap
+    t0(e + 1) - t1, grouped by the linear the boundary feeds; per stage, the median streaming time
+    t1 - t0.  Ticks are converted with the rate implied by a HIP-event-timed pass."""
+    import numpy as np
+    dev = "cuda"
+    kinds = [name.split(".")[-1] if "." in name else name for name, _, _ in shapes]
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    report = {"workload": "Llama-3-8B-shaped INT4 stack, 129 linears", "grid": grid, "passes": {}}
+    rng = W.rng_for(5)
+    for mode, m, label in ((qs.QS_W4A16, 4, "verify W4A16 M=4"), (qs.QS_W4A4, 1, "draft W4A4 M=1"),
+                           (qs.QS_W4A16, 1, "target W4A16 M=1"), (qs.QS_W4A4, 4, "draft W4A4 M=4")):
+        nbytes = chain.trace_bytes(mode, m)
+        if nbytes == 0:
+            continue
+        x = torch.from_numpy(W.activations(rng, m, W.HIDDEN)[0]).to(dev)
+        out = torch.empty((m, chain.out_features), dtype=torch.float32, device=dev)
+        ws = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=dev)
+        tr = torch.zeros(nbytes // 8, dtype=torch.int64, device=dev)
+        for _ in range(3):  # warm
+            qs.qs_chain_forward_trace(mode, x, chain, tr, out=out, ws=ws)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        qs.qs_chain_forward_trace(mode, x, chain, tr, out=out, ws=ws)
+        eb.record()
+        torch.cuda.synchronize()
+        ms = ea.elapsed_time(eb)
+        t = tr.cpu().numpy().reshape(-1, grid, 4).astype(np.float64)
+        span = t[:, :, 3].max() - t[:, :, 0].min()
+        rate = span / (ms * 1e-3)  # ticks per second, the pass's own (launch overheads included)
+        us = 1e6 / rate
+        n_e = t.shape[0]
+        if n_e != len(shapes):  # K-chunked entries: not broken down per linear here
+            report["passes"][label] = {"entries": n_e, "pass_ms": ms}
+            continue
+        stream = np.median(t[:, :, 1] - t[:, :, 0], axis=1) * us
+        epi = np.median(t[:-1, :, 2] - t[:-1, :, 1], axis=1) * us
+        hand = np.median(t[:-1, :, 3] - t[:-1, :, 2], axis=1) * us
+        stag = np.median(t[1:, :, 0] - t[:-1, :, 3], axis=1) * us
+        gap = np.median(t[1:, :, 0] - t[:-1, :, 1], axis=1) * us
+        by = {}
+        for e in range(n_e - 1):
+            k = kinds[e + 1]
+            d = by.setdefault(k, {"n": 0, "epilogue_us": [], "handover_us": [], "staging_us": [], "gap_us": []})
+            d["n"] += 1
+            d["epilogue_us"].append(epi[e])
+            d["handover_us"].append(hand[e])
+            d["staging_us"].append(stag[e])
+            d["gap_us"].append(gap[e])
+        feeds = {k: {"boundaries": v["n"], **{f: float(np.median(v[f])) for f in
+                                              ("epilogue_us", "handover_us", "staging_us", "gap_us")}}
+                 for k, v in by.items()}
+        streams = {}
+        for e in range(n_e):
+            streams.setdefault(kinds[e], []).append(stream[e])
+        report["passes"][label] = {
+            "pass_ms": ms, "ticks_per_s": rate, "entries": n_e,
+            "sum_gap_ms": float(gap.sum()) / 1e3, "sum_stream_ms": float(stream.sum()) / 1e3,
+            "boundary_into": feeds,
+            "stage_stream_us": {k: float(np.median(v)) for k, v in streams.items()},
+        }
+        log(f"{label}: pass {ms:.3f} ms; per-workgroup gaps sum to {gap.sum() / 1e3:.3f} ms, streaming "
+            f"{stream.sum() / 1e3:.3f} ms (medians over workgroups)")
+        for k, v in feeds.items():
+            log(f"  into {k:8s} x{v['boundaries']:3d}: epilogue {v['epilogue_us']:.2f}  hand-over "
+                f"{v['handover_us']:.2f}  staging {v['staging_us']:.2f}  gap {v['gap_us']:.2f} us; stage "
+                f"streams {report['passes'][label]['stage_stream_us'][k]:.2f} us")
+        del x, out, ws, tr
+    print(json.dumps(report), flush=True)
 
 
 def linear_rates(qs, W, torch, E):
@@ -312,6 +389,9 @@ def main():
     torch.cuda.synchronize()
     chain = qs.Chain(layers)
     log(f"packed {len(shapes)} linears, {pass_bytes} weight bytes per pass, {time.perf_counter() - t0:.1f} s")
+    if args.pass_trace:
+        pass_trace_report(qs, W, torch, chain, shapes)
+        return
 
     # ---------------- inputs and buffers
     rng = W.rng_for(3)

@@ -280,6 +280,36 @@ int qs_chain_pass_status(int mode, int M, const qs_linear_desc* chain, int n, vo
                          size_t ws_bytes, int* timed_out, void* stream);
 
 /*
+ * Measurement helpers of the persistent pass, for profiling the stage
+ * hand-over; they compute nothing the pages define beyond qs_chain_forward.
+ *
+ * qs_chain_trace_bytes -- bytes of the timestamp buffer of qs_chain_forward_trace
+ * for this chain and row count: entries x workgroups x 4 x 8, where entries is
+ * the number of stage-table entries of the pass (a linear, or one K chunk of a
+ * linear) and workgroups the number of compute units.  0 when the row count
+ * does not run as a persistent pass (or for invalid arguments).
+ *
+ * qs_chain_forward_trace -- qs_chain_forward (same arguments, workspace, output
+ * and errors), and in addition writes to the device buffer trace
+ * (uint64 [entries][workgroups][4], trace_bytes >= qs_chain_trace_bytes,
+ * 16-byte aligned, owned by the caller) the device wall-clock (the 100 MHz
+ * realtime counter, read by each workgroup's first control thread) at four
+ * points of every entry:
+ *   [0] the entry's input is staged in LDS (its streaming may start);
+ *   [1] the streaming waves have parked the entry's partial sums;
+ *   [2] the entry's outputs are stored (W4A16: all of the workgroup's stores
+ *       acknowledged; the integer modes: the first control wave's stores issued);
+ *   [3] the hand-over is done (W4A16: all workgroups' arrival flags seen; equal
+ *       to [2] where no grid barrier follows).
+ * The timestamps cost one store each; results equal qs_chain_forward's.
+ * QS_ERR_UNSUPPORTED when the row count runs one launch per linear.
+ */
+size_t qs_chain_trace_bytes(int mode, int M, const qs_linear_desc* chain, int n);
+int qs_chain_forward_trace(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n,
+                           float* out, void* ws, size_t ws_bytes, unsigned long long* trace,
+                           size_t trace_bytes, void* stream);
+
+/*
  * Workspace bytes for qs_verify_greedy / qs_verify_sample at (B, gamma, V);
  * 0 for arguments out of range (gamma > 63).  A batch of more than
  * QS_MAX_VERIFY_SEQS sequences runs as consecutive blocks of at most that many

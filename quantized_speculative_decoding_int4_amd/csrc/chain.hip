@@ -56,7 +56,8 @@ static size_t top1_bytes(int mode, int M, const qs_linear_desc* c, int n) {
 
 // One pass of the chain; t1 (nullable) asks for the final stage's Top-1, with its region at t1_ws.
 static int chain_run(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
-                     int32_t* top1, float* top1_prob, void* ws, size_t ws_bytes, hipStream_t st) {
+                     int32_t* top1, float* top1_prob, void* ws, size_t ws_bytes, hipStream_t st,
+                     unsigned long long* trace = nullptr) {
   const size_t ab = act_bytes(M, chain, n);
   uint16_t* buf[2] = {reinterpret_cast<uint16_t*>(ws),
                       reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + ab)};
@@ -69,7 +70,7 @@ static int chain_run(int mode, const uint16_t* x, int M, const qs_linear_desc* c
         reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(qws) + scratch_bytes(mode, M, chain, n));
     PassTop1 t1{top1, top1_prob, t1_ws};
     return launch_pass(mode, x, M, chain, n, out, static_cast<unsigned*>(qws), stage_out, st,
-                       top1 ? &t1 : nullptr);
+                       top1 ? &t1 : nullptr, trace);
   }
   const uint16_t* in = x;
   int ldx = chain[0].K;
@@ -121,6 +122,27 @@ int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n) 
   if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
   if (!device_info()->ok) return QS_ERR_DEVICE;
   return pass_eligible(mode, M, chain, n) ? pass_launch_count(mode, M, chain, n) : 0;
+}
+
+size_t qs_chain_trace_bytes(int mode, int M, const qs_linear_desc* chain, int n) {
+  if ((mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) || M < 1 || M > QS_MAX_M || !chain_ok(chain, n)) return 0;
+  if (!device_info()->ok || !pass_eligible(mode, M, chain, n)) return 0;
+  return (size_t)pass_entry_count(mode, M, chain, n) * (size_t)device_info()->num_cus * 4 * sizeof(unsigned long long);
+}
+
+int qs_chain_forward_trace(int mode, const uint16_t* x, int M, const qs_linear_desc* chain, int n, float* out,
+                           void* ws, size_t ws_bytes, unsigned long long* trace, size_t trace_bytes, void* stream) {
+  if (mode != QS_W4A16 && mode != QS_W4A4 && mode != QS_W4A8) return QS_ERR_INVALID_ARG;
+  if (!x || !out || !trace || !chain_ok(chain, n) || M < 1) return QS_ERR_INVALID_ARG;
+  if (M > QS_MAX_M) return QS_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(trace)) return QS_ERR_MISALIGNED;
+  if (!ws || ws_bytes < chain_workspace(mode, M, chain, n)) return QS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QS_ERR_MISALIGNED;
+  if (!device_info()->ok) return QS_ERR_DEVICE;
+  if (!pass_eligible(mode, M, chain, n)) return QS_ERR_UNSUPPORTED;  // nothing to trace: one launch per linear
+  if (trace_bytes < qs_chain_trace_bytes(mode, M, chain, n)) return QS_ERR_WORKSPACE;
+  return chain_run(mode, x, M, chain, n, out, nullptr, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                   trace);
 }
 
 int qs_set_barrier_timeout_us(int us) {

@@ -150,6 +150,10 @@ struct PassArgs {
   unsigned epoch0;    // W4A16: epochs of this launch's boundaries are epoch0 + 1, epoch0 + 2, ...
   unsigned* error;    // set to 1 if a wait passed its deadline
   long long deadline; // wall-clock ticks allowed per wait
+  // Boundary timestamps (nullable): wall-clock ticks per (pass-wide entry trace_e0 + s, workgroup),
+  // four per entry -- input staged, partials parked (stage done), outputs stored, hand-over done.
+  unsigned long long* trace;
+  int trace_e0;
   int M;
   int n_stages;
   PassStage st[kMaxPassStages];
@@ -783,6 +787,12 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
   };
 
+  // one timestamp of the running entry, from the first control thread (trace runs only)
+  auto trace_mark = [&](int s, int k) __attribute__((always_inline)) {
+    if (a.trace != nullptr && ct == 0)
+      a.trace[((size_t)(a.trace_e0 + s) * (size_t)grid + (size_t)bid) * 4 + k] = (unsigned long long)wall_clock64();
+  };
+
   constexpr int kCarry = MODE == 0 ? kCtrlSlots : 1;
   Acc carry[kCarry];  // W4A16 chunked linears: this wave's partial sums of the earlier chunks
 #pragma unroll
@@ -790,7 +800,9 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   for (int s = 0; s < a.n_stages; ++s) {
     prologue(s);
     if (__builtin_amdgcn_readfirstlane(fail_sh)) return;
+    trace_mark(s, 0);
     lds_barrier();  // A: the streaming waves have parked the partials of stage s
+    trace_mark(s, 1);
     const PassStage ps = stage_at(s);
     const int sets = stage_sets(ps, bid, grid);
     const bool final_out = a.last_is_final && s + 1 == a.n_stages;
@@ -859,12 +871,14 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
     if (want_t1) top1_epilogue(Top1Out{a.top1, a.top1_prob, a.t1_stats, a.t1_cnt}, t1v, t1_wave, &t1_arrive, cw, lane,
                                bid, grid, M);
+    bool marked = false;
     if constexpr (MODE == 0) {
       // grid barrier after a linear's last chunk: all outputs of the linear are in memory (the
       // streaming waves take the same condition)
       if (s + 1 < a.n_stages && chunk_last(ps)) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's output stores have completed
         lds_barrier();  // B
+        trace_mark(s, 2);
         const unsigned epoch = a.epoch0 + (unsigned)(s + 1);
         if (ct == 0)
           __hip_atomic_store(a.flags + (size_t)bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -872,7 +886,13 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
         for (int t = ct; t < grid; t += kCT)
           if (!wait_at_least(a.flags + (size_t)t * kFlagStride, epoch, a)) fail_sh = 1;
         lds_barrier();  // C
+        trace_mark(s, 3);
+        marked = true;
       }
+    }
+    if (!marked) {  // no grid barrier: the integer modes' data-carried hand-over, or the last entry
+      trace_mark(s, 2);
+      trace_mark(s, 3);
     }
   }
 }
@@ -997,8 +1017,15 @@ static std::atomic<int> g_barrier_timeout_us{200000};
 int pass_barrier_timeout_us() { return g_barrier_timeout_us.load(); }
 void set_pass_barrier_timeout_us(int us) { g_barrier_timeout_us.store(us); }
 
+int pass_entry_count(int mode, int M, const qs_linear_desc* c, int n) {
+  int e = 0;
+  for (int i = 0; i < n; ++i) e += pass_chunks(mode, M, c[i].K);
+  return e;
+}
+
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1) {
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1,
+                unsigned long long* trace) {
   const DeviceInfo* di = device_info();
   const int grid = di->num_cus;
   const bool wide = mode != QS_W4A16 && M > 1;
@@ -1067,6 +1094,8 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     a.error = ctrl + 1;
     a.flags = ctrl + kFlagStride;
     a.epoch0 = (unsigned)entry0;
+    a.trace = trace;
+    a.trace_e0 = entry0;
     a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
     int e = 0;

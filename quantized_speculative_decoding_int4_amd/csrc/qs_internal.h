@@ -95,9 +95,12 @@ struct PassTop1 {
   unsigned char* stats;
 };
 size_t pass_top1_bytes(int M);
-// out nullable when t1 is given
+// out nullable when t1 is given; trace (nullable) receives pass_entry_count(...) x grid x 4 boundary
+// timestamps (wall-clock ticks), [entry][workgroup][4]
 int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int n, float* out,
-                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1 = nullptr);
+                unsigned* ctrl, uint16_t* stage_out, hipStream_t st, const PassTop1* t1 = nullptr,
+                unsigned long long* trace = nullptr);
+int pass_entry_count(int mode, int M, const qs_linear_desc* c, int n);  // stage-table entries of a pass
 
 size_t verify_workspace(int B, int gamma, int V);
 size_t verify_counter_bytes();  // the arrival counters at the start of a verify workspace

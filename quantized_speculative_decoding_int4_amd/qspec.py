@@ -55,6 +55,8 @@ _SIGS = {
     "qs_chain_pass_launches": ([_i, _i, _p, _i], _i),
     "qs_set_barrier_timeout_us": ([_i], _i),
     "qs_chain_pass_status": ([_i, _i, _p, _i, _p, _sz, _p, _p], _i),
+    "qs_chain_trace_bytes": ([_i, _i, _p, _i], _sz),
+    "qs_chain_forward_trace": ([_i, _p, _i, _p, _i, _p, _p, _sz, _p, _sz, _p], _i),
     "qs_verify_greedy": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "qs_verify_greedy_noalloc": ([_p, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
     "qs_verify_greedy_noalloc_max_bytes": ([], _sz),
@@ -372,6 +374,10 @@ class Chain:
         """Workspace of qs_chain_forward_top1."""
         return _lib.qs_chain_top1_workspace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
 
+    def trace_bytes(self, mode: int, m: int) -> int:
+        """Timestamp buffer of qs_chain_forward_trace (0: the row count runs one launch per linear)."""
+        return _lib.qs_chain_trace_bytes(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
+
     def pass_launches(self, mode: int, m: int) -> int:
         """Persistent pass-kernel launches of qs_chain_forward (0: one launch per linear)."""
         rc = _lib.qs_chain_pass_launches(mode, m, ctypes.cast(self.array, ctypes.c_void_p), self.n)
@@ -407,6 +413,23 @@ def qs_chain_forward(mode: int, x, chain: Chain, out=None, ws=None):
         mode, _ptr(x, torch.float16, (m, k), "x"), m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n,
         _ptr(out, torch.float32, (m, chain.out_features), "out"), _ptr(ws, torch.uint8, None, "ws"),
         ws.numel(), _stream()))
+    return out
+
+
+def qs_chain_forward_trace(mode: int, x, chain: Chain, trace, out=None, ws=None):
+    """qs_chain_forward that also records the persistent pass's boundary timestamps into trace
+    (int64 tensor of chain.trace_bytes(mode, M) / 8 elements, viewed as [entries][workgroups][4])."""
+    m, k = x.shape
+    if k != chain.in_features:
+        raise ValueError("x width does not match the first linear")
+    if out is None:
+        out = torch.empty((m, chain.out_features), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(chain.workspace_bytes(mode, m), dtype=torch.uint8, device=x.device)
+    _check("qs_chain_forward_trace", _lib.qs_chain_forward_trace(
+        mode, _ptr(x, torch.float16, (m, k), "x"), m, ctypes.cast(chain.array, ctypes.c_void_p), chain.n,
+        _ptr(out, torch.float32, (m, chain.out_features), "out"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _ptr(trace, torch.int64, None, "trace"), trace.numel() * 8, _stream()))
     return out
 
 

@@ -168,6 +168,23 @@ def test_new_entry_points_argument_errors(lib):
     assert tg(fake, fake, fake, 1, 4, 10, fake, fake, fake, None, fake, 0, None) == -4
 
 
+def test_chain_trace_argument_errors(lib):
+    """The traced chain pass refuses a missing timestamp buffer, a bad mode and oversized rows before
+    any device work, and its size helper returns 0 for invalid arguments."""
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fake = 1 << 20
+    tr = lib.qs_chain_forward_trace
+    tr.argtypes = [i, p, i, p, i, p, p, sz, p, sz, p]
+    tr.restype = i
+    assert tr(0, fake, 4, fake, 1, fake, fake, 1 << 30, None, 1 << 30, None) == -1   # no timestamp buffer
+    assert tr(3, fake, 4, fake, 1, fake, fake, 1 << 30, fake, 1 << 30, None) == -1   # bad mode
+    assert tr(0, fake, 4, None, 1, fake, fake, 1 << 30, fake, 1 << 30, None) == -1   # no chain
+    tb = lib.qs_chain_trace_bytes
+    tb.argtypes = [i, i, p, i]
+    tb.restype = sz
+    assert tb(0, 4, None, 1) == 0 and tb(3, 4, None, 1) == 0
+
+
 def test_noalloc_greedy_refuses_before_any_device_work(lib):
     """The greedy verify without a workspace: argument errors and sizes beyond its fixed scratch are
     refused on the host (fake pointers are never dereferenced)."""

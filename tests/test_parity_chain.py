@@ -481,3 +481,32 @@ def test_speculative_iteration(qs, draft_mode, B):
     print(f"  greedy: accepted {host(gr['n_accept']).tolist()} (oracle end to end {oe['n_accept'].tolist()}), "
           f"sampling accepted {host(sm['n_accept']).tolist()}", flush=True)
     assert np.array_equal(host(gr["out_tokens"])[clear], oe["out_tokens"][clear])
+
+
+# ---------------------------------------------------------------- boundary timestamps
+
+@pytest.mark.parametrize("mode,m", [(0, 4), (0, 8), (1, 1), (2, 4)])
+def test_chain_forward_trace(qs, mode, m):
+    """qs_chain_forward_trace returns what qs_chain_forward returns, bit for bit, and fills every
+    (entry, workgroup) slot with four timestamps in order: input staged <= stage done <= outputs
+    stored <= hand-over done <= the next entry's input staged."""
+    print(f"trace mode={mode} m={m}", flush=True)
+    rng = W.rng_for(1210 + 10 * mode + m)
+    shapes = [(8192, 512), (512, 8192), (4096, 512), (3000, 4096)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 512)
+    chain = _pack_chain(qs, layers)
+    assert chain.pass_launches(mode, m) >= 1
+    nbytes = chain.trace_bytes(mode, m)
+    assert nbytes > 0 and nbytes % 32 == 0
+    xd = dev(x)
+    ref = host(qs.qs_chain_forward(mode, xd, chain))
+    trace = torch.zeros(nbytes // 8, dtype=torch.int64, device="cuda")
+    got = host(qs.qs_chain_forward_trace(mode, xd, chain, trace))
+    assert np.array_equal(got, ref)
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    t = host(trace).reshape(-1, grid, 4)
+    assert t.shape[0] * grid * 32 == nbytes
+    assert (t > 0).all(), "a workgroup left an entry without timestamps"
+    assert (np.diff(t, axis=2) >= 0).all(), "timestamps of one entry out of order"
+    assert (t[1:, :, 0] >= t[:-1, :, 3]).all(), "an entry's input staged before the previous hand-over"
