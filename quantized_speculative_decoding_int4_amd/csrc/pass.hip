@@ -376,7 +376,9 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
 // WIDE (integer modes, more than one row): rows of up to kPiecesMax4 pieces per control thread,
 // staged in two rounds above 8; a separate instance, since the second round's code costs the one-row
 // kernel registers it does not have to spare.
-template <int MODE, bool WIDE>
+// TRACE: record the boundary timestamps of PassArgs::trace (a separate instance, so the passes that do
+// not record them carry no check).
+template <int MODE, bool WIDE, bool TRACE>
 __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   // Partials of the streaming waves: fp32 (W4A16) or fp64 (the integer modes: exact sums).
   using Acc = std::conditional_t<MODE == 0, float4_t, double4_t>;
@@ -787,10 +789,12 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
   };
 
-  // one timestamp of the running entry, from the first control thread (trace runs only)
+  // one timestamp of the running entry, from the first control thread (trace instances only)
   auto trace_mark = [&](int s, int k) __attribute__((always_inline)) {
-    if (a.trace != nullptr && ct == 0)
-      a.trace[((size_t)(a.trace_e0 + s) * (size_t)grid + (size_t)bid) * 4 + k] = (unsigned long long)wall_clock64();
+    if constexpr (TRACE) {
+      if (ct == 0)
+        a.trace[((size_t)(a.trace_e0 + s) * (size_t)grid + (size_t)bid) * 4 + k] = (unsigned long long)wall_clock64();
+    }
   };
 
   constexpr int kCarry = MODE == 0 ? kCtrlSlots : 1;
@@ -1029,13 +1033,19 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
   const DeviceInfo* di = device_info();
   const int grid = di->num_cus;
   const bool wide = mode != QS_W4A16 && M > 1;
-  const int variant = mode + (wide ? 2 : 0);  // 0 W4A16, 1 W4A4, 2 W4A8, 3 W4A4 wide, 4 W4A8 wide
-  const void* fns[5] = {reinterpret_cast<const void*>(pass_kernel<0, false>),
-                        reinterpret_cast<const void*>(pass_kernel<1, false>),
-                        reinterpret_cast<const void*>(pass_kernel<2, false>),
-                        reinterpret_cast<const void*>(pass_kernel<1, true>),
-                        reinterpret_cast<const void*>(pass_kernel<2, true>)};
-  static int lds_set[5] = {0, 0, 0, 0, 0};
+  // 0 W4A16, 1 W4A4, 2 W4A8, 3 W4A4 wide, 4 W4A8 wide; + 5: the same recording boundary timestamps
+  const int variant = mode + (wide ? 2 : 0) + (trace ? 5 : 0);
+  const void* fns[10] = {reinterpret_cast<const void*>(pass_kernel<0, false, false>),
+                         reinterpret_cast<const void*>(pass_kernel<1, false, false>),
+                         reinterpret_cast<const void*>(pass_kernel<2, false, false>),
+                         reinterpret_cast<const void*>(pass_kernel<1, true, false>),
+                         reinterpret_cast<const void*>(pass_kernel<2, true, false>),
+                         reinterpret_cast<const void*>(pass_kernel<0, false, true>),
+                         reinterpret_cast<const void*>(pass_kernel<1, false, true>),
+                         reinterpret_cast<const void*>(pass_kernel<2, false, true>),
+                         reinterpret_cast<const void*>(pass_kernel<1, true, true>),
+                         reinterpret_cast<const void*>(pass_kernel<2, true, true>)};
+  static int lds_set[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (!lds_set[variant]) {
     const int limit = (int)(mode == QS_W4A16 ? kPassLdsStage : kPassLdsStageInt);
     if (hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, limit) != hipSuccess) {
@@ -1128,11 +1138,16 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     a.n_stages = e;
     entry0 += e;
     switch (variant) {
-      case 0: hipLaunchKernelGGL((pass_kernel<0, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
-      case 1: hipLaunchKernelGGL((pass_kernel<1, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
-      case 2: hipLaunchKernelGGL((pass_kernel<2, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
-      case 3: hipLaunchKernelGGL((pass_kernel<1, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
-      default: hipLaunchKernelGGL((pass_kernel<2, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 0: hipLaunchKernelGGL((pass_kernel<0, false, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 1: hipLaunchKernelGGL((pass_kernel<1, false, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 2: hipLaunchKernelGGL((pass_kernel<2, false, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 3: hipLaunchKernelGGL((pass_kernel<1, true, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 4: hipLaunchKernelGGL((pass_kernel<2, true, false>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 5: hipLaunchKernelGGL((pass_kernel<0, false, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 6: hipLaunchKernelGGL((pass_kernel<1, false, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 7: hipLaunchKernelGGL((pass_kernel<2, false, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      case 8: hipLaunchKernelGGL((pass_kernel<1, true, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
+      default: hipLaunchKernelGGL((pass_kernel<2, true, true>), dim3(grid), dim3(kPThreads), lds, st, a); break;
     }
     rc = launch_status();
     if (rc != QS_OK) return rc;
