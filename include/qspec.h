@@ -251,15 +251,17 @@ int qs_chain_forward_top1(int mode, const uint16_t* x, int M, const qs_linear_de
  * grid-wide hand-over between them), or 0 if the chain runs one linear per
  * launch (row counts or shapes the persistent kernel does not take).  The
  * persistent launches of a pass are preceded by one launch that clears the
- * control words and (W4A4) fills the stage outputs with the not-yet-written
- * pattern.  Negative status codes as qs_chain_forward for bad arguments.
+ * control words and (W4A4, W4A8) fills the stage outputs with the
+ * not-yet-written pattern (and, W4A4 above one row, the shared activation
+ * codes).  Negative status codes as qs_chain_forward for bad arguments.
  */
 int qs_chain_pass_launches(int mode, int M, const qs_linear_desc* chain, int n);
 
 /*
  * Wall-clock limit, in microseconds, of every wait inside a persistent pass
- * (W4A16: a grid-barrier wait; W4A4 and W4A8: the wait for one stage's input
- * to be written) (process-wide; default 200000).  A wait that passes it sets
+ * (W4A16: a grid-barrier wait; W4A4 and W4A8: the wait for one stage's input,
+ * or for its shared activation codes, to be written) (process-wide; default
+ * 200000).  A wait that passes it sets
  * the workspace's time-out word and the workgroup exits, so a pass can never
  * wait forever.  The output is then partly or wholly NaN: every value is
  * either the correct one or NaN (the pass fills its output with NaN before it

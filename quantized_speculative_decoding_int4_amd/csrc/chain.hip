@@ -42,7 +42,7 @@ static size_t scratch_bytes(int mode, int M, const qs_linear_desc* c, int n) {
 }
 
 size_t chain_workspace(int mode, int M, const qs_linear_desc* c, int n) {
-  const size_t stages = M <= pass_max_rows(mode) ? pass_stage_bytes(M, c, n) : 0;
+  const size_t stages = M <= pass_max_rows(mode) ? pass_area_bytes(mode, M, c, n) : 0;
   return 2 * act_bytes(M, c, n) + scratch_bytes(mode, M, c, n) + stages;
 }
 

@@ -109,6 +109,7 @@ constexpr int kPassSlots = 4;              // row-block sets a workgroup may own
 constexpr int kCtrlSlots = (kPassSlots * kPW + kCW - 1) / kCW;  // (set, row block) pairs per control wave
 constexpr int kPiecesMax4 = 16;            // W4A4: 16-byte input pieces of a control thread per stage (two rounds above 8)
 constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
+constexpr uint32_t kCodeEmpty = 0x80808080u;  // W4A4 shared codes not yet written: -128 is no INT4 code
 constexpr int kSc1 = 16;                   // cache-policy bit SC1: device-coherent access
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw 32-bit buffer resource, no swizzle
 
@@ -154,6 +155,12 @@ struct PassArgs {
   // four per entry -- input staged, partials parked (stage done), outputs stored, hand-over done.
   unsigned long long* trace;
   int trace_e0;
+  // W4A4 shared codes, [M][K] bytes in MFMA operand order, kCodeEmpty before the pass: those of the
+  // fp16 stage output at byte offset o of the stage-output area (stage_base) are at codes_base +
+  // o / 2; those of the launch's input at codes_in.
+  const unsigned char* stage_base;
+  int8_t* codes_base;
+  int8_t* codes_in;  // codes of the launch's input
   int M;
   int n_stages;
   PassStage st[kMaxPassStages];
@@ -232,6 +239,15 @@ __device__ __forceinline__ bool has_empty(const uint4 v) {
   return (zero_half(~v.x) | zero_half(~v.y) | zero_half(~v.z) | zero_half(~v.w)) != 0u;
 }
 
+// True if any byte of v is 0x80 (kCodeEmpty's byte): v ^ 0x80.. then has a zero byte.
+__device__ __forceinline__ bool has_code_empty(const uint4 v) {
+  auto zero_byte = [](uint32_t w) {
+    w ^= kCodeEmpty;
+    return (w - 0x01010101u) & ~w & 0x80808080u;
+  };
+  return (zero_byte(v.x) | zero_byte(v.y) | zero_byte(v.z) | zero_byte(v.w)) != 0u;
+}
+
 // Buffer resource over extent bytes at base (base the same in all lanes); reads past the extent
 // return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sc1_rsrc(const void* base, uint32_t extent) {
@@ -265,6 +281,14 @@ constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
 // Largest activation code of the integer modes: 7 (W4A4, INT4 codes), 127 (W4A8, INT8 codes).
 template <int MODE>
 constexpr int kPassQmax = MODE == 2 ? 127 : 7;
+// The W4A4 pass of 2-4 rows stages every input through the shared codes (stage_in4s).  Measured on
+// the Llama-3-8B-shaped stack: the 4-row draft pass 1.94 ms against 2.41 ms with every workgroup
+// quantising all rows.  The one-row pass keeps stage_in4: shared codes took it from 1.38 to 1.64 ms
+// (1.45 ms when used only into the 14336-wide down projection), the extra exchange costing more
+// than the quantisation of one row it saves.  W4A8 codes use all 256 byte values, so no byte can
+// mark a code not yet written.
+template <int MODE, bool WIDE>
+constexpr bool kPassShared = MODE == 1 && WIDE;
 
 // W4A16 grid barrier between stages, free of contended atomics: workgroup b stores the epoch into
 // its own flag (one 128-byte line each) once its outputs are acknowledged, and the control threads
@@ -373,9 +397,10 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
   }
 }
 
-// WIDE (integer modes, more than one row): rows of up to kPiecesMax4 pieces per control thread,
-// staged in two rounds above 8; a separate instance, since the second round's code costs the one-row
-// kernel registers it does not have to spare.
+// WIDE (integer modes, more than one row): W4A4 stages its inputs through the shared codes
+// (stage_in4s); W4A8 takes rows of up to kPiecesMax4 pieces per control thread, staged in two rounds
+// above 8.  A separate instance, since that code costs the one-row kernel registers it does not have
+// to spare.
 // TRACE: record the boundary timestamps of PassArgs::trace (a separate instance, so the passes that do
 // not record them carry no check).
 template <int MODE, bool WIDE, bool TRACE>
@@ -590,6 +615,44 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
   };
 
+  // Integer modes: the row statistics of the staged input (this thread's sums, max, min) combined over
+  // the row's waves, then the row parameters (mean, 1/std, code scale) in LDS, behind barriers E
+  // and F; computed where `want`.
+  auto finish_params = [&](double su, double sq, float mx, float mn, int K, int norm, bool want)
+      __attribute__((always_inline)) {
+    su = wave_sum_dpp64(su);
+    sq = wave_sum_dpp64(sq);
+    mx = wave_max_dpp(mx);
+    mn = wave_min_dpp(mn);
+    if (lane == 0) {
+      stat_sum[0][cw] = su;
+      stat_sum[1][cw] = sq;
+      stat_mm[0][cw] = mx;
+      stat_mm[1][cw] = mn;
+    }
+    lds_barrier();  // E
+    // Row parameters, one wave per row: lane u reads the statistics of the row's u-th wave.
+    if (want && cw < M) {
+      const int m = cw;
+      const bool mine = lane < units_per_row;
+      const int u = m * units_per_row + (mine ? lane : 0);
+      const double tsu = lanes8_sum_dpp64(mine ? stat_sum[0][u] : 0.0);
+      const double tsq = lanes8_sum_dpp64(mine ? stat_sum[1][u] : 0.0);
+      const float xmax = lanes8_reduce_dpp(mine ? stat_mm[0][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
+      const float xmin = lanes8_reduce_dpp(mine ? stat_mm[1][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
+      if (lane == 0) {
+        double mu = 0.0, inv = 0.0;
+        if (norm) norm_params64(tsu, tsq, xmax, xmin, K, mu, inv);
+        row_mu64[m] = mu;
+        row_inv64[m] = inv;
+        const float amax = norm ? fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)))
+                                : fmaxf(xmax, -xmin);
+        row_c[m] = h2f(f2h(amax / (float)kPassQmax<MODE>));
+      }
+    }
+    lds_barrier();  // F
+  };
+
   // W4A16 (input complete: after the grid barrier, or from the previous launch): raw fp16 rows of
   // this entry's K chunk straight into LDS, [M][K] row-major, by direct DMA, 64 pieces (1 KiB) per
   // wave instruction.  The row statistics for the epilogue are taken after barrier G, while the
@@ -713,37 +776,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
           if (j < nh) stats_block8_64(v[j], su, sq, mx, mn);
       }
     }
-    su = wave_sum_dpp64(su);
-    sq = wave_sum_dpp64(sq);
-    mx = wave_max_dpp(mx);
-    mn = wave_min_dpp(mn);
-    if (lane == 0) {
-      stat_sum[0][cw] = su;
-      stat_sum[1][cw] = sq;
-      stat_mm[0][cw] = mx;
-      stat_mm[1][cw] = mn;
-    }
-    lds_barrier();  // E
-    // Row parameters, one wave per row: lane u reads the statistics of the row's u-th wave.
-    if (has && cw < M) {
-      const int m = cw;
-      const bool mine = lane < units_per_row;
-      const int u = m * units_per_row + (mine ? lane : 0);
-      const double tsu = lanes8_sum_dpp64(mine ? stat_sum[0][u] : 0.0);
-      const double tsq = lanes8_sum_dpp64(mine ? stat_sum[1][u] : 0.0);
-      const float xmax = lanes8_reduce_dpp(mine ? stat_mm[0][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
-      const float xmin = lanes8_reduce_dpp(mine ? stat_mm[1][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
-      if (lane == 0) {
-        double mu = 0.0, inv = 0.0;
-        if (norm) norm_params64(tsu, tsq, xmax, xmin, K, mu, inv);
-        row_mu64[m] = mu;
-        row_inv64[m] = inv;
-        const float amax = norm ? fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)))
-                                : fmaxf(xmax, -xmin);
-        row_c[m] = h2f(f2h(amax / (float)kPassQmax<MODE>));
-      }
-    }
-    lds_barrier();  // F
+    finish_params(su, sq, mx, mn, K, norm, has);
     if (active) {
       int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K + 8 * row_tid;
       const double mu = row_mu64[my_row], inv = row_inv64[my_row];
@@ -770,12 +803,127 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     lds_barrier();  // G
   };
 
+  // W4A4 with shared codes: the row statistics as in stage_in4 (rounds of P pieces per thread, each
+  // polled until complete and added up, none kept), then each workgroup standardises and quantises
+  // only its share of the rows -- pieces [bid * per, (bid + 1) * per) of the M * K / 8 pieces, at
+  // most one per control thread -- and stores the codes to the stage's code buffer with
+  // device-coherent stores.  It then reads the whole code buffer (16-byte pieces, polled until no
+  // byte holds kCodeEmpty's) into LDS.  Every workgroup takes part, with or without sets in the
+  // stage, so that all shares get written; only those with sets read the codes.  This replaces the
+  // per-workgroup quantisation of all M * K values (whose time grows with the rows and with K) by
+  // one more all-to-all exchange, 1 byte per value.
+  auto stage_in4s = [&](auto pc, int s, bool has) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    const PassStage ps = stage_at(s);
+    const int K = ps.K;
+    const uint16_t* x;
+    int ldx, norm;
+    input_of(ps, s, &x, &ldx, &norm);
+    const int nb = K / 8;
+    const bool part = !fail_sh;
+    const bool active = part && my_row < M;
+    const int np = row_tid < nb ? (nb - row_tid + gsz - 1) / gsz : 0;
+    const int H = ((nb + gsz - 1) / gsz + P - 1) / P;  // rounds (uniform)
+    const __amdgpu_buffer_rsrc_t rs = sc1_rsrc(x, (uint32_t)(((M - 1) * ldx + K) * 2));
+    const uint32_t voff = (uint32_t)(((my_row < M ? my_row : 0) * ldx + 8 * row_tid) * 2);
+    const uint32_t pstride = (uint32_t)gsz * 16u;
+    const int per = (M * nb + grid - 1) / grid;  // <= gsz (host check): one piece per thread at most
+    const int q0 = bid * per - my_row * nb;      // this row's share: pieces [q0, q0 + per) of the row
+    uint4 mine = make_uint4(0u, 0u, 0u, 0u);
+    int mine_idx = -1;
+    double su = 0.0, sq = 0.0;
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll 1
+    for (int h = 0; h < H; ++h) {
+      const int nh = np - h * P;
+      if (active) {
+        uint4 v[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)(h * P + j) * pstride);
+        if (s > 0) {
+          auto pending = [&]() {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < P; ++j)
+              if (j < nh && has_empty(v[j])) m |= 1u << j;
+            return m;
+          };
+          const long long t0 = wall_clock64();
+          while (a.deadline <= 0 || __any(pending() != 0u)) {
+            if (wait_failed(t0)) break;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < P; ++j) v[j] = load_sc1(rs, voff, (uint32_t)(h * P + j) * pstride);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (j < nh) {
+            stats_block8_64(v[j], su, sq, mx, mn);
+            const int idx = row_tid + (h * P + j) * gsz;
+            if (idx >= q0 && idx < q0 + per) {
+              mine = v[j];
+              mine_idx = idx;
+            }
+          }
+        }
+      }
+    }
+    finish_params(su, sq, mx, mn, K, norm, part);
+    int8_t* const codes = chunk_back(ps) == 0 ? a.codes_in
+                                              : a.codes_base + (reinterpret_cast<const unsigned char*>(x) - a.stage_base) / 2;
+    if (active && mine_idx >= 0) {
+      uint4 w = mine;
+      if (norm) w = norm_block8_64(w, row_mu64[my_row], row_inv64[my_row]);
+      uint2 op, lg;
+      quant_block8<kPassQmax<MODE>>(w, row_c[my_row], op, lg);
+      const __amdgpu_buffer_rsrc_t rw = sc1_rsrc(codes, (uint32_t)(M * K));
+      typedef int v2i_t __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(v2i_t{(int)op.x, (int)op.y}, rw, my_row * K + 8 * mine_idx, 0, kSc1);
+    }
+    if (has && !fail_sh) {
+      constexpr int Q = 4;  // 16-byte code pieces per thread and round (8 spilled registers)
+      const int nq = M * K / 16;
+      const __amdgpu_buffer_rsrc_t rc = sc1_rsrc(codes, (uint32_t)(M * K));
+#pragma unroll 1
+      for (int b0 = 0; b0 < nq; b0 += Q * kCT) {
+        uint4 c[Q];
+#pragma unroll
+        for (int u = 0; u < Q; ++u) c[u] = load_sc1(rc, (uint32_t)(b0 + u * kCT + ct) * 16u, 0u);  // zeros past the end
+        auto pending = [&]() {
+          uint32_t m = 0;
+#pragma unroll
+          for (int u = 0; u < Q; ++u)
+            if (has_code_empty(c[u])) m |= 1u << u;
+          return m;
+        };
+        const long long t0 = wall_clock64();
+        while (a.deadline <= 0 || __any(pending() != 0u)) {
+          if (wait_failed(t0)) break;
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int u = 0; u < Q; ++u) c[u] = load_sc1(rc, (uint32_t)(b0 + u * kCT + ct) * 16u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+          const int q = b0 + u * kCT + ct;
+          if (q < nq) reinterpret_cast<uint4*>(dyn_lds)[q] = c[u];
+        }
+      }
+    }
+    lds_barrier();  // G
+  };
+
   auto prologue = [&](int s) {
     const bool has = stage_sets(stage_at(s), bid, grid) > 0 && !fail_sh;
     if constexpr (MODE == 0) {
       stage_in16(s, has);
     } else {
       const int npmax = (stage_at(s).K / 8 + gsz - 1) / gsz;  // <= kPiecesMax4 (host check)
+      if constexpr (kPassShared<MODE, WIDE>) {
+        stage_in4s(std::integral_constant<int, 4>{}, s, has);  // rounds of 4 pieces (8 spilled registers)
+        return;
+      }
       static_assert(kPiecesMax4 == 16, "piece buckets below end at kPiecesMax4");
       using one = std::integral_constant<int, 1>;
       if (npmax <= 2)
@@ -901,10 +1049,12 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
   }
 }
 
-// Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores), the
+// Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores) and the
+// n16c 16-byte pieces after them (the W4A4 code buffer) with kCodeEmpty, the
 // final output with NaN and the Top-1 outputs with -1 and NaN, and zeroes the control words (the
 // Top-1 arrival counter and the error word, then n_flags arrival flags kFlagStride apart).
-__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, unsigned* ctrl, int n_flags,
+__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, uint32_t n16c, unsigned* ctrl,
+                                                         int n_flags,
                                                          float* out, uint32_t n_out, int32_t* top1, float* top1_prob,
                                                          int n_top1) {
   if (blockIdx.x == 0 && top1) {
@@ -918,10 +1068,13 @@ __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n
     for (int i = threadIdx.x; i < n_flags; i += 256)
       __hip_atomic_store(ctrl + (size_t)(i + 1) * kFlagStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bufs, (short)0, (int)(n16 * 16u), (int)kBufWord3);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(bufs, (short)0, (int)((n16 + n16c) * 16u), (int)kBufWord3);
   const int4_t e = int4_t{-1, -1, -1, -1};
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += gridDim.x * 256u)
-    __builtin_amdgcn_raw_buffer_store_b128(e, r, (int)(i * 16u), 0, kSc1);
+  const int ce = (int)kCodeEmpty;
+  const int4_t ec = int4_t{ce, ce, ce, ce};
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16 + n16c; i += gridDim.x * 256u)
+    __builtin_amdgcn_raw_buffer_store_b128(i < n16 ? e : ec, r, (int)(i * 16u), 0, kSc1);
   if (out) {
     for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n_out; i += gridDim.x * 256u)
       out[i] = __builtin_nanf("");
@@ -944,6 +1097,14 @@ static int pass_chunks(int mode, int M, int K) {
 // Groups in each chunk of a linear split into nch chunks (the last may be shorter).
 static int chunk_groups(int K, int nch) { return (K / kGroup + nch - 1) / nch; }
 
+// Workgroup share of the shared-code staging fits: at most one 16-byte piece per control thread.
+static bool pass_share_fits(int M, int K, int grid) {
+  const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);
+  return (M * (K / 8) + grid - 1) / grid <= gsz;
+}
+// The pass stages its inputs through the shared codes (kPassShared): W4A4 above one row.
+static bool pass_shared_codes(int mode, int M) { return mode == QS_W4A4 && M > 1; }
+
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   if (M > pass_max_rows(mode)) return false;
   const int grid = device_info()->num_cus;
@@ -953,6 +1114,7 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
     const int nch = pass_chunks(mode, M, c[i].K);
     if (nch < 1 || nch > kMaxPassStages) return false;
     if (mode != QS_W4A16 && c[i].K / 8 > (M > 1 ? kPiecesMax4 : 8) * gsz) return false;
+    if (pass_shared_codes(mode, M) && !pass_share_fits(M, c[i].K, grid)) return false;
     if (pick_pass_split(c[i].N, chunk_groups(c[i].K, nch) * kGroup, grid) < 0) return false;
   }
   return true;
@@ -963,9 +1125,10 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
 // 1.41, 1.40, 1.43, 1.90 ms per pass against 2.1-2.3 ms with one launch per linear; at 15 rows every
 // 4096-wide linear needs two K chunks and the pass took 2.25 ms against 2.12 ms.
 //
-// The integer modes take up to 4 rows (every workgroup standardises and quantises all rows itself,
-// so the staging grows with M): W4A4 pass 1.42 / 1.81 / 2.34 / 2.41 ms at 1 / 2 / 3 / 4 rows against
-// 2.97 ms with one launch per linear at 4 rows.
+// The integer modes take up to 4 rows (the row statistics are taken in every workgroup, so the
+// staging grows with M): W4A4 pass 1.38 / 1.79 / 1.92 / 1.94 ms at 1 / 2 / 3 / 4 rows (shared codes
+// above one row; 2.34 / 2.41 ms at 3 / 4 rows with every workgroup quantising all rows, as W4A8
+// does: 2.41 ms at 4 rows) against 2.97 ms with one launch per linear at 4 rows.
 int pass_max_rows(int mode) { return mode == QS_W4A16 ? 14 : (mode == QS_W4A4 || mode == QS_W4A8) ? 4 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
@@ -973,6 +1136,13 @@ size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   for (int i = 0; i + 1 < n; ++i) b += align_up((size_t)M * c[i].N * 2, 256);
   return b;
 }
+// Stage outputs and, for W4A4 above one row, the code buffer after them: one byte per fp16 output, at half its
+// offset (so each stage's codes start 128-byte aligned), then the codes of the pass's input.
+size_t pass_area_bytes(int mode, int M, const qs_linear_desc* c, int n) {
+  const size_t sb = pass_stage_bytes(M, c, n);
+  return pass_shared_codes(mode, M) ? sb + sb / 2 + align_up((size_t)M * c[0].K, 256) : sb;
+}
+
 
 // K-split S per stage: fewest tiles per wave, subject to at most kPassSlots sets per workgroup;
 // ties go to the smaller S (fewer, longer sets).  Returns -1 if no S fits.
@@ -1061,16 +1231,17 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     lds = b > lds ? b : lds;
   }
 
-  // Stage outputs of the whole pass -> kEmpty, error word -> 0.
+  // Stage outputs of the whole pass -> kEmpty, W4A4 codes -> kCodeEmpty, error word -> 0.
   const size_t sb = pass_stage_bytes(M, c, n);
-  if (sb > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
+  if (pass_area_bytes(mode, M, c, n) > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
   const uint32_t n16 = mode != QS_W4A16 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
+  const uint32_t n16c = (uint32_t)((pass_area_bytes(mode, M, c, n) - sb) / 16);  // W4A4 codes
   const size_t n_out = out ? (size_t)M * c[n - 1].N : 0;
   if (n_out > 0xFFFFFFFFu) return QS_ERR_UNSUPPORTED;
-  const size_t work = (size_t)n16 + n_out / 4;
+  const size_t work = (size_t)n16 + n16c + n_out / 4;
   const unsigned rblocks = (unsigned)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
   hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st,
-                     reinterpret_cast<uint4*>(stage_out), n16, ctrl, mode == QS_W4A16 ? grid : 0, out,
+                     reinterpret_cast<uint4*>(stage_out), n16, n16c, ctrl, mode == QS_W4A16 ? grid : 0, out,
                      (uint32_t)n_out, t1 ? t1->top1 : nullptr, t1 ? t1->top1_prob : nullptr, M);
   int rc = launch_status();
   if (rc != QS_OK) return rc;
@@ -1106,6 +1277,11 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     a.epoch0 = (unsigned)entry0;
     a.trace = trace;
     a.trace_e0 = entry0;
+    a.stage_base = base;
+    a.codes_base = reinterpret_cast<int8_t*>(base + sb);
+    // the launch's input: the pass input's own code area, or the codes of the previous launch's output
+    a.codes_in = i0 == 0 ? reinterpret_cast<int8_t*>(base + sb + sb / 2)
+                         : reinterpret_cast<int8_t*>(base + sb + (reinterpret_cast<unsigned char*>(prev) - base) / 2);
     a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
     int e = 0;

@@ -85,6 +85,8 @@ int pass_max_rows(int mode);   // most rows a persistent pass takes in this mode
 int pass_launch_count(int mode, int M, const qs_linear_desc* c, int n);  // launches of a persistent pass
 // fp16 outputs of all stages but the last, each 256-byte aligned, in chain order
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n);
+// the stage outputs, then (W4A4) one code byte per output at half the output's offset
+size_t pass_area_bytes(int mode, int M, const qs_linear_desc* c, int n);
 int pass_barrier_timeout_us();  // wall-clock limit of one wait for a stage's input (process-wide)
 void set_pass_barrier_timeout_us(int us);
 // Top-1 of the final stage (the LM-head): top1 [M], top1_prob [M] (nullable), and stats, the

@@ -100,11 +100,13 @@ def test_chain_with_vocabulary_wide_head(qs, mode, m):
         assert_exact(y, ref, f"chain wide head mode={mode} m={m}")
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 8), (0, 12), (1, 12), (0, 16), (1, 16)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (2, 1), (0, 2), (1, 2), (1, 4), (1, 8), (0, 12), (1, 12), (0, 16),
+                                    (1, 16)])
 def test_chain_longer_than_one_persistent_launch(qs, mode, m):
-    """75 linears.  At M <= 4 (W4A16) / M = 1 (integer modes) the persistent pass splits them over
-    two launches (at most 72 per launch), so the hand-over at the seam is covered; so do W4A16 up
-    to 14 rows and the integer modes up to 4; the other row counts run linear by linear."""
+    """75 linears.  The persistent pass (W4A16 up to 14 rows, the integer modes up to 4) splits them
+    over two launches (at most 72 per launch), so the hand-over at the seam is covered -- for W4A4
+    above one row that includes the shared codes of the second launch's input, the first launch's
+    last output; the other row counts run linear by linear."""
     print(f"long chain mode={mode} m={m}", flush=True)
     rng = W.rng_for(900 + 10 * m + mode)
     shapes = [(384, 256), (256, 384)] * 37 + [(1000, 256)]
@@ -190,7 +192,7 @@ def test_chain_top1_fused(qs, mode, m):
         assert np.array_equal(t1, t_or)
 
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (1, 1), (1, 3)])
 def test_chain_top1_after_a_timeout(qs, mode, m):
     """A persistent pass whose waits time out leaves Top-1 -1 and probability NaN (the last
     workgroup's merge never runs), and the next call on the same workspace is correct."""
@@ -219,8 +221,10 @@ def test_chain_top1_after_a_timeout(qs, mode, m):
 @pytest.mark.parametrize("m", [2, 3, 4])
 def test_chain_int_rows_2_to_4(qs, mode, m):
     """The integer-mode persistent pass at 2-4 rows (its own kernel instance), on a chain with a
-    14336-wide input: at 3 and 4 rows a control thread's share of such a row exceeds 8 pieces and is
-    staged in two rounds.  Bit-exact against the oracle, like every integer chain; and its fused
+    14336-wide input.  W4A4 stages every input through the shared codes (statistics read in rounds
+    of 4 pieces per thread, each workgroup quantising its share); W4A8 quantises all rows in every
+    workgroup, and at 3 and 4 rows a control thread's share of a 14336-wide row exceeds 8 pieces and
+    is staged in two rounds.  Bit-exact against the oracle, like every integer chain; and its fused
     Top-1."""
     print(f"int rows mode={mode} m={m}", flush=True)
     rng = W.rng_for(1010 + 10 * m + mode)
@@ -485,7 +489,7 @@ def test_speculative_iteration(qs, draft_mode, B):
 
 # ---------------------------------------------------------------- boundary timestamps
 
-@pytest.mark.parametrize("mode,m", [(0, 4), (0, 8), (1, 1), (2, 4)])
+@pytest.mark.parametrize("mode,m", [(0, 4), (0, 8), (1, 1), (1, 4), (2, 4)])
 def test_chain_forward_trace(qs, mode, m):
     """qs_chain_forward_trace returns what qs_chain_forward returns, bit for bit, and fills every
     (entry, workgroup) slot with four timestamps in order: input staged <= stage done <= outputs
