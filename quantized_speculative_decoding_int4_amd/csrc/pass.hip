@@ -107,9 +107,11 @@ constexpr size_t kPassLdsStageInt = 81920;
 constexpr size_t kPassLdsMin = 81920;
 constexpr int kPassSlots = 4;              // row-block sets a workgroup may own per stage
 constexpr int kCtrlSlots = (kPassSlots * kPW + kCW - 1) / kCW;  // (set, row block) pairs per control wave
-constexpr int kPiecesMax4 = 16;            // W4A4: 16-byte input pieces of a control thread per stage (two rounds above 8)
 constexpr uint16_t kEmpty = 0xFFFFu;       // pattern of a stage output not yet written
-constexpr uint32_t kCodeEmpty = 0x80808080u;  // W4A4 shared codes not yet written: -128 is no INT4 code
+// Shared activation codes not yet written: W4A4 stores a byte per code and -128 is no INT4 code; W4A8
+// codes take every byte value, so W4A8 stores 16 bits per code and -32768 marks the empty ones.
+constexpr uint32_t kCodeEmpty = 0x80808080u;
+constexpr uint32_t kCodeEmpty16 = 0x80008000u;
 constexpr int kSc1 = 16;                   // cache-policy bit SC1: device-coherent access
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw 32-bit buffer resource, no swizzle
 
@@ -155,15 +157,17 @@ struct PassArgs {
   // four per entry -- input staged, partials parked (stage done), outputs stored, hand-over done.
   unsigned long long* trace;
   int trace_e0;
-  // W4A4 shared codes, [M][K] bytes in MFMA operand order, kCodeEmpty before the pass: those of the
-  // fp16 stage output at byte offset o of the stage-output area (stage_base) are at codes_base +
-  // o / 2; those of the launch's input at codes_in.
-  const unsigned char* stage_base;
-  int8_t* codes_base;
-  int8_t* codes_in;  // codes of the launch's input
   int M;
   int n_stages;
   PassStage st[kMaxPassStages];
+  // Shared activation codes (integer modes above one row), [M][K] in MFMA operand order, empty before
+  // the pass (W4A4: bytes, kCodeEmpty; W4A8: 16-bit, kCodeEmpty16): those of the fp16 stage output at
+  // byte offset o of the stage-output area (stage_base) are at codes_base + o / 2 (W4A4) or + o
+  // (W4A8); those of the launch's input at codes_in.  After the stage table, which keeps its offset
+  // in the argument segment.
+  const unsigned char* stage_base;
+  int8_t* codes_base;
+  int8_t* codes_in;  // codes of the launch's input
 };
 static_assert(sizeof(PassArgs) <= 4096, "the stage table travels in the 4 KiB kernel-argument segment");
 
@@ -239,13 +243,20 @@ __device__ __forceinline__ bool has_empty(const uint4 v) {
   return (zero_half(~v.x) | zero_half(~v.y) | zero_half(~v.z) | zero_half(~v.w)) != 0u;
 }
 
-// True if any byte of v is 0x80 (kCodeEmpty's byte): v ^ 0x80.. then has a zero byte.
+// True if any byte (CB = 1) or 16-bit word (CB = 2) of v holds the empty code: v ^ kCodeEmpty(16)
+// then has a zero byte or word.
+template <int CB>
 __device__ __forceinline__ bool has_code_empty(const uint4 v) {
-  auto zero_byte = [](uint32_t w) {
-    w ^= kCodeEmpty;
-    return (w - 0x01010101u) & ~w & 0x80808080u;
+  auto zero_part = [](uint32_t w) {
+    if constexpr (CB == 1) {
+      w ^= kCodeEmpty;
+      return (w - 0x01010101u) & ~w & 0x80808080u;
+    } else {
+      w ^= kCodeEmpty16;
+      return (w - 0x00010001u) & ~w & 0x80008000u;
+    }
   };
-  return (zero_byte(v.x) | zero_byte(v.y) | zero_byte(v.z) | zero_byte(v.w)) != 0u;
+  return (zero_part(v.x) | zero_part(v.y) | zero_part(v.z) | zero_part(v.w)) != 0u;
 }
 
 // Buffer resource over extent bytes at base (base the same in all lanes); reads past the extent
@@ -281,14 +292,14 @@ constexpr int kStagingBarriers = MODE == 0 ? 1 : 3;
 // Largest activation code of the integer modes: 7 (W4A4, INT4 codes), 127 (W4A8, INT8 codes).
 template <int MODE>
 constexpr int kPassQmax = MODE == 2 ? 127 : 7;
-// The W4A4 pass of 2-4 rows stages every input through the shared codes (stage_in4s).  Measured on
-// the Llama-3-8B-shaped stack: the 4-row draft pass 1.94 ms against 2.41 ms with every workgroup
-// quantising all rows.  The one-row pass keeps stage_in4: shared codes took it from 1.38 to 1.64 ms
-// (1.45 ms when used only into the 14336-wide down projection), the extra exchange costing more
-// than the quantisation of one row it saves.  W4A8 codes use all 256 byte values, so no byte can
-// mark a code not yet written.
+// The integer-mode passes of 2-4 rows stage every input through the shared codes (stage_in4s).
+// Measured on the Llama-3-8B-shaped stack, 4-row draft pass: W4A4 1.94 ms, W4A8 2.02 ms (16-bit
+// codes), against 2.41 ms with every workgroup quantising all rows (3 rows: 1.92 / 1.97 against
+// 2.34; 2 rows: 1.79 either way).  The one-row pass keeps stage_in4: shared codes took the W4A4 one
+// from 1.38 to 1.64 ms (1.45 ms when used only into the 14336-wide down projection), the extra
+// exchange costing more than the quantisation of one row it saves.
 template <int MODE, bool WIDE>
-constexpr bool kPassShared = MODE == 1 && WIDE;
+constexpr bool kPassShared = MODE != 0 && WIDE;
 
 // W4A16 grid barrier between stages, free of contended atomics: workgroup b stores the epoch into
 // its own flag (one 128-byte line each) once its outputs are acknowledged, and the control threads
@@ -397,10 +408,9 @@ __device__ __forceinline__ void top1_epilogue(const Top1Out o, Msi (&t1v)[4], fl
   }
 }
 
-// WIDE (integer modes, more than one row): W4A4 stages its inputs through the shared codes
-// (stage_in4s); W4A8 takes rows of up to kPiecesMax4 pieces per control thread, staged in two rounds
-// above 8.  A separate instance, since that code costs the one-row kernel registers it does not have
-// to spare.
+// WIDE (integer modes, more than one row): the inputs are staged through the shared codes
+// (stage_in4s) instead of being quantised whole in every workgroup (stage_in4).  A separate instance:
+// both stagings in one kernel spill registers.
 // TRACE: record the boundary timestamps of PassArgs::trace (a separate instance, so the passes that do
 // not record them carry no check).
 template <int MODE, bool WIDE, bool TRACE>
@@ -583,8 +593,8 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     ones_pad[ct] = 0x3C003C00u;
   }
   // Input rows spread over groups of control threads: gsz threads per row (M <= 4, so gsz >= 128),
-  // thread row_tid of a group holds pieces row_tid, row_tid + gsz, ... (at most kPiecesMax4, host
-  // check) of its row.  Reduction units are whole waves.
+  // thread row_tid of a group holds pieces row_tid, row_tid + gsz, ... of its row.  Reduction units
+  // are whole waves.
   const int mp = M <= 1 ? 1 : M <= 2 ? 2 : 4;
   const int gsz = kCT / mp;
   const int my_row = ct / gsz;
@@ -717,18 +727,18 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     }
   };
 
-  // W4A4: rows staged through registers (statistics, scale, quantisation, then LDS).  From the
-  // launch's second stage on, the input is being written by other workgroups: pieces that still
-  // hold kEmpty are read again until all hold data or the deadline passes.  Each thread
-  // holds P pieces, P a compile-time bucket of the stage's pieces per thread chosen with a uniform
-  // branch.  The loads are unconditional: a load under a condition is merged with the old value by
-  // a select, and the compiler then keeps two copies of all pieces live.  Pieces past this thread's
-  // count are read (next row, or zeros past the buffer resource's extent) and not used.
-  // Rows wider than P pieces per thread (the 14336-wide down projection at 4 rows) are taken in H
-  // rounds of P pieces: each round is loaded (and, within a pass, polled until complete) and added to
-  // the statistics; after the row parameters every round but the last, whose pieces are still in
-  // registers, is loaded again (complete by then) to be quantised.  Holding 16 pieces per thread in
-  // registers instead spilled.
+  // The integer modes at one row: the row staged through registers (statistics, scale,
+  // quantisation, then LDS).  From the launch's second stage on, the input is being written by other
+  // workgroups: pieces that still hold kEmpty are read again until all hold data or the deadline
+  // passes.  Each thread holds P pieces, P a compile-time bucket of the stage's pieces per thread
+  // chosen with a uniform branch.  The loads are unconditional: a load under a condition is merged
+  // with the old value by a select, and the compiler then keeps two copies of all pieces live.
+  // Pieces past this thread's count are read (next row, or zeros past the buffer resource's extent)
+  // and not used.  Rows wider than P pieces per thread would be taken in H rounds of P pieces: each
+  // round loaded (polled) and added to the statistics, then, after the row parameters, every round
+  // but the last reloaded to be quantised.  The passes call it with H = 1 only (it staged the wider
+  // rows of 3-4 rows before the shared codes); the round loop stays because the kernel written
+  // without it compiled to another schedule that made the one-row draft pass 2% slower.
   auto stage_in4 = [&](auto pc, auto hc, int s, bool has) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     constexpr int H = decltype(hc)::value;
@@ -776,7 +786,37 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
           if (j < nh) stats_block8_64(v[j], su, sq, mx, mn);
       }
     }
-    finish_params(su, sq, mx, mn, K, norm, has);
+    su = wave_sum_dpp64(su);
+    sq = wave_sum_dpp64(sq);
+    mx = wave_max_dpp(mx);
+    mn = wave_min_dpp(mn);
+    if (lane == 0) {
+      stat_sum[0][cw] = su;
+      stat_sum[1][cw] = sq;
+      stat_mm[0][cw] = mx;
+      stat_mm[1][cw] = mn;
+    }
+    lds_barrier();  // E
+    // Row parameters, one wave per row: lane u reads the statistics of the row's u-th wave.
+    if (has && cw < M) {
+      const int m = cw;
+      const bool mine = lane < units_per_row;
+      const int u = m * units_per_row + (mine ? lane : 0);
+      const double tsu = lanes8_sum_dpp64(mine ? stat_sum[0][u] : 0.0);
+      const double tsq = lanes8_sum_dpp64(mine ? stat_sum[1][u] : 0.0);
+      const float xmax = lanes8_reduce_dpp(mine ? stat_mm[0][u] : -INFINITY, [](float p, float q) { return fmaxf(p, q); });
+      const float xmin = lanes8_reduce_dpp(mine ? stat_mm[1][u] : INFINITY, [](float p, float q) { return fminf(p, q); });
+      if (lane == 0) {
+        double mu = 0.0, inv = 0.0;
+        if (norm) norm_params64(tsu, tsq, xmax, xmin, K, mu, inv);
+        row_mu64[m] = mu;
+        row_inv64[m] = inv;
+        const float amax = norm ? fmaxf(h2f(norm_h64(xmax, mu, inv)), -h2f(norm_h64(xmin, mu, inv)))
+                                : fmaxf(xmax, -xmin);
+        row_c[m] = h2f(f2h(amax / (float)kPassQmax<MODE>));
+      }
+    }
+    lds_barrier();  // F
     if (active) {
       int8_t* xq = reinterpret_cast<int8_t*>(dyn_lds) + (size_t)my_row * K + 8 * row_tid;
       const double mu = row_mu64[my_row], inv = row_inv64[my_row];
@@ -870,21 +910,31 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
       }
     }
     finish_params(su, sq, mx, mn, K, norm, part);
-    int8_t* const codes = chunk_back(ps) == 0 ? a.codes_in
-                                              : a.codes_base + (reinterpret_cast<const unsigned char*>(x) - a.stage_base) / 2;
+    constexpr int CB = MODE == 1 ? 1 : 2;  // bytes per shared code
+    int8_t* const codes =
+        chunk_back(ps) == 0 ? a.codes_in
+                            : a.codes_base + (reinterpret_cast<const unsigned char*>(x) - a.stage_base) * CB / 2;
     if (active && mine_idx >= 0) {
       uint4 w = mine;
       if (norm) w = norm_block8_64(w, row_mu64[my_row], row_inv64[my_row]);
       uint2 op, lg;
       quant_block8<kPassQmax<MODE>>(w, row_c[my_row], op, lg);
-      const __amdgpu_buffer_rsrc_t rw = sc1_rsrc(codes, (uint32_t)(M * K));
-      typedef int v2i_t __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64(v2i_t{(int)op.x, (int)op.y}, rw, my_row * K + 8 * mine_idx, 0, kSc1);
+      const __amdgpu_buffer_rsrc_t rw = sc1_rsrc(codes, (uint32_t)(M * K * CB));
+      if constexpr (CB == 1) {
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(v2i_t{(int)op.x, (int)op.y}, rw, my_row * K + 8 * mine_idx, 0, kSc1);
+      } else {  // each code byte sign-extended to 16 bits, same order
+        auto widen = [](uint32_t b) {  // bytes 0, 1 of b -> 16-bit words 0, 1
+          return ((uint32_t)((int32_t)(b << 24) >> 24) & 0xFFFFu) | ((uint32_t)((int32_t)(b << 16) >> 24) << 16);
+        };
+        const int4_t v16 = int4_t{(int)widen(op.x), (int)widen(op.x >> 16), (int)widen(op.y), (int)widen(op.y >> 16)};
+        __builtin_amdgcn_raw_buffer_store_b128(v16, rw, (my_row * K + 8 * mine_idx) * 2, 0, kSc1);
+      }
     }
     if (has && !fail_sh) {
       constexpr int Q = 4;  // 16-byte code pieces per thread and round (8 spilled registers)
-      const int nq = M * K / 16;
-      const __amdgpu_buffer_rsrc_t rc = sc1_rsrc(codes, (uint32_t)(M * K));
+      const int nq = M * K * CB / 16;
+      const __amdgpu_buffer_rsrc_t rc = sc1_rsrc(codes, (uint32_t)(M * K * CB));
 #pragma unroll 1
       for (int b0 = 0; b0 < nq; b0 += Q * kCT) {
         uint4 c[Q];
@@ -894,7 +944,7 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
           uint32_t m = 0;
 #pragma unroll
           for (int u = 0; u < Q; ++u)
-            if (has_code_empty(c[u])) m |= 1u << u;
+            if (has_code_empty<CB>(c[u])) m |= 1u << u;
           return m;
         };
         const long long t0 = wall_clock64();
@@ -907,7 +957,16 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
 #pragma unroll
         for (int u = 0; u < Q; ++u) {
           const int q = b0 + u * kCT + ct;
-          if (q < nq) reinterpret_cast<uint4*>(dyn_lds)[q] = c[u];
+          if (q < nq) {
+            if constexpr (CB == 1) {
+              reinterpret_cast<uint4*>(dyn_lds)[q] = c[u];
+            } else {  // the low byte of each 16-bit code
+              auto narrow = [](uint32_t lo, uint32_t hi) {
+                return (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | ((hi & 0xFF0000u) << 8);
+              };
+              reinterpret_cast<uint2*>(dyn_lds)[q] = make_uint2(narrow(c[u].x, c[u].y), narrow(c[u].z, c[u].w));
+            }
+          }
         }
       }
     }
@@ -919,21 +978,18 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     if constexpr (MODE == 0) {
       stage_in16(s, has);
     } else {
-      const int npmax = (stage_at(s).K / 8 + gsz - 1) / gsz;  // <= kPiecesMax4 (host check)
       if constexpr (kPassShared<MODE, WIDE>) {
         stage_in4s(std::integral_constant<int, 4>{}, s, has);  // rounds of 4 pieces (8 spilled registers)
-        return;
+      } else {  // one row: at most 8 pieces per thread (host check)
+        const int npmax = (stage_at(s).K / 8 + gsz - 1) / gsz;
+        using one = std::integral_constant<int, 1>;
+        if (npmax <= 2)
+          stage_in4(std::integral_constant<int, 2>{}, one{}, s, has);
+        else if (npmax <= 4)
+          stage_in4(std::integral_constant<int, 4>{}, one{}, s, has);
+        else
+          stage_in4(std::integral_constant<int, 8>{}, one{}, s, has);
       }
-      static_assert(kPiecesMax4 == 16, "piece buckets below end at kPiecesMax4");
-      using one = std::integral_constant<int, 1>;
-      if (npmax <= 2)
-        stage_in4(std::integral_constant<int, 2>{}, one{}, s, has);
-      else if (npmax <= 4)
-        stage_in4(std::integral_constant<int, 4>{}, one{}, s, has);
-      else if (!WIDE || npmax <= 8)  // one row: at most 8 (host check)
-        stage_in4(std::integral_constant<int, 8>{}, one{}, s, has);
-      else if constexpr (WIDE)
-        stage_in4(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{}, s, has);
     }
   };
 
@@ -1050,11 +1106,11 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
 }
 
 // Start of a pass: fills the stage outputs with kEmpty (integer modes; device-coherent stores) and the
-// n16c 16-byte pieces after them (the W4A4 code buffer) with kCodeEmpty, the
+// n16c 16-byte pieces after them (the shared codes) with cfill, the
 // final output with NaN and the Top-1 outputs with -1 and NaN, and zeroes the control words (the
 // Top-1 arrival counter and the error word, then n_flags arrival flags kFlagStride apart).
-__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, uint32_t n16c, unsigned* ctrl,
-                                                         int n_flags,
+__global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n16, uint32_t n16c, uint32_t cfill,
+                                                         unsigned* ctrl, int n_flags,
                                                          float* out, uint32_t n_out, int32_t* top1, float* top1_prob,
                                                          int n_top1) {
   if (blockIdx.x == 0 && top1) {
@@ -1071,7 +1127,7 @@ __global__ __launch_bounds__(256) void pass_reset_kernel(uint4* bufs, uint32_t n
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(bufs, (short)0, (int)((n16 + n16c) * 16u), (int)kBufWord3);
   const int4_t e = int4_t{-1, -1, -1, -1};
-  const int ce = (int)kCodeEmpty;
+  const int ce = (int)cfill;
   const int4_t ec = int4_t{ce, ce, ce, ce};
   for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16 + n16c; i += gridDim.x * 256u)
     __builtin_amdgcn_raw_buffer_store_b128(i < n16 ? e : ec, r, (int)(i * 16u), 0, kSc1);
@@ -1102,8 +1158,9 @@ static bool pass_share_fits(int M, int K, int grid) {
   const int gsz = kCT / (M <= 1 ? 1 : M <= 2 ? 2 : 4);
   return (M * (K / 8) + grid - 1) / grid <= gsz;
 }
-// The pass stages its inputs through the shared codes (kPassShared): W4A4 above one row.
-static bool pass_shared_codes(int mode, int M) { return mode == QS_W4A4 && M > 1; }
+// The pass stages its inputs through the shared codes (kPassShared): the integer modes above one row.
+static bool pass_shared_codes(int mode, int M) { return (mode == QS_W4A4 || mode == QS_W4A8) && M > 1; }
+static size_t pass_code_bytes(int mode) { return mode == QS_W4A8 ? 2 : 1; }  // per shared code
 
 bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   if (M > pass_max_rows(mode)) return false;
@@ -1113,7 +1170,7 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
   for (int i = 0; i < n; ++i) {
     const int nch = pass_chunks(mode, M, c[i].K);
     if (nch < 1 || nch > kMaxPassStages) return false;
-    if (mode != QS_W4A16 && c[i].K / 8 > (M > 1 ? kPiecesMax4 : 8) * gsz) return false;
+    if (mode != QS_W4A16 && M <= 1 && c[i].K / 8 > 8 * gsz) return false;  // one-row staging: 8 pieces per thread
     if (pass_shared_codes(mode, M) && !pass_share_fits(M, c[i].K, grid)) return false;
     if (pick_pass_split(c[i].N, chunk_groups(c[i].K, nch) * kGroup, grid) < 0) return false;
   }
@@ -1127,8 +1184,8 @@ bool pass_eligible(int mode, int M, const qs_linear_desc* c, int n) {
 //
 // The integer modes take up to 4 rows (the row statistics are taken in every workgroup, so the
 // staging grows with M): W4A4 pass 1.38 / 1.79 / 1.92 / 1.94 ms at 1 / 2 / 3 / 4 rows (shared codes
-// above one row; 2.34 / 2.41 ms at 3 / 4 rows with every workgroup quantising all rows, as W4A8
-// does: 2.41 ms at 4 rows) against 2.97 ms with one launch per linear at 4 rows.
+// above one row; 2.34 / 2.41 ms at 3 / 4 rows with every workgroup quantising all rows), W4A8
+// 1.39 / 1.80 / 1.97 / 2.02 ms, against 2.97 ms with one launch per linear at 4 rows.
 int pass_max_rows(int mode) { return mode == QS_W4A16 ? 14 : (mode == QS_W4A4 || mode == QS_W4A8) ? 4 : 0; }
 
 size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
@@ -1136,11 +1193,14 @@ size_t pass_stage_bytes(int M, const qs_linear_desc* c, int n) {
   for (int i = 0; i + 1 < n; ++i) b += align_up((size_t)M * c[i].N * 2, 256);
   return b;
 }
-// Stage outputs and, for W4A4 above one row, the code buffer after them: one byte per fp16 output, at half its
-// offset (so each stage's codes start 128-byte aligned), then the codes of the pass's input.
+// Stage outputs and, for the integer modes above one row, the shared codes after them: one byte (W4A4)
+// or two (W4A8) per fp16 output, at half or all of its offset (so each stage's codes start 128-byte
+// aligned), then the codes of the pass's input.
 size_t pass_area_bytes(int mode, int M, const qs_linear_desc* c, int n) {
   const size_t sb = pass_stage_bytes(M, c, n);
-  return pass_shared_codes(mode, M) ? sb + sb / 2 + align_up((size_t)M * c[0].K, 256) : sb;
+  if (!pass_shared_codes(mode, M)) return sb;
+  const size_t cb = pass_code_bytes(mode);
+  return sb + sb * cb / 2 + align_up((size_t)M * c[0].K * cb, 256);
 }
 
 
@@ -1231,17 +1291,18 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     lds = b > lds ? b : lds;
   }
 
-  // Stage outputs of the whole pass -> kEmpty, W4A4 codes -> kCodeEmpty, error word -> 0.
+  // Stage outputs of the whole pass -> kEmpty, shared codes -> empty, error word -> 0.
   const size_t sb = pass_stage_bytes(M, c, n);
   if (pass_area_bytes(mode, M, c, n) > (size_t)0x7FFFFF00) return QS_ERR_UNSUPPORTED;  // one buffer resource spans them
   const uint32_t n16 = mode != QS_W4A16 ? (uint32_t)(sb / 16) : 0u;  // W4A16 stages hand over at a grid barrier
-  const uint32_t n16c = (uint32_t)((pass_area_bytes(mode, M, c, n) - sb) / 16);  // W4A4 codes
+  const uint32_t n16c = (uint32_t)((pass_area_bytes(mode, M, c, n) - sb) / 16);  // shared codes
+  const uint32_t cfill = mode == QS_W4A8 ? kCodeEmpty16 : kCodeEmpty;
   const size_t n_out = out ? (size_t)M * c[n - 1].N : 0;
   if (n_out > 0xFFFFFFFFu) return QS_ERR_UNSUPPORTED;
   const size_t work = (size_t)n16 + n16c + n_out / 4;
   const unsigned rblocks = (unsigned)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
   hipLaunchKernelGGL(pass_reset_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st,
-                     reinterpret_cast<uint4*>(stage_out), n16, n16c, ctrl, mode == QS_W4A16 ? grid : 0, out,
+                     reinterpret_cast<uint4*>(stage_out), n16, n16c, cfill, ctrl, mode == QS_W4A16 ? grid : 0, out,
                      (uint32_t)n_out, t1 ? t1->top1 : nullptr, t1 ? t1->top1_prob : nullptr, M);
   int rc = launch_status();
   if (rc != QS_OK) return rc;
@@ -1280,8 +1341,9 @@ int launch_pass(int mode, const uint16_t* x, int M, const qs_linear_desc* c, int
     a.stage_base = base;
     a.codes_base = reinterpret_cast<int8_t*>(base + sb);
     // the launch's input: the pass input's own code area, or the codes of the previous launch's output
-    a.codes_in = i0 == 0 ? reinterpret_cast<int8_t*>(base + sb + sb / 2)
-                         : reinterpret_cast<int8_t*>(base + sb + (reinterpret_cast<unsigned char*>(prev) - base) / 2);
+    const size_t cb = pass_code_bytes(mode);
+    a.codes_in = i0 == 0 ? reinterpret_cast<int8_t*>(base + sb + sb * cb / 2)
+                         : reinterpret_cast<int8_t*>(base + sb + (reinterpret_cast<unsigned char*>(prev) - base) * cb / 2);
     a.deadline = (long long)di->clock_khz * pass_barrier_timeout_us() / 1000;  // wall-clock ticks
     a.M = M;
     int e = 0;
