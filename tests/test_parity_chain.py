@@ -242,6 +242,29 @@ def test_chain_int_rows_2_to_4(qs, mode, m):
     _check_fused_top1(y, host(t1), host(p1), f"int rows mode={mode} m={m}")
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("m", [2, 4])
+def test_chain_int_rows_degenerate(qs, mode, m):
+    """The integer-mode pass above one row (shared codes) with degenerate rows: an all-zero input row
+    (zero scale, so all codes 0, and every later stage sees a row of zero spread, standardised to
+    zeros) and, at 4 rows, a constant row (every code the largest one) beside ordinary rows.  The
+    workgroups' shares then hold whole zero rows.  Bit-exact against the oracle."""
+    print(f"degenerate rows mode={mode} m={m}", flush=True)
+    rng = W.rng_for(1060 + 10 * m + mode)
+    shapes = [(1024, 512), (512, 1024), (700, 512)]
+    layers = [W.int4_weights(rng, n, k) for n, k in shapes]
+    x, _ = W.activations(rng, m, 512)
+    x[m - 1] = 0
+    if m == 4:
+        x[1] = np.float16(0.375)
+    chain = _pack_chain(qs, layers)
+    assert chain.pass_launches(mode, m) == 1
+    y = host(qs.qs_chain_forward(mode, dev(x), chain))
+    ref = O.chain_forward(MODE_NAMES[mode], x, layers)
+    assert_exact(y, ref, f"degenerate rows mode={mode} m={m}")
+    assert (y[m - 1] == 0).all()
+
+
 # ---------------------------------------------------------------- W4A16 persistent pass above four rows (K chunks)
 
 @pytest.mark.parametrize("m", [5, 8, 12, 14])
