@@ -843,15 +843,15 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     lds_barrier();  // G
   };
 
-  // W4A4 with shared codes: the row statistics as in stage_in4 (rounds of P pieces per thread, each
-  // polled until complete and added up, none kept), then each workgroup standardises and quantises
-  // only its share of the rows -- pieces [bid * per, (bid + 1) * per) of the M * K / 8 pieces, at
-  // most one per control thread -- and stores the codes to the stage's code buffer with
-  // device-coherent stores.  It then reads the whole code buffer (16-byte pieces, polled until no
-  // byte holds kCodeEmpty's) into LDS.  Every workgroup takes part, with or without sets in the
-  // stage, so that all shares get written; only those with sets read the codes.  This replaces the
-  // per-workgroup quantisation of all M * K values (whose time grows with the rows and with K) by
-  // one more all-to-all exchange, 1 byte per value.
+  // The integer modes above one row, with shared codes: the row statistics as in stage_in4 (rounds
+  // of P pieces per thread, each polled until complete and added up, none kept), then each
+  // workgroup standardises and quantises only its share of the rows -- pieces [bid * per, (bid + 1)
+  // * per) of the M * K / 8 pieces, at most one per control thread -- and stores the codes to the
+  // stage's code buffer with device-coherent stores (W4A4 a byte per code, W4A8 16 bits).  It then
+  // reads the whole code buffer (16-byte pieces, polled until none holds the empty code) into LDS.
+  // Every workgroup takes part, with or without sets in the stage, so that all shares get written;
+  // only those with sets read the codes.  This replaces the per-workgroup quantisation of all M * K
+  // values (whose time grows with the rows and with K) by one more all-to-all exchange.
   auto stage_in4s = [&](auto pc, int s, bool has) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     const PassStage ps = stage_at(s);
