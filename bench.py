@@ -531,6 +531,9 @@ def main():
     verify_dist = time_dist(runners[1], reps=100)
     log(f"verify phase over 100 replays: median {verify_dist['median_us']:.1f} us, "
         f"p10 {verify_dist['p10_us']:.1f}, p90 {verify_dist['p90_us']:.1f}")
+    draft_dist = time_dist(runners[0], reps=100)  # the draft phase: GAMMA passes back to back
+    log(f"draft phase ({GAMMA} passes) over 100 replays: median {draft_dist['median_us']:.1f} us, "
+        f"p10 {draft_dist['p10_us']:.1f}, p90 {draft_dist['p90_us']:.1f}")
     def optional_sections():
         """Accept throughput, per-linear rates, batched sweep and the timing model (skipped by --core-only)."""
         # "cold": a 1 GiB read before each call evicts the inputs from L2 and the 256 MiB MALL with clean
@@ -851,6 +854,7 @@ def main():
         "verify_pass_ms": verify_ms,
         "verify_phase_dist": verify_dist,
         "draft_pass_ms": draft_ms / GAMMA,
+        "draft_phase_dist": draft_dist,
         "draft_pass_GBps": draft_gbs,
         "accept_phase_ms": accept_ms,
         "iteration_accepted_tokens": n_acc + 1,
