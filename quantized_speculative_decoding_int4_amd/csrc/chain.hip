@@ -31,7 +31,8 @@ static size_t act_bytes(int M, const qs_linear_desc* c, int n) {
 
 // Workspace: two fp16 ping-pong buffers for the launch-per-linear path, then the per-linear scratch
 // or the control words of the persistent pass, then (for row counts a persistent pass takes) the
-// stage outputs of the persistent pass.
+// stage outputs of the persistent pass and, for the integer modes above one row, its shared
+// activation codes (pass_area_bytes).
 static size_t scratch_bytes(int mode, int M, const qs_linear_desc* c, int n) {
   size_t q = 0;
   for (int i = 0; i < n; ++i) {
