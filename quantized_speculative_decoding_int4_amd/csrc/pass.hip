@@ -914,7 +914,9 @@ __global__ __launch_bounds__(kPThreads) void pass_kernel(const PassArgs a) {
     int8_t* const codes =
         chunk_back(ps) == 0 ? a.codes_in
                             : a.codes_base + (reinterpret_cast<const unsigned char*>(x) - a.stage_base) * CB / 2;
-    if (active && mine_idx >= 0) {
+    // A workgroup one of whose waits failed publishes nothing (its statistics may be incomplete), so
+    // every other workgroup's wait for the codes fails too and no output is computed from them.
+    if (active && mine_idx >= 0 && !fail_sh) {
       uint4 w = mine;
       if (norm) w = norm_block8_64(w, row_mu64[my_row], row_inv64[my_row]);
       uint2 op, lg;
